@@ -1,0 +1,239 @@
+#!/usr/bin/env python3
+"""Benchmark of the GDN decode mixer on one MI355X.
+
+A step is one pass of the whole mixer (conv/SiLU/L2 -> gated delta rule -> gated
+RMSNorm, three kernels) over one batch: by default the bandwidth-bound decode of
+256 sequences x 1 token (768 MiB of fp32 state), inputs already in HBM.  Prints
+ONE JSON line on stdout; diagnostics go to stderr.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--config b256]
+                  [--cpu-seconds S | --no-cpu-baseline] [--copy-probe-mib M]
+
+The `roofline` object is for the dominant kernel (decode_step_kernel): its
+algorithmic bytes per launch over its average launch time, measured with HIP
+events recorded on the stream the kernels run on.  `traffic` (HBM bytes per
+launch from rocprofv3 FETCH_SIZE / WRITE_SIZE counters, scaled by a copy-kernel
+calibration) is read from profiles/decode_step_b256_traffic.txt and reported only
+while the kernel source it was measured on is unchanged.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0            # MI355X HBM3E, published peak
+KERNEL_SRC = os.path.join(ROOT, "gated_deltanet_mixer_gdn_amd", "csrc", "gdn_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_step_b256_traffic.txt")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def read_traffic():
+    """(bytes per launch, note) if the committed counter summary matches this kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    fields = {}
+    for line in open(TRAFFIC_FILE):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    if fields.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    try:
+        return float(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def algorithmic_bytes(wl):
+    """Bytes each kernel must move at minimum (inputs read once, outputs written once)."""
+    g = wl.geom
+    C, V, S, hv = g.channels, g.value_dim, g.s, g.h_v
+    tok = int(wl.B * wl.T if wl.n_tok is None else wl.n_tok.sum())
+    seqs = int(wl.B if wl.n_tok is None else (wl.n_tok > 0).sum())
+    all_tok = wl.B * wl.T
+    conv = tok * C * 4 + all_tok * C * 4 + seqs * C * (g.d_conv - 1) * 4 * 2 + C * g.d_conv * 4
+    step = (seqs * hv * S * S * 4 * 2          # state read + write, once per call
+            + tok * (C * 4 + 2 * hv * 4)       # h (q|k|v) and alpha / beta logits of each token
+            + all_tok * hv * S * 4             # o
+            + 2 * hv * 4)                      # dt, ssm_a
+    norm = all_tok * hv * S * 4 * 3 + S * 4    # o, z in; y out; norm weight
+    return {"conv": conv, "step": step, "norm": norm}, tok * hv
+
+
+def cpu_baseline(wl, seconds: float):
+    """The fp64 oracle, as it stands, on the host cores: whole batches of the same
+    workload, repeated until `seconds` of wall time have passed."""
+    import oracle
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    cores = max(1, min(cores, 16))
+    oracle.lib()
+    units = sum(wl.tokens_of(b) for b in range(wl.B)) * wl.geom.h_v
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.run_workload(wl, threads=cores)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": units * reps / el, "unit": "seq-head-steps/s", "cores": cores, "kind": "oracle",
+            "sample": f"{reps} full passes of the {wl.name} workload ({units} seq-head-steps each, "
+                      f"all {wl.B} sequences), fp64 C oracle, {cores} threads, {el:.1f} s"}
+
+
+def copy_probe(mib: int, reps: int = 5):
+    """A plain device copy of known size, for calibrating HBM byte counters."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_read": n * 4, "copy_probe_bytes_written": n * 4, "reps": reps}))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="b256", choices=["tiny", "b64", "b256", "prefill", "ragged"])
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build runs on one GPU only; the decode mixer shards by sequence "
+              "slots or head groups with no exchange inside the path, and multi-GPU runs are "
+              "not part of it. Use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import gated_deltanet_mixer_gdn_amd as G
+    import gdn_workloads as W
+
+    if not os.path.exists(G.LIB_PATH):
+        from gated_deltanet_mixer_gdn_amd import _build
+        _build.build()
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py: no GPU visible")
+    torch.cuda.set_device(0)
+    if args.copy_probe_mib:
+        copy_probe(args.copy_probe_mib)
+        return
+
+    wl = W.CONFIGS[args.config]()
+    g = wl.geom
+    log(f"workload {wl.name}: B={wl.B} T={wl.T} pool={wl.n_slots} slots")
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    pool = G.StatePool(wl.n_slots)
+    pool.state.copy_(dev(wl.state))
+    pool.conv.copy_(dev(wl.conv_state))
+    pool.flags.zero_()
+    qkv, alpha, bl, z = dev(wl.qkv), dev(wl.alpha), dev(wl.beta_logit), dev(wl.z)
+    conv_w, dt, ssm_a, norm_w = dev(wl.conv_w), dev(wl.dt), dev(wl.ssm_a), dev(wl.norm_w)
+    slots = dev(wl.slots)
+    n_tok = dev(wl.n_tok) if wl.n_tok is not None else None
+    h = torch.empty(wl.B, wl.T, g.channels, device="cuda")
+    o = torch.empty(wl.B, wl.T, g.h_v, g.s, device="cuda")
+    y = torch.empty(wl.B, wl.T, g.value_dim, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        G.gdn_conv_silu_norm(pool, qkv, conv_w, wl.eps, h, slots, n_tok)
+        if ev:
+            ev[1].record(stream)
+        G.gdn_decode_step(pool, h, alpha, bl, dt, ssm_a, o, slots, n_tok)
+        if ev:
+            ev[2].record(stream)
+        G.gdn_gated_rmsnorm(o, z, norm_w, wl.eps, y)
+        if ev:
+            ev[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    # wall-clock timed region (no events inside)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall_s = time.perf_counter() - t0
+    # per-kernel durations: the same steps again with event pairs on the launch stream
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for k in range(args.steps):
+        step(evs[k])
+    torch.cuda.synchronize()
+    k_ms = {name: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs]))
+            for i, name in enumerate(("conv", "step", "norm"))}
+    flags = int(pool.flags.item())
+    if flags:
+        raise SystemExit(f"bench.py: device flag word set ({flags:#x})")
+
+    ms_per_step = wall_s * 1000.0 / args.steps
+    nbytes, units = algorithmic_bytes(wl)
+    value = units / (ms_per_step / 1000.0)
+    achieved = nbytes["step"] / (k_ms["step"] / 1000.0) / 1e9
+    mixer_gbps = sum(nbytes.values()) / (ms_per_step / 1000.0) / 1e9
+    log(f"kernel ms: " + ", ".join(f"{k}={v * 1000:.1f}us" for k, v in k_ms.items()) +
+        f"; step {ms_per_step * 1000:.1f} us; decode kernel {achieved:.0f} GB/s; mixer {mixer_gbps:.0f} GB/s")
+    traffic = read_traffic() if args.config == "b256" else None
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the oracle on the host cores ...")
+        cpu = cpu_baseline(wl, args.cpu_seconds)
+        log(f"oracle: {cpu['value']:.0f} {cpu['unit']} on {cpu['cores']} threads")
+
+    out = {
+        "metric": "GDN decode seq-head-steps/s and achieved HBM GB/s vs peak at B=256",
+        "value": value,
+        "unit": "seq-head-steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "B": wl.B, "T": wl.T, "n_slots": wl.n_slots,
+                   "h_k": g.h_k, "h_v": g.h_v, "S": g.s, "d_conv": g.d_conv,
+                   "state_bytes": int(wl.n_slots * g.h_v * g.s * g.s * 4), "parallelism": "none"},
+        "hbm_gbps_mixer": mixer_gbps,
+        "hbm_frac_mixer": mixer_gbps / HBM_PEAK_GBPS,
+        "kernel_us": {k: v * 1000.0 for k, v in k_ms.items()},
+        "roofline": {"kernel": "decode_step_kernel", "bound": "hbm", "achieved": achieved,
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": traffic, "algorithmic_bytes_per_launch": nbytes["step"]},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

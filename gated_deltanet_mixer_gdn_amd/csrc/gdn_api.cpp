@@ -1,0 +1,308 @@
+// gdn_api.cpp - the C ABI declared in include/gdn.h: argument checks, the state
+// pool descriptor and kernel launches.  Host code only; it allocates nothing on
+// the device, never synchronises, and turns every failure into a status code plus
+// a thread-local message (the pages' layer functions return false with a message
+// naming the stage, `gdn_layer` on the "src/core/layer.cpp" page; here the
+// message names the function and the argument).
+#include <hip/hip_runtime_api.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdint>
+#include <new>
+#include <string>
+
+#include "gdn.h"
+#include "gdn_kernels.h"
+
+struct gdn_pool {
+    gdn_geom g;
+    int64_t n_slots;
+    int device;
+    char* base;
+    size_t bytes;
+    float* state;
+    float* conv;
+    uint32_t* flags;
+};
+
+namespace {
+
+thread_local std::string g_last_error;
+
+constexpr size_t kAlign = 256;
+constexpr size_t kFlagBytes = 256;
+
+int fail(int code, const char* fn, const char* fmt, ...) {
+    char msg[512];
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(msg, sizeof msg, fmt, ap);
+    va_end(ap);
+    g_last_error = std::string(fn) + ": " + msg;
+    return code;
+}
+
+int ok() {
+    g_last_error.clear();
+    return GDN_OK;
+}
+
+size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Geometry the HIP kernels are built for (s = 128, d_conv = 4, h_v a multiple of h_k).
+int check_geom(const gdn_geom* g, const char* fn) {
+    if (!g) return fail(GDN_ERR_ARG, fn, "geometry is null");
+    if (g->h_k <= 0 || g->h_v <= 0 || g->s <= 0 || g->d_conv <= 0)
+        return fail(GDN_ERR_ARG, fn, "geometry {h_k=%d, h_v=%d, s=%d, d_conv=%d} has a non-positive field",
+                    g->h_k, g->h_v, g->s, g->d_conv);
+    if (g->h_v % g->h_k != 0)
+        return fail(GDN_ERR_ARG, fn, "h_v=%d is not a multiple of h_k=%d", g->h_v, g->h_k);
+    if (g->s != gdn::kS || g->d_conv != gdn::kDConv)
+        return fail(GDN_ERR_UNSUPPORTED, fn, "the kernels are built for s=%d, d_conv=%d (got s=%d, d_conv=%d)",
+                    gdn::kS, gdn::kDConv, g->s, g->d_conv);
+    if ((int64_t) (2 * g->h_k + g->h_v) * g->s > (int64_t) 1 << 30)
+        return fail(GDN_ERR_UNSUPPORTED, fn, "channel count too large");
+    return GDN_OK;
+}
+
+int64_t channels(const gdn_geom& g) { return (int64_t) (2 * g.h_k + g.h_v) * g.s; }
+size_t state_bytes_per_slot(const gdn_geom& g) { return (size_t) g.h_v * g.s * g.s * sizeof(float); }
+size_t conv_bytes_per_slot(const gdn_geom& g) {
+    return (size_t) channels(g) * (g.d_conv - 1) * sizeof(float);
+}
+
+int check_pool(const gdn_pool* p, const char* fn) {
+    if (!p) return fail(GDN_ERR_ARG, fn, "pool is null");
+    int dev = -1;
+    const hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(GDN_ERR_HIP, fn, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev != p->device)
+        return fail(GDN_ERR_ARG, fn, "current device %d is not the pool's device %d", dev, p->device);
+    return GDN_OK;
+}
+
+int check_f4(const void* ptr, const char* fn, const char* name) {
+    if (!ptr) return fail(GDN_ERR_ARG, fn, "%s is null", name);
+    if (!aligned(ptr, 16)) return fail(GDN_ERR_ARG, fn, "%s is not 16-byte aligned", name);
+    return GDN_OK;
+}
+
+int check_f1(const void* ptr, const char* fn, const char* name) {
+    if (!ptr) return fail(GDN_ERR_ARG, fn, "%s is null", name);
+    if (!aligned(ptr, 4)) return fail(GDN_ERR_ARG, fn, "%s is not 4-byte aligned", name);
+    return GDN_OK;
+}
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + nb && y < x + na;
+}
+
+int launched(hipError_t e, const char* fn) {
+    if (e != hipSuccess) return fail(GDN_ERR_HIP, fn, "kernel launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int gdn_abi_version(void) { return GDN_ABI_VERSION; }
+
+const char* gdn_last_error(void) { return g_last_error.c_str(); }
+
+size_t gdn_state_pool_bytes(const gdn_geom* g, int64_t n_slots) {
+    if (check_geom(g, "gdn_state_pool_bytes") != GDN_OK) return 0;
+    if (n_slots <= 0 || n_slots > ((int64_t) 1 << 31)) {
+        fail(GDN_ERR_ARG, "gdn_state_pool_bytes", "n_slots=%lld out of range", (long long) n_slots);
+        return 0;
+    }
+    ok();
+    return kFlagBytes + round_up((size_t) n_slots * state_bytes_per_slot(*g)) +
+           round_up((size_t) n_slots * conv_bytes_per_slot(*g));
+}
+
+int gdn_state_pool_create(const gdn_geom* g, int64_t n_slots, void* dev_base, size_t bytes,
+                          gdn_pool** out) {
+    const char* fn = "gdn_state_pool_create";
+    if (!out) return fail(GDN_ERR_ARG, fn, "out is null");
+    *out = nullptr;
+    if (int rc = check_geom(g, fn)) return rc;
+    if (n_slots <= 0 || n_slots > ((int64_t) 1 << 31))
+        return fail(GDN_ERR_ARG, fn, "n_slots=%lld out of range", (long long) n_slots);
+    const size_t need = gdn_state_pool_bytes(g, n_slots);
+    if (!dev_base) return fail(GDN_ERR_ARG, fn, "dev_base is null");
+    if (!aligned(dev_base, kAlign)) return fail(GDN_ERR_ARG, fn, "dev_base is not 256-byte aligned");
+    if (bytes < need)
+        return fail(GDN_ERR_ARG, fn, "bytes=%zu is less than the %zu a pool of %lld slots needs", bytes, need,
+                    (long long) n_slots);
+    hipPointerAttribute_t attr;
+    hipError_t e = hipPointerGetAttributes(&attr, dev_base);
+    if (e != hipSuccess) {
+        (void) hipGetLastError();
+        return fail(GDN_ERR_HIP, fn, "hipPointerGetAttributes(dev_base): %s", hipGetErrorString(e));
+    }
+    if (attr.type != hipMemoryTypeDevice)
+        return fail(GDN_ERR_ARG, fn, "dev_base is not device memory");
+    int dev = -1;
+    e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(GDN_ERR_HIP, fn, "hipGetDevice: %s", hipGetErrorString(e));
+    if (attr.device != dev)
+        return fail(GDN_ERR_ARG, fn, "dev_base is on device %d, the current device is %d", attr.device, dev);
+    gdn_pool* p = new (std::nothrow) gdn_pool;
+    if (!p) return fail(GDN_ERR_ARG, fn, "out of host memory");
+    p->g = *g;
+    p->n_slots = n_slots;
+    p->device = dev;
+    p->base = static_cast<char*>(dev_base);
+    p->bytes = bytes;
+    p->flags = reinterpret_cast<uint32_t*>(p->base);
+    p->state = reinterpret_cast<float*>(p->base + kFlagBytes);
+    p->conv = reinterpret_cast<float*>(p->base + kFlagBytes + round_up((size_t) n_slots * state_bytes_per_slot(*g)));
+    *out = p;
+    return ok();
+}
+
+void gdn_state_pool_destroy(gdn_pool* p) { delete p; }
+
+float* gdn_state_pool_state(const gdn_pool* p) { return p ? p->state : nullptr; }
+float* gdn_state_pool_conv(const gdn_pool* p) { return p ? p->conv : nullptr; }
+uint32_t* gdn_state_pool_flags(const gdn_pool* p) { return p ? p->flags : nullptr; }
+int64_t gdn_state_pool_slots(const gdn_pool* p) { return p ? p->n_slots : 0; }
+
+int gdn_state_pool_zero(gdn_pool* p, const int32_t* slots, int32_t n, void* stream) {
+    const char* fn = "gdn_state_pool_zero";
+    if (int rc = check_pool(p, fn)) return rc;
+    if (slots) {
+        if (n < 0) return fail(GDN_ERR_ARG, fn, "n=%d is negative", n);
+        if (n > 65535) return fail(GDN_ERR_ARG, fn, "n=%d exceeds 65535 slots per call", n);
+        if (!aligned(slots, 4)) return fail(GDN_ERR_ARG, fn, "slots is not 4-byte aligned");
+        if (n == 0) return ok();
+    }
+    gdn::ZeroParams z;
+    z.state = p->state;
+    z.conv = p->conv;
+    z.flags = p->flags;
+    z.slots = slots;
+    z.n_slots = p->n_slots;
+    z.state_f4 = (long long) (state_bytes_per_slot(p->g) / 16);
+    z.conv_f4 = (long long) (conv_bytes_per_slot(p->g) / 16);
+    z.n = slots ? n : 0;
+    return launched(gdn::launch_zero(z, static_cast<hipStream_t>(stream)), fn);
+}
+
+int gdn_conv_silu_norm(gdn_pool* p, const int32_t* slots, const int32_t* n_tok, int32_t B, int32_t T,
+                       const float* qkv, const float* conv_w, float eps, float* h, void* stream) {
+    const char* fn = "gdn_conv_silu_norm";
+    if (int rc = check_pool(p, fn)) return rc;
+    if (B < 0) return fail(GDN_ERR_ARG, fn, "B=%d is negative", B);
+    if (T < 1) return fail(GDN_ERR_ARG, fn, "T=%d must be >= 1", T);
+    if (!(eps >= 0.0f) || !std::isfinite(eps)) return fail(GDN_ERR_ARG, fn, "eps must be finite and >= 0");
+    if (B == 0) return ok();
+    const int n_tb = (T + gdn::kConvTokensPerBlock - 1) / gdn::kConvTokensPerBlock;
+    if ((int64_t) B * n_tb > INT32_MAX) return fail(GDN_ERR_ARG, fn, "B*T too large");
+    if (int rc = check_f4(qkv, fn, "qkv")) return rc;
+    if (int rc = check_f4(conv_w, fn, "conv_w")) return rc;
+    if (int rc = check_f4(h, fn, "h")) return rc;
+    if (slots && !aligned(slots, 4)) return fail(GDN_ERR_ARG, fn, "slots is not 4-byte aligned");
+    if (n_tok && !aligned(n_tok, 4)) return fail(GDN_ERR_ARG, fn, "n_tok is not 4-byte aligned");
+    if (!slots && B > p->n_slots)
+        return fail(GDN_ERR_ARG, fn, "slots is null and B=%d exceeds the pool's %lld slots", B,
+                    (long long) p->n_slots);
+    const size_t io = (size_t) B * T * channels(p->g) * sizeof(float);
+    if (overlap(qkv, io, h, io)) return fail(GDN_ERR_ARG, fn, "h overlaps qkv");
+    gdn::ConvParams c;
+    c.conv = p->conv;
+    c.slots = slots;
+    c.n_tok = n_tok;
+    c.qkv = qkv;
+    c.w = conv_w;
+    c.h = h;
+    c.flags = p->flags;
+    c.n_slots = p->n_slots;
+    c.B = B;
+    c.T = T;
+    c.h_k = p->g.h_k;
+    c.n_heads = 2 * p->g.h_k + p->g.h_v;
+    c.n_tb = n_tb;
+    c.eps = eps;
+    c.qscale = 1.0f / std::sqrt((float) p->g.s);
+    return launched(gdn::launch_conv_silu_norm(c, static_cast<hipStream_t>(stream)), fn);
+}
+
+int gdn_decode_step(gdn_pool* p, const int32_t* slots, const int32_t* n_tok, int32_t B, int32_t T,
+                    const float* h, const float* alpha, const float* beta_logit, const float* dt,
+                    const float* ssm_a, float* o, void* stream) {
+    const char* fn = "gdn_decode_step";
+    if (int rc = check_pool(p, fn)) return rc;
+    if (B < 0) return fail(GDN_ERR_ARG, fn, "B=%d is negative", B);
+    if (T < 1) return fail(GDN_ERR_ARG, fn, "T=%d must be >= 1", T);
+    if (B == 0) return ok();
+    if ((int64_t) B * p->g.h_v > INT32_MAX) return fail(GDN_ERR_ARG, fn, "B*h_v too large");
+    if (int rc = check_f4(h, fn, "h")) return rc;
+    if (int rc = check_f1(alpha, fn, "alpha")) return rc;
+    if (int rc = check_f1(beta_logit, fn, "beta_logit")) return rc;
+    if (int rc = check_f1(dt, fn, "dt")) return rc;
+    if (int rc = check_f1(ssm_a, fn, "ssm_a")) return rc;
+    if (int rc = check_f4(o, fn, "o")) return rc;
+    if (slots && !aligned(slots, 4)) return fail(GDN_ERR_ARG, fn, "slots is not 4-byte aligned");
+    if (n_tok && !aligned(n_tok, 4)) return fail(GDN_ERR_ARG, fn, "n_tok is not 4-byte aligned");
+    if (!slots && B > p->n_slots)
+        return fail(GDN_ERR_ARG, fn, "slots is null and B=%d exceeds the pool's %lld slots", B,
+                    (long long) p->n_slots);
+    const size_t o_bytes = (size_t) B * T * p->g.h_v * p->g.s * sizeof(float);
+    const size_t h_bytes = (size_t) B * T * channels(p->g) * sizeof(float);
+    if (overlap(o, o_bytes, h, h_bytes)) return fail(GDN_ERR_ARG, fn, "o overlaps h");
+    const size_t pool_bytes = (size_t) ((p->base + p->bytes) - reinterpret_cast<char*>(p->state));
+    if (overlap(o, o_bytes, p->state, pool_bytes)) return fail(GDN_ERR_ARG, fn, "o overlaps the pool");
+    gdn::StepParams s;
+    s.state = p->state;
+    s.slots = slots;
+    s.n_tok = n_tok;
+    s.h = h;
+    s.alpha = alpha;
+    s.beta_logit = beta_logit;
+    s.dt = dt;
+    s.ssm_a = ssm_a;
+    s.o = o;
+    s.flags = p->flags;
+    s.n_slots = p->n_slots;
+    s.B = B;
+    s.T = T;
+    s.h_k = p->g.h_k;
+    s.h_v = p->g.h_v;
+    s.group = p->g.h_v / p->g.h_k;
+    return launched(gdn::launch_decode_step(s, static_cast<hipStream_t>(stream)), fn);
+}
+
+int gdn_gated_rmsnorm(const float* o, const float* z, const float* w, float eps, int64_t rows, int32_t s,
+                      float* y, void* stream) {
+    const char* fn = "gdn_gated_rmsnorm";
+    if (rows < 0) return fail(GDN_ERR_ARG, fn, "rows=%lld is negative", (long long) rows);
+    if (s != gdn::kS) return fail(GDN_ERR_UNSUPPORTED, fn, "s=%d: the kernel is built for s=%d", s, gdn::kS);
+    if (!(eps >= 0.0f) || !std::isfinite(eps)) return fail(GDN_ERR_ARG, fn, "eps must be finite and >= 0");
+    if (rows == 0) return ok();
+    if ((rows + gdn::kNormRowsPerBlock - 1) / gdn::kNormRowsPerBlock > INT32_MAX)
+        return fail(GDN_ERR_ARG, fn, "rows too large");
+    if (int rc = check_f4(o, fn, "o")) return rc;
+    if (int rc = check_f4(z, fn, "z")) return rc;
+    if (int rc = check_f4(w, fn, "w")) return rc;
+    if (int rc = check_f4(y, fn, "y")) return rc;
+    const size_t n = (size_t) rows * s * sizeof(float);
+    if (y != o && overlap(y, n, o, n)) return fail(GDN_ERR_ARG, fn, "y partially overlaps o");
+    if (overlap(y, n, z, n)) return fail(GDN_ERR_ARG, fn, "y overlaps z");
+    gdn::NormParams np;
+    np.o = o;
+    np.z = z;
+    np.w = w;
+    np.y = y;
+    np.rows = (long long) rows;
+    np.eps = eps;
+    return launched(gdn::launch_gated_rmsnorm(np, static_cast<hipStream_t>(stream)), fn);
+}
+
+}  // extern "C"

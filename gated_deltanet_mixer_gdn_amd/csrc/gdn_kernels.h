@@ -1,0 +1,76 @@
+// gdn_kernels.h - internal interface between the C-ABI layer (gdn_api.cpp) and the
+// gfx950 kernels (gdn_kernels.hip).  Not installed, not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+#include "gdn.h"
+
+namespace gdn {
+
+// Head size and conv width the kernels are built for.
+constexpr int kS = 128;
+constexpr int kDConv = 4;
+constexpr int kHist = kDConv - 1;
+// Tokens of one sequence handled by one conv workgroup (>= kHist, so only the
+// first token block of a sequence ever reads or writes the stored conv history).
+constexpr int kConvTokensPerBlock = 8;
+// Rows (value heads x tokens) per gated-RMSNorm workgroup: one half-wave per row.
+constexpr int kNormRowsPerBlock = 8;
+
+struct ConvParams {
+    float* conv;            // pool conv region [n_slots][C][3]
+    const int32_t* slots;   // [B] or null
+    const int32_t* n_tok;   // [B] or null
+    const float* qkv;       // [B][T][C]
+    const float* w;         // [C][4]
+    float* h;               // [B][T][C]
+    uint32_t* flags;        // pool flag word
+    long long n_slots;
+    int B, T, h_k, n_heads; // n_heads = 2*h_k + h_v (128-channel heads)
+    int n_tb;               // token blocks per sequence
+    float eps, qscale;
+};
+
+struct StepParams {
+    float* state;           // pool state region [n_slots][h_v][128][128]
+    const int32_t* slots;
+    const int32_t* n_tok;
+    const float* h;         // [B][T][C]
+    const float* alpha;     // [B][T][h_v]
+    const float* beta_logit;
+    const float* dt;        // [h_v]
+    const float* ssm_a;     // [h_v]
+    float* o;               // [B][T][h_v][128]
+    uint32_t* flags;
+    long long n_slots;
+    int B, T, h_k, h_v, group;  // group = h_v / h_k
+};
+
+struct NormParams {
+    const float* o;
+    const float* z;
+    const float* w;
+    float* y;
+    long long rows;
+    float eps;
+};
+
+struct ZeroParams {
+    float* state;
+    float* conv;
+    uint32_t* flags;
+    const int32_t* slots;   // null: zero everything and clear the flag word
+    long long n_slots;
+    long long state_f4;     // float4s of state per slot
+    long long conv_f4;      // float4s of conv history per slot
+    int n;                  // slots listed
+};
+
+hipError_t launch_conv_silu_norm(const ConvParams& p, hipStream_t stream);
+hipError_t launch_decode_step(const StepParams& p, hipStream_t stream);
+hipError_t launch_gated_rmsnorm(const NormParams& p, hipStream_t stream);
+hipError_t launch_zero(const ZeroParams& p, hipStream_t stream);
+
+}  // namespace gdn

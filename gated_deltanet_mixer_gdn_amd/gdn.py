@@ -1,0 +1,217 @@
+"""Thin Python binding of the C ABI in include/gdn.h (libgdn_hip.so).
+
+Argument marshalling only: torch tensors supply device memory and the current
+HIP stream; every step of the mixer runs in the library's gfx950 kernels. The
+functions keep the ABI's names. There is no fallback: if the library is not
+built, or no GPU is present, calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libgdn_hip.so")
+
+GDN_OK, GDN_ERR_ARG, GDN_ERR_UNSUPPORTED, GDN_ERR_HIP = 0, -1, -2, -3
+GDN_FLAG_BAD_SLOT, GDN_FLAG_BAD_NTOK = 0x1, 0x2
+EXPORTS = (
+    "gdn_abi_version", "gdn_last_error", "gdn_state_pool_bytes", "gdn_state_pool_create",
+    "gdn_state_pool_destroy", "gdn_state_pool_state", "gdn_state_pool_conv", "gdn_state_pool_flags",
+    "gdn_state_pool_slots", "gdn_state_pool_zero", "gdn_conv_silu_norm", "gdn_decode_step",
+    "gdn_gated_rmsnorm",
+)
+
+
+class GdnError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"[{code}] {msg}")
+        self.code = code
+
+
+class gdn_geom(ctypes.Structure):
+    _fields_ = [("h_k", ctypes.c_int32), ("h_v", ctypes.c_int32), ("s", ctypes.c_int32),
+                ("d_conv", ctypes.c_int32)]
+
+
+@dataclass(frozen=True)
+class Geom:
+    """GDN geometry; the defaults are the pages' model (16 qk heads, 48 value heads)."""
+    h_k: int = 16
+    h_v: int = 48
+    s: int = 128
+    d_conv: int = 4
+
+    @property
+    def channels(self) -> int:
+        return (2 * self.h_k + self.h_v) * self.s
+
+    def c(self) -> gdn_geom:
+        return gdn_geom(self.h_k, self.h_v, self.s, self.d_conv)
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libgdn_hip.so. torch is imported first so the library binds to the HIP
+    runtime torch already loaded (one runtime, one set of device pointers)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    import torch  # noqa: F401  (loads libamdhip64 into the process)
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is not built; run __graft_entry__.build() first")
+    L = ctypes.CDLL(path)
+    vp, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+    G = ctypes.POINTER(gdn_geom)
+    sig = {
+        "gdn_abi_version": ([], ctypes.c_int),
+        "gdn_last_error": ([], ctypes.c_char_p),
+        "gdn_state_pool_bytes": ([G, i64], ctypes.c_size_t),
+        "gdn_state_pool_create": ([G, i64, vp, ctypes.c_size_t, ctypes.POINTER(vp)], ctypes.c_int),
+        "gdn_state_pool_destroy": ([vp], None),
+        "gdn_state_pool_state": ([vp], vp),
+        "gdn_state_pool_conv": ([vp], vp),
+        "gdn_state_pool_flags": ([vp], vp),
+        "gdn_state_pool_slots": ([vp], i64),
+        "gdn_state_pool_zero": ([vp, vp, i32, vp], ctypes.c_int),
+        "gdn_conv_silu_norm": ([vp, vp, vp, i32, i32, vp, vp, f32, vp, vp], ctypes.c_int),
+        "gdn_decode_step": ([vp, vp, vp, i32, i32, vp, vp, vp, vp, vp, vp, vp], ctypes.c_int),
+        "gdn_gated_rmsnorm": ([vp, vp, vp, f32, i64, i32, vp, vp], ctypes.c_int),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(L, name)
+        fn.argtypes = args
+        fn.restype = res
+    _lib = L
+    return L
+
+
+def _check(rc: int):
+    if rc != GDN_OK:
+        raise GdnError(rc, load_library().gdn_last_error().decode())
+
+
+def _stream(t) -> int:
+    import torch
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _f32(t, name: str, shape=None):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous float32 CUDA tensor")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t.data_ptr()
+
+
+def _i32(t, name: str, n: int):
+    import torch
+    if t is None:
+        return None
+    if t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous() or t.numel() != n:
+        raise ValueError(f"{name} must be a contiguous int32 CUDA tensor of {n} elements")
+    return t.data_ptr()
+
+
+def gdn_state_pool_bytes(n_slots: int, geom: Geom = Geom()) -> int:
+    g = geom.c()
+    n = load_library().gdn_state_pool_bytes(ctypes.byref(g), n_slots)
+    if n == 0:
+        raise GdnError(GDN_ERR_ARG, load_library().gdn_last_error().decode())
+    return n
+
+
+class StatePool:
+    """A pool of recurrent-state slots in one torch-owned device buffer.
+
+    .state  float32 [n_slots][h_v][s][s]  (row = key index, column = value index)
+    .conv   float32 [n_slots][C][d_conv-1] (raw qkv history, oldest first)
+    .flags  int32 [1] device flag word (GDN_FLAG_* bits)
+    """
+
+    def __init__(self, n_slots: int, geom: Geom = Geom(), device=None):
+        import torch
+        L = load_library()
+        self.geom = geom
+        self.n_slots = n_slots
+        self.device = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
+        nbytes = gdn_state_pool_bytes(n_slots, geom)
+        with torch.cuda.device(self.device):
+            self.buffer = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
+            h = ctypes.c_void_p()
+            g = geom.c()
+            _check(L.gdn_state_pool_create(ctypes.byref(g), n_slots, self.buffer.data_ptr(), nbytes,
+                                           ctypes.byref(h)))
+        self.handle = h
+        base = self.buffer.data_ptr()
+        st = L.gdn_state_pool_state(h) - base
+        cv = L.gdn_state_pool_conv(h) - base
+        fl = L.gdn_state_pool_flags(h) - base
+        n_st = n_slots * geom.h_v * geom.s * geom.s * 4
+        n_cv = n_slots * geom.channels * (geom.d_conv - 1) * 4
+        self.state = self.buffer[st:st + n_st].view(torch.float32).view(n_slots, geom.h_v, geom.s, geom.s)
+        self.conv = self.buffer[cv:cv + n_cv].view(torch.float32).view(n_slots, geom.channels,
+                                                                         geom.d_conv - 1)
+        self.flags = self.buffer[fl:fl + 4].view(torch.int32)
+
+    def __del__(self):
+        h = getattr(self, "handle", None)
+        if h is not None and _lib is not None:
+            _lib.gdn_state_pool_destroy(h)
+            self.handle = None
+
+    def zero(self, slots=None):
+        gdn_state_pool_zero(self, slots)
+
+
+def gdn_state_pool_zero(pool: StatePool, slots=None):
+    n = 0 if slots is None else slots.numel()
+    ptr = _i32(slots, "slots", n)
+    _check(load_library().gdn_state_pool_zero(pool.handle, ptr, n, _stream(pool.buffer)))
+
+
+def gdn_conv_silu_norm(pool: StatePool, qkv, conv_w, eps: float, h, slots=None, n_tok=None):
+    """qkv, h [B][T][C]; conv_w [C][d_conv]; slots/n_tok int32 [B] or None."""
+    B, T = qkv.shape[0], qkv.shape[1]
+    C = pool.geom.channels
+    args = (_f32(qkv, "qkv", (B, T, C)), _f32(conv_w, "conv_w", (C, pool.geom.d_conv)),
+            _f32(h, "h", (B, T, C)))
+    _check(load_library().gdn_conv_silu_norm(pool.handle, _i32(slots, "slots", B), _i32(n_tok, "n_tok", B),
+                                             B, T, args[0], args[1], float(eps), args[2], _stream(qkv)))
+
+
+def gdn_decode_step(pool: StatePool, h, alpha, beta_logit, dt, ssm_a, o, slots=None, n_tok=None):
+    """h [B][T][C]; alpha, beta_logit [B][T][h_v]; dt, ssm_a [h_v]; o [B][T][h_v][s]."""
+    g = pool.geom
+    B, T = h.shape[0], h.shape[1]
+    ptrs = (_f32(h, "h", (B, T, g.channels)), _f32(alpha, "alpha", (B, T, g.h_v)),
+            _f32(beta_logit, "beta_logit", (B, T, g.h_v)), _f32(dt, "dt", (g.h_v,)),
+            _f32(ssm_a, "ssm_a", (g.h_v,)), _f32(o, "o", (B, T, g.h_v, g.s)))
+    _check(load_library().gdn_decode_step(pool.handle, _i32(slots, "slots", B), _i32(n_tok, "n_tok", B), B, T,
+                                          *ptrs, _stream(h)))
+
+
+def gdn_gated_rmsnorm(o, z, w, eps: float, y):
+    """o, z, y: any contiguous float32 layout whose last axis is s = 128 rows; w [s]."""
+    s = w.shape[-1]
+    rows = o.numel() // s
+    ptrs = (_f32(o, "o"), _f32(z, "z"), _f32(w, "w", (s,)), _f32(y, "y"))
+    if z.numel() != o.numel() or y.numel() != o.numel():
+        raise ValueError("o, z and y must hold the same number of elements")
+    _check(load_library().gdn_gated_rmsnorm(ptrs[0], ptrs[1], ptrs[2], float(eps), rows, s, ptrs[3],
+                                            _stream(o)))
+
+
+def gdn_mixer(pool: StatePool, qkv, alpha, beta_logit, z, conv_w, dt, ssm_a, norm_w, eps: float,
+              h, o, y, slots=None, n_tok=None):
+    """One pass of the whole mixer: the three ABI calls in the layer's order."""
+    gdn_conv_silu_norm(pool, qkv, conv_w, eps, h, slots, n_tok)
+    gdn_decode_step(pool, h, alpha, beta_logit, dt, ssm_a, o, slots, n_tok)
+    gdn_gated_rmsnorm(o, z, norm_w, eps, y)

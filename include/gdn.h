@@ -1,0 +1,165 @@
+/*
+ * gdn.h - C ABI of the MI355X (gfx950) Gated DeltaNet decode mixer.
+ *
+ * The mixer is the part of the GDN layer between the qkv / alpha / beta / z
+ * projections and the output projection, in the order the GDN layer's docstring
+ * on the "include/strata/core/layer.hpp" page gives and `gdn_layer` on the
+ * "src/core/layer.cpp" page runs (its steps 3 to 7):
+ *
+ *   gdn_conv_silu_norm  depthwise causal conv (d_conv = 4) with a rolling
+ *                       conv state, SiLU on all C channels, L2 norm of the q
+ *                       and k heads (v untouched), q scaled by 1/sqrt(S)
+ *   gdn_decode_step     beta = sigmoid(beta logit), gate = softplus(alpha + dt)
+ *                       * ssm_a, then the gated delta rule on each value head's
+ *                       S x S fp32 state; T >= 1 tokens per call, state held
+ *                       on chip across the tokens of one call
+ *   gdn_gated_rmsnorm   y = rms_norm(o) * w * sigmoid(z)   (sigmoid, not SiLU)
+ *
+ * States live in a pool of slots carved from caller-provided device memory (the
+ * pattern of `gdn_buffers_bytes` / `gdn_buffers_init` / `gdn_buffers_zero_state`
+ * on the layer.hpp page); a call works on a batch of B sequences whose states are
+ * gathered from the pool by a device array of slot indices.
+ *
+ * Conventions for every function:
+ *   - Pointers are DEVICE pointers unless the comment says host.  `stream` is a
+ *     hipStream_t passed as void* (NULL = the null stream of the current device).
+ *   - The library never allocates, frees or synchronises device memory and never
+ *     throws or exits across this ABI.  Work is only enqueued on `stream`; the
+ *     call returns before it runs.  Calls are capturable into HIP graphs (no
+ *     memset nodes are recorded; zeroing uses a kernel).
+ *   - Outputs are overwritten; state and conv state are updated in place.
+ *   - All float data is fp32, row-major, last index fastest, 16-byte aligned.
+ *   - Return value: GDN_OK, or a negative GDN_ERR_* code; gdn_last_error() then
+ *     names the function and the argument.  Nothing is enqueued on error.
+ *   - Errors that only the device can see (a slot index outside the pool, a
+ *     token count outside [0, T]) do not fault: the kernel skips that sequence
+ *     (slot) or clamps the count, and ORs a GDN_FLAG_* bit into the pool's flag
+ *     word (gdn_state_pool_flags), which the caller may read and clear.
+ *   - Slots within one call must be unique; duplicates race.  Calls on one pool
+ *     are ordered only by the stream they are enqueued on.
+ *
+ * Geometry supported by the GPU path: s = 128, d_conv = 4, h_k >= 1 and h_v a
+ * multiple of h_k (the pages' model is h_k = 16, h_v = 48, C = 10240).  Anything
+ * else returns GDN_ERR_UNSUPPORTED.
+ */
+#ifndef GDN_H_
+#define GDN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDN_ABI_VERSION 1
+
+enum {
+    GDN_OK = 0,
+    GDN_ERR_ARG = -1,          /* a null, misaligned, negative or inconsistent argument */
+    GDN_ERR_UNSUPPORTED = -2,  /* a geometry the GPU kernels are not built for */
+    GDN_ERR_HIP = -3           /* the HIP runtime reported an error (message says which) */
+};
+
+/* Bits of the pool's device flag word. */
+#define GDN_FLAG_BAD_SLOT 0x1u  /* a slot index was < 0 or >= n_slots: that sequence was skipped */
+#define GDN_FLAG_BAD_NTOK 0x2u  /* a token count was outside [0, T]: it was clamped */
+
+/* GDN geometry: qk heads, value heads, head size S, conv width.  The value head i
+ * reads qk head i / (h_v / h_k).  Channels C = (2*h_k + h_v) * s: q | k | v. */
+typedef struct gdn_geom {
+    int32_t h_k;
+    int32_t h_v;
+    int32_t s;
+    int32_t d_conv;
+} gdn_geom;
+
+/* Opaque host-side descriptor of a state pool.  It owns no device memory. */
+typedef struct gdn_pool gdn_pool;
+
+/* ABI version of the loaded library (GDN_ABI_VERSION it was built with). */
+int gdn_abi_version(void);
+
+/* Message of the last failed call on this host thread ("" if none). */
+const char* gdn_last_error(void);
+
+/* ---------------------------------------------------------------- state pool
+ * Device layout of a pool carved from `dev_base` (256-byte aligned):
+ *   [flags: 256 B, one uint32 flag word at offset 0]
+ *   [state: n_slots x h_v x s x s fp32]   state[slot][i][r][c]: r = key index,
+ *                                          c = value index (o = S^T q reads
+ *                                          down the rows)
+ *   [conv:  n_slots x C x (d_conv-1) fp32] conv[slot][c][j]: the last d_conv-1
+ *                                          RAW qkv inputs of channel c, oldest
+ *                                          first
+ * Each region starts on a 256-byte boundary.  Per slot at the pages' geometry:
+ * 3 MiB of state + 120 KiB of conv history. */
+
+/* Bytes a pool of n_slots needs (0 if the arguments are invalid).  Host call. */
+size_t gdn_state_pool_bytes(const gdn_geom* g, int64_t n_slots);
+
+/* Describe a pool over `dev_base` (>= gdn_state_pool_bytes bytes of device memory
+ * on the current device, 256-byte aligned, owned by the caller and outliving the
+ * pool).  Contents are NOT initialised: call gdn_state_pool_zero or write the
+ * state and conv regions directly.  *out receives a host-allocated descriptor. */
+int gdn_state_pool_create(const gdn_geom* g, int64_t n_slots, void* dev_base, size_t bytes,
+                          gdn_pool** out);
+
+/* Free the descriptor (not the device memory).  NULL is ignored. */
+void gdn_state_pool_destroy(gdn_pool* p);
+
+/* Device addresses of the regions above, and the pool's shape (NULL / 0 for p = NULL). */
+float* gdn_state_pool_state(const gdn_pool* p);
+float* gdn_state_pool_conv(const gdn_pool* p);
+uint32_t* gdn_state_pool_flags(const gdn_pool* p);
+int64_t gdn_state_pool_slots(const gdn_pool* p);
+
+/* Zero the state and conv history of n slots (device int32 [n]; slots = NULL
+ * zeroes every slot and n is ignored), so a fresh sequence starts from zeros
+ * as `gdn_buffers_zero_state` does.  Also clears the flag word when slots is NULL. */
+int gdn_state_pool_zero(gdn_pool* p, const int32_t* slots, int32_t n, void* stream);
+
+/* ---------------------------------------------------------------- the mixer */
+
+/* Steps 3-4 of gdn_layer for B sequences x T tokens: for every channel c,
+ *   u = sum_{j<3} conv_w[c][j] * X[c][j] + conv_w[c][3] * qkv[c],  X rolled with the raw qkv,
+ *   h = u * sigmoid(u)                        (all C channels, before the split)
+ *   q heads (channels [0, h_k*s)):       h / sqrt(|h|^2 + eps) / sqrt(s)
+ *   k heads (channels [h_k*s, 2*h_k*s)): h / sqrt(|h|^2 + eps)
+ *   v (channels [2*h_k*s, C)):           unchanged
+ * slots  int32 [B]          pool slot of each sequence (NULL: slot b for sequence b)
+ * n_tok  int32 [B]          tokens each sequence takes, in [0, T] (NULL: all T);
+ *                           outputs of tokens t >= n_tok[b] are written as 0 and
+ *                           the conv history advances by n_tok[b] tokens only
+ * qkv    [B][T][C]          raw projections;  conv_w [C][d_conv]
+ * h      [B][T][C]          output (may not alias qkv)
+ * B >= 0, T >= 1; B = 0 is a no-op. */
+int gdn_conv_silu_norm(gdn_pool* p, const int32_t* slots, const int32_t* n_tok, int32_t B,
+                       int32_t T, const float* qkv, const float* conv_w, float eps, float* h,
+                       void* stream);
+
+/* Steps 5-6 of gdn_layer for B sequences x T tokens, token by token:
+ *   beta = sigmoid(beta_logit), g = softplus(alpha + dt[i]) * ssm_a[i]
+ *   S <- exp(g) S;  m = S^T k;  S <- S + k (beta (v - m))^T;  o = S^T q
+ * for every value head i with q, k of qk head i / (h_v/h_k), taken from h as
+ * produced by gdn_conv_silu_norm (q already carries its 1/sqrt(s)).
+ * slots, n_tok  as above; tokens t >= n_tok[b] leave the state alone and write o = 0
+ * h        [B][T][C];  alpha, beta_logit [B][T][h_v];  dt, ssm_a [h_v]
+ * o        [B][T][h_v][s]   output
+ * The state of each listed slot is read once and written once per call. */
+int gdn_decode_step(gdn_pool* p, const int32_t* slots, const int32_t* n_tok, int32_t B, int32_t T,
+                    const float* h, const float* alpha, const float* beta_logit, const float* dt,
+                    const float* ssm_a, float* o, void* stream);
+
+/* Step 7 of gdn_layer: per row of s values,
+ *   y = o / sqrt(mean(o^2) + eps) * w * sigmoid(z)
+ * o, z, y [rows][s] (rows = B*T*h_v); w [s], shared by all rows.  s must be 128.
+ * y may alias o. */
+int gdn_gated_rmsnorm(const float* o, const float* z, const float* w, float eps, int64_t rows,
+                      int32_t s, float* y, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H_ */

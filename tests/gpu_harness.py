@@ -1,0 +1,87 @@
+"""Helpers for the GPU parity tests: move a seeded workload onto the device, run the
+HIP path through the C ABI, and compare against the fp64 oracle."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+
+def log(msg: str):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def dev(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def assert_close(name: str, gpu, ref, rel: float):
+    """max |gpu - ref| <= rel * max |ref|, on the whole array."""
+    g = np.asarray(gpu, dtype=np.float64)
+    r = np.asarray(ref, dtype=np.float64)
+    assert g.shape == r.shape, f"{name}: shape {g.shape} vs {r.shape}"
+    assert np.isfinite(g).all(), f"{name}: non-finite values from the GPU"
+    m = float(np.abs(r).max()) if r.size else 0.0
+    err = float(np.abs(g - r).max()) if r.size else 0.0
+    assert err <= rel * m, f"{name}: max abs err {err:.3e} > {rel:g} x max|ref| ({m:.3e})"
+    return err / m if m else 0.0
+
+
+class GpuMixer:
+    """The workload's tensors on the device plus a state pool filled from it."""
+
+    def __init__(self, wl, pool=None):
+        import torch
+        import gated_deltanet_mixer_gdn_amd as G
+        self.G = G
+        self.wl = wl
+        g = wl.geom
+        self.geom = G.Geom(g.h_k, g.h_v, g.s, g.d_conv)
+        if pool is None:
+            pool = G.StatePool(wl.n_slots, self.geom)
+            pool.state.copy_(dev(wl.state))
+            pool.conv.copy_(dev(wl.conv_state))
+            pool.flags.zero_()
+        self.pool = pool
+        self.conv_w = dev(wl.conv_w)
+        self.dt = dev(wl.dt)
+        self.ssm_a = dev(wl.ssm_a)
+        self.norm_w = dev(wl.norm_w)
+        self.qkv = dev(wl.qkv)
+        self.alpha = dev(wl.alpha)
+        self.beta_logit = dev(wl.beta_logit)
+        self.z = dev(wl.z)
+        self.slots = dev(wl.slots)
+        self.n_tok = dev(wl.n_tok) if wl.n_tok is not None else None
+        B, T = wl.B, wl.T
+        self.h = torch.empty(B, T, g.channels, device="cuda")
+        self.o = torch.empty(B, T, g.h_v, g.s, device="cuda")
+        self.y = torch.empty(B, T, g.h_v * g.s, device="cuda")
+
+    def run(self, t0: int = 0, t1=None, slots=None, n_tok="default"):
+        """One mixer pass over tokens [t0, t1) of every sequence (one call per kernel)."""
+        import torch
+        t1 = self.wl.T if t1 is None else t1
+        sl = lambda x: x[:, t0:t1].contiguous()
+        qkv, alpha, bl, z = sl(self.qkv), sl(self.alpha), sl(self.beta_logit), sl(self.z)
+        B, T = qkv.shape[0], qkv.shape[1]
+        g = self.geom
+        h = torch.empty(B, T, g.channels, device="cuda")
+        o = torch.empty(B, T, g.h_v, g.s, device="cuda")
+        y = torch.empty(B, T, g.h_v * g.s, device="cuda")
+        slots = self.slots if slots is None else slots
+        n_tok = self.n_tok if isinstance(n_tok, str) else n_tok
+        self.G.gdn_mixer(self.pool, qkv, alpha, bl, z, self.conv_w, self.dt, self.ssm_a, self.norm_w,
+                         self.wl.eps, h, o, y, slots, n_tok)
+        self.h[:, t0:t1] = h
+        self.o[:, t0:t1] = o
+        self.y[:, t0:t1] = y
+        return h, o, y
+
+    def slot_state(self, b: int):
+        return self.pool.state[int(self.wl.slots[b])].cpu().numpy()
+
+    def slot_conv(self, b: int):
+        return self.pool.conv[int(self.wl.slots[b])].cpu().numpy()

@@ -1,0 +1,171 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+The library must load, export every function include/gdn.h declares, and reject
+bad arguments with the documented codes before touching the device.
+"""
+import ctypes
+import os
+import re
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    from gated_deltanet_mixer_gdn_amd import gdn
+    if not os.path.exists(gdn.LIB_PATH):
+        from gated_deltanet_mixer_gdn_amd import _build
+        _build.build()
+    return gdn.load_library()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_declares_the_abi():
+    names = declared_functions()
+    for n in ("gdn_state_pool_create", "gdn_conv_silu_norm", "gdn_decode_step", "gdn_gated_rmsnorm",
+              "gdn_state_pool_zero", "gdn_last_error"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    from gated_deltanet_mixer_gdn_amd import gdn
+    for name in declared_functions():
+        assert hasattr(L, name), f"{name} is declared in gdn.h but not exported"
+    assert sorted(gdn.EXPORTS) == declared_functions()
+    out = subprocess.run(["nm", "-D", "--defined-only", gdn.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\sT\s(gdn_[a-z0-9_]+)$", out, flags=re.M))
+    assert exported == set(declared_functions())
+
+
+def test_library_is_built_for_gfx950_only(tmp_path):
+    from gated_deltanet_mixer_gdn_amd import gdn
+    fb = tmp_path / "fatbin.bin"
+    subprocess.check_call(["objcopy", "-O", "binary", "--only-section=.hip_fatbin", gdn.LIB_PATH, str(fb)])
+    out = subprocess.run(["/opt/rocm/llvm/bin/clang-offload-bundler", "--list", "--type=o",
+                          "--input=" + str(fb)], capture_output=True, text=True)
+    assert out.returncode == 0, out.stderr
+    targets = [t for t in out.stdout.split() if "amdgcn" in t]
+    assert targets and all(t.endswith("gfx950") for t in targets), targets
+
+
+def test_abi_version(L):
+    assert L.gdn_abi_version() == 1
+
+
+def _geom(h_k=16, h_v=48, s=128, d_conv=4):
+    from gated_deltanet_mixer_gdn_amd.gdn import gdn_geom
+    return gdn_geom(h_k, h_v, s, d_conv)
+
+
+def test_pool_bytes(L):
+    g = _geom()
+    n = L.gdn_state_pool_bytes(ctypes.byref(g), 3)
+    state = 3 * 48 * 128 * 128 * 4
+    conv = 3 * 10240 * 3 * 4
+    r = lambda x: (x + 255) // 256 * 256
+    assert n == 256 + r(state) + r(conv)
+    assert L.gdn_state_pool_bytes(ctypes.byref(g), 0) == 0
+    assert b"n_slots" in L.gdn_last_error()
+    assert L.gdn_state_pool_bytes(None, 3) == 0
+    bad = _geom(s=64)
+    assert L.gdn_state_pool_bytes(ctypes.byref(bad), 3) == 0
+    assert b"built for" in L.gdn_last_error()
+
+
+def test_pool_create_argument_errors(L):
+    from gated_deltanet_mixer_gdn_amd.gdn import GDN_ERR_ARG, GDN_ERR_UNSUPPORTED
+    g = _geom()
+    h = ctypes.c_void_p()
+    need = L.gdn_state_pool_bytes(ctypes.byref(g), 2)
+    assert L.gdn_state_pool_create(ctypes.byref(g), 2, 4096, need, None) == GDN_ERR_ARG
+    assert L.gdn_state_pool_create(ctypes.byref(g), 2, None, need, ctypes.byref(h)) == GDN_ERR_ARG
+    assert b"dev_base is null" in L.gdn_last_error()
+    assert L.gdn_state_pool_create(ctypes.byref(g), 2, 4096 + 16, need, ctypes.byref(h)) == GDN_ERR_ARG
+    assert b"256-byte" in L.gdn_last_error()
+    assert L.gdn_state_pool_create(ctypes.byref(g), 2, 4096, need - 1, ctypes.byref(h)) == GDN_ERR_ARG
+    assert L.gdn_state_pool_create(ctypes.byref(g), -1, 4096, need, ctypes.byref(h)) == GDN_ERR_ARG
+    odd = _geom(h_k=16, h_v=40)
+    assert L.gdn_state_pool_create(ctypes.byref(odd), 2, 4096, need, ctypes.byref(h)) == GDN_ERR_ARG
+    assert b"multiple" in L.gdn_last_error()
+    wide = _geom(d_conv=5)
+    assert L.gdn_state_pool_create(ctypes.byref(wide), 2, 4096, need, ctypes.byref(h)) == GDN_ERR_UNSUPPORTED
+    assert h.value is None
+
+
+def test_calls_on_null_pool_are_rejected(L):
+    from gated_deltanet_mixer_gdn_amd.gdn import GDN_ERR_ARG
+    assert L.gdn_conv_silu_norm(None, None, None, 1, 1, 16, 16, 1e-6, 16, None) == GDN_ERR_ARG
+    assert L.gdn_last_error().startswith(b"gdn_conv_silu_norm: pool is null")
+    assert L.gdn_decode_step(None, None, None, 1, 1, 16, 16, 16, 16, 16, 16, None) == GDN_ERR_ARG
+    assert L.gdn_last_error().startswith(b"gdn_decode_step: pool is null")
+    assert L.gdn_state_pool_zero(None, None, 0, None) == GDN_ERR_ARG
+    assert L.gdn_state_pool_state(None) is None
+    assert L.gdn_state_pool_slots(None) == 0
+    L.gdn_state_pool_destroy(None)
+
+
+def test_rmsnorm_argument_errors(L):
+    from gated_deltanet_mixer_gdn_amd.gdn import GDN_ERR_ARG, GDN_ERR_UNSUPPORTED, GDN_OK
+    assert L.gdn_gated_rmsnorm(16, 16, 16, 1e-6, 4, 64, 16, None) == GDN_ERR_UNSUPPORTED
+    assert L.gdn_gated_rmsnorm(16, 16, 16, 1e-6, -1, 128, 16, None) == GDN_ERR_ARG
+    assert L.gdn_gated_rmsnorm(16, 16, 16, float("nan"), 4, 128, 16, None) == GDN_ERR_ARG
+    assert L.gdn_gated_rmsnorm(16, 16, 16, -1.0, 4, 128, 16, None) == GDN_ERR_ARG
+    assert L.gdn_gated_rmsnorm(None, 16, 16, 1e-6, 4, 128, 16, None) == GDN_ERR_ARG
+    assert b"o is null" in L.gdn_last_error()
+    assert L.gdn_gated_rmsnorm(16, 16, 20, 1e-6, 4, 128, 16, None) == GDN_ERR_ARG
+    assert b"w is not 16-byte aligned" in L.gdn_last_error()
+    # z and y overlapping is refused; rows = 0 is a no-op that touches nothing
+    assert L.gdn_gated_rmsnorm(4096, 1 << 20, 16, 1e-6, 4, 128, 1 << 20, None) == GDN_ERR_ARG
+    assert L.gdn_gated_rmsnorm(None, None, None, 1e-6, 0, 128, None, None) == GDN_OK
+    assert L.gdn_last_error() == b""
+
+
+def test_last_error_is_thread_local(L):
+    import threading
+    L.gdn_gated_rmsnorm(16, 16, 16, 1e-6, 4, 64, 16, None)
+    seen = []
+    t = threading.Thread(target=lambda: seen.append(L.gdn_last_error()))
+    t.start()
+    t.join()
+    assert seen == [b""]
+    assert b"s=64" in L.gdn_last_error()
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    from gated_deltanet_mixer_gdn_amd import gdn
+    x = torch.zeros(4, 128)
+    with pytest.raises(ValueError):
+        gdn.gdn_gated_rmsnorm(x, x, torch.zeros(128), 1e-6, x)
+
+
+def test_product_path_does_not_reference_the_oracle():
+    """The HIP path and the oracle share no code; neither imports the other."""
+    pkg = os.path.join(ROOT, "gated_deltanet_mixer_gdn_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".h")):
+                src = open(os.path.join(dirpath, f)).read()
+                assert "oracle" not in src.lower().replace("oracle-free", ""), f
+                assert "gdn_workloads" not in src, f
+    for f in os.listdir(os.path.join(ROOT, "oracle")):
+        if f.endswith((".py", ".c", ".h")):
+            src = open(os.path.join(ROOT, "oracle", f)).read()
+            assert "gated_deltanet_mixer_gdn_amd" not in src and "gdn.h" not in src, f
+
+
+def test_import_without_gpu_does_not_load_library():
+    code = ("import gated_deltanet_mixer_gdn_amd.gdn as g, sys; "
+            "assert g._lib is None; print('ok')")
+    out = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True)
+    assert out.returncode == 0 and "ok" in out.stdout, out.stderr

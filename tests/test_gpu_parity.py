@@ -1,0 +1,325 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle on MI355X.
+
+Every workload is seeded and synthetic. Tolerances: max |gpu - ref| <= 1e-4 x
+max |ref| per decode step for o, y, h, state and conv state; <= 1e-3 x max |ref|
+after 512 sequential steps. Integer / placement results (untouched slots, skipped
+tokens, flags) are compared bit for bit.
+"""
+import numpy as np
+import pytest
+
+import gdn_workloads as W
+import oracle
+from gpu_harness import GpuMixer, assert_close, dev, log
+
+pytestmark = pytest.mark.gpu
+
+STEP_TOL = 1e-4
+LONG_TOL = 1e-3
+
+
+def _stack(results, key, n=None):
+    return np.stack([r[key] if n is None else r[key][:n] for r in results])
+
+
+def _compare_all(gm, wl, res, tol, tag):
+    """Compare o, y, h for every valid token and the final state / conv of every slot."""
+    o = gm.o.cpu().numpy()
+    y = gm.y.cpu().numpy()
+    h = gm.h.cpu().numpy()
+    st = gm.pool.state.cpu().numpy()
+    cv = gm.pool.conv.cpu().numpy()
+    errs = {}
+    for key, arr in (("o", o), ("y", y), ("h", h)):
+        g_parts, r_parts = [], []
+        for b in range(wl.B):
+            n = wl.tokens_of(b)
+            g_parts.append(arr[b, :n].reshape(-1))
+            r_parts.append(res[b][key].reshape(-1))
+            if n < wl.T:
+                assert (arr[b, n:] == 0).all(), f"{tag}: {key} of skipped tokens is not zero"
+        errs[key] = assert_close(f"{tag} {key}", np.concatenate(g_parts), np.concatenate(r_parts), tol)
+    sl = wl.slots
+    errs["state"] = assert_close(f"{tag} state", st[sl], _stack(res, "state"), tol)
+    errs["conv"] = assert_close(f"{tag} conv", cv[sl], _stack(res, "conv_state"), tol)
+    log(f"{tag}: rel errors " + ", ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    return st, cv
+
+
+# ------------------------------------------------------------------ the five workloads
+def test_tiny_b1_t8_every_step():
+    """One sequence, 8 sequential single-token calls, parity after every step."""
+    wl = W.tiny()
+    log("tiny_b1_t8: start")
+    gm = GpuMixer(wl)
+    st, cs = wl.state[0], wl.conv_state[0]
+    for t in range(wl.T):
+        h, o, y = gm.run(t, t + 1)
+        r = oracle.run_sequence(wl, 0, t, t + 1, state=st, conv_state=cs)
+        st, cs = r["state"], r["conv_state"]
+        assert_close(f"step {t} h", h.cpu().numpy()[0], r["h"], STEP_TOL)
+        assert_close(f"step {t} o", o.cpu().numpy()[0], r["o"], STEP_TOL)
+        assert_close(f"step {t} y", y.cpu().numpy()[0], r["y"], STEP_TOL)
+        assert_close(f"step {t} state", gm.slot_state(0), st, STEP_TOL)
+        assert_close(f"step {t} conv", gm.slot_conv(0), cs, STEP_TOL)
+    assert int(gm.pool.flags.item()) == 0
+
+
+def test_decode_b64_one_step():
+    wl = W.decode_b64()
+    log("decode_b64: start")
+    gm = GpuMixer(wl)
+    gm.run()
+    res = oracle.run_workload(wl)
+    _compare_all(gm, wl, res, STEP_TOL, "decode_b64")
+    assert int(gm.pool.flags.item()) == 0
+
+
+def test_decode_b256_one_step():
+    """The bandwidth-bound decode: 256 sequences, 768 MiB of state, in the launch
+    configuration the benchmark times."""
+    wl = W.decode_b256()
+    log("decode_b256: start")
+    gm = GpuMixer(wl)
+    gm.run()
+    log("decode_b256: gpu done, running oracle")
+    res = oracle.run_workload(wl)
+    _compare_all(gm, wl, res, STEP_TOL, "decode_b256")
+
+
+def test_prefill_b16_t512_state_on_chip():
+    """16 sequences x 512 tokens in ONE call: the state stays in VGPRs across the tokens."""
+    wl = W.prefill_b16_t512()
+    log("prefill_b16_t512: start")
+    gm = GpuMixer(wl)
+    gm.run()
+    log("prefill_b16_t512: gpu done, running oracle")
+    res = oracle.run_workload(wl)
+    # the first token is a plain decode step; after 512 steps the looser bound applies
+    assert_close("prefill o[t=0]", gm.o[:, 0].cpu().numpy(), _stack(res, "o")[:, 0], STEP_TOL)
+    assert_close("prefill h", gm.h.cpu().numpy(), _stack(res, "h"), STEP_TOL)
+    _compare_all(gm, wl, res, LONG_TOL, "prefill_b16_t512")
+
+
+def test_ragged_pool2048_b1024():
+    """2048-slot pool, 1024 sequences at random unique slots, U{1..8} tokens each, one call
+    with per-sequence token counts. Untouched slots stay bit-identical."""
+    import torch
+    wl = W.ragged_pool()
+    log(f"ragged: start, {int(wl.n_tok.sum())} seq-steps")
+    gm = GpuMixer(wl)
+    gm.run()
+    log("ragged: gpu done, running oracle")
+    res = oracle.run_workload(wl)
+    st, _ = _compare_all(gm, wl, res, STEP_TOL, "ragged")
+    untouched = np.setdiff1d(np.arange(wl.n_slots), wl.slots)
+    assert np.array_equal(st[untouched], wl.state[untouched]), "an untouched slot changed"
+    assert np.array_equal(gm.pool.conv.cpu().numpy()[untouched], wl.conv_state[untouched])
+    assert int(gm.pool.flags.item()) == 0
+
+    # The same work as continuous batching: call t advances only the sequences that still
+    # have a token t, gathered by slot.  Bitwise equal to the one-call form.
+    log("ragged: continuous-batching form")
+    gm2 = GpuMixer(wl)
+    for t in range(wl.T):
+        act = np.nonzero(wl.n_tok > t)[0]
+        if act.size == 0:
+            continue
+        idx = dev(act.astype(np.int64))
+        sub = lambda x: x[idx, t:t + 1].contiguous()
+        B = act.size
+        h = torch.empty(B, 1, wl.geom.channels, device="cuda")
+        o = torch.empty(B, 1, wl.geom.h_v, wl.geom.s, device="cuda")
+        y = torch.empty(B, 1, wl.geom.value_dim, device="cuda")
+        gm2.G.gdn_mixer(gm2.pool, sub(gm2.qkv), sub(gm2.alpha), sub(gm2.beta_logit), sub(gm2.z),
+                        gm2.conv_w, gm2.dt, gm2.ssm_a, gm2.norm_w, wl.eps, h, o, y, gm2.slots[idx].contiguous())
+        gm2.o[idx, t:t + 1] = o
+        gm2.y[idx, t:t + 1] = y
+    assert torch.equal(gm2.pool.state, gm.pool.state)
+    assert torch.equal(gm2.pool.conv, gm.pool.conv)
+    mask = torch.arange(wl.T, device="cuda")[None, :] < gm.n_tok[:, None].long()
+    assert torch.equal(gm2.o[mask], gm.o[mask])
+    assert torch.equal(gm2.y[mask], gm.y[mask])
+
+
+# ------------------------------------------------------------------ properties and edges
+SMALL_GEOMS = [W.Geom(h_k=1, h_v=3), W.Geom(h_k=2, h_v=4), W.Geom(h_k=2, h_v=6)]
+
+
+@pytest.mark.parametrize("geom", SMALL_GEOMS, ids=lambda g: f"hk{g.h_k}hv{g.h_v}")
+@pytest.mark.parametrize("B,T", [(1, 1), (5, 11), (3, 17)])
+def test_small_geometries_several_tiles_ragged_tail(geom, B, T):
+    """Other head counts of the family; T spans several 8-token conv blocks with a tail."""
+    wl = W.make("small", B, T, seed=40 + B + T + geom.h_v, geom=geom, n_slots=B + 2, state_std=0.05,
+                conv_std=1.0, slot_choice="random")
+    log(f"small geometry h_k={geom.h_k} h_v={geom.h_v} B={B} T={T}")
+    gm = GpuMixer(wl)
+    gm.run()
+    res = oracle.run_workload(wl)
+    _compare_all(gm, wl, res, STEP_TOL if T == 1 else 2 * STEP_TOL, "small")
+
+
+def test_chunked_calls_equal_one_call_bitwise():
+    """T tokens in one call equal the same tokens split over several calls, bit for bit
+    (the multi-token path must reproduce the single-token decode exactly)."""
+    import torch
+    wl = W.make("chunk", 4, 20, seed=50, state_std=0.02, conv_std=1.0)
+    log("chunked vs one call")
+    a = GpuMixer(wl)
+    a.run()
+    b = GpuMixer(wl)
+    for t0, t1 in [(0, 1), (1, 8), (8, 9), (9, 20)]:
+        b.run(t0, t1)
+    assert torch.equal(a.pool.state, b.pool.state)
+    assert torch.equal(a.pool.conv, b.pool.conv)
+    assert torch.equal(a.o, b.o) and torch.equal(a.y, b.y) and torch.equal(a.h, b.h)
+
+
+def test_batch_order_invariance():
+    import torch
+    wl = W.make("perm", 6, 3, seed=51, n_slots=9, state_std=0.02, conv_std=1.0, slot_choice="random")
+    log("batch order invariance")
+    a = GpuMixer(wl)
+    a.run()
+    perm = np.array([3, 0, 5, 1, 4, 2])
+    wl2 = W.make("perm", 6, 3, seed=51, n_slots=9, state_std=0.02, conv_std=1.0, slot_choice="random")
+    for f in ("qkv", "alpha", "beta_logit", "z", "slots"):
+        setattr(wl2, f, getattr(wl2, f)[perm].copy())
+    b = GpuMixer(wl2)
+    b.run()
+    assert torch.equal(a.pool.state, b.pool.state)
+    assert torch.equal(a.o[dev(perm)], b.o)
+    assert torch.equal(a.y[dev(perm)], b.y)
+
+
+def test_beta0_gate0_leaves_state_bit_identical():
+    """beta logit = -inf gives beta = 0 and ssm_a = 0 gives exp(g) = 1 exactly."""
+    import torch
+    wl = W.make("inv", 3, 2, seed=52, state_std=0.02, conv_std=1.0)
+    wl.beta_logit[:] = -np.inf
+    wl.ssm_a[:] = 0.0
+    gm = GpuMixer(wl)
+    before = gm.pool.state.clone()
+    gm.run()
+    assert torch.equal(gm.pool.state, before)
+    res = oracle.run_workload(wl)
+    _compare_all(gm, wl, res, STEP_TOL, "beta0")
+
+
+def test_beta1_unit_k_recalls_v():
+    """beta = 1, decay 1: after the step S^T k = v for the (unit) k of each head."""
+    wl = W.make("recall", 2, 1, seed=53, state_std=0.02, conv_std=1.0)
+    wl.beta_logit[:] = np.inf
+    wl.ssm_a[:] = 0.0
+    gm = GpuMixer(wl)
+    gm.run()
+    h = gm.h.cpu().numpy()
+    st = gm.pool.state.cpu().numpy()
+    g = wl.geom
+    for b in range(2):
+        for i in range(g.h_v):
+            j = i // (g.h_v // g.h_k)
+            k = h[b, 0, (g.h_k + j) * g.s:(g.h_k + j + 1) * g.s].astype(np.float64)
+            v = h[b, 0, (2 * g.h_k + i) * g.s:(2 * g.h_k + i + 1) * g.s].astype(np.float64)
+            kv = st[b, i].astype(np.float64).T @ k
+            assert np.abs(kv - v).max() <= STEP_TOL * np.abs(v).max()
+
+
+def test_zero_tokens_and_bad_counts():
+    """n_tok = 0 leaves a slot untouched and writes zeros; counts outside [0, T] are
+    clamped and flagged."""
+    import torch
+    wl = W.make("ntok", 4, 5, seed=54, n_slots=6, state_std=0.02, conv_std=1.0, slot_choice="random")
+    wl.n_tok = np.array([0, 5, 2, 3], np.int32)
+    gm = GpuMixer(wl)
+    gm.run()
+    assert int(gm.pool.flags.item()) == 0
+    st = gm.pool.state.cpu().numpy()
+    assert np.array_equal(st[wl.slots[0]], wl.state[wl.slots[0]])
+    assert (gm.o[0] == 0).all() and (gm.h[0] == 0).all()
+    res = oracle.run_workload(wl)
+    _compare_all(gm, wl, res, STEP_TOL * 2, "ntok")
+    # out-of-range counts: 9 -> 5 (T) and -3 -> 0, with the flag raised
+    wl2 = W.make("ntok", 2, 5, seed=55, state_std=0.02, conv_std=1.0)
+    gm2 = GpuMixer(wl2)
+    before = gm2.pool.state.clone()
+    gm2.run(n_tok=dev(np.array([9, -3], np.int32)))
+    assert int(gm2.pool.flags.item()) & gm2.G.GDN_FLAG_BAD_NTOK
+    assert torch.equal(gm2.pool.state[1], before[1])
+    wl2.n_tok = np.array([5, 0], np.int32)
+    res2 = oracle.run_workload(wl2)
+    _compare_all(gm2, wl2, res2, STEP_TOL * 2, "ntok-clamped")
+
+
+def test_bad_slot_is_skipped_and_flagged():
+    import torch
+    wl = W.make("badslot", 3, 2, seed=56, n_slots=4, state_std=0.02, conv_std=1.0)
+    gm = GpuMixer(wl)
+    before = gm.pool.state.clone()
+    bad = dev(np.array([0, 7, -1], np.int32))
+    gm.run(slots=bad)
+    assert int(gm.pool.flags.item()) & gm.G.GDN_FLAG_BAD_SLOT
+    assert (gm.o[1:] == 0).all() and (gm.y[1:] == 0).all() and (gm.h[1:] == 0).all()
+    assert torch.equal(gm.pool.state[1:], before[1:])
+    res = oracle.run_workload(wl, seqs=[0])
+    assert_close("badslot o", gm.o[0].cpu().numpy(), res[0]["o"], STEP_TOL)
+
+
+def test_pool_zero():
+    import torch
+    wl = W.make("zero", 2, 1, seed=57, n_slots=5, state_std=0.02, conv_std=1.0)
+    gm = GpuMixer(wl)
+    gm.pool.flags.fill_(3)
+    gm.pool.zero(dev(np.array([1, 3], np.int32)))
+    st, cv = gm.pool.state.cpu().numpy(), gm.pool.conv.cpu().numpy()
+    assert (st[[1, 3]] == 0).all() and (cv[[1, 3]] == 0).all()
+    assert np.array_equal(st[[0, 2, 4]], wl.state[[0, 2, 4]])
+    assert int(gm.pool.flags.item()) == 3
+    gm.pool.zero()
+    assert int(torch.count_nonzero(gm.pool.state)) == 0 and int(torch.count_nonzero(gm.pool.conv)) == 0
+    assert int(gm.pool.flags.item()) == 0
+
+
+def test_gated_rmsnorm_ragged_rows_and_in_place():
+    import torch
+    import gated_deltanet_mixer_gdn_amd as G
+    rng = np.random.default_rng(58)
+    for rows in (1, 7, 13, 1031):
+        o = rng.standard_normal((rows, 128)).astype(np.float32) * rng.uniform(0.01, 10, (rows, 1)).astype(np.float32)
+        z = rng.standard_normal((rows, 128)).astype(np.float32)
+        w = (1 + 0.1 * rng.standard_normal(128)).astype(np.float32)
+        ref = oracle.gated_rmsnorm(o, z, w, 1e-6)
+        od = dev(o)
+        y = torch.empty_like(od)
+        G.gdn_gated_rmsnorm(od, dev(z), dev(w), 1e-6, y)
+        assert_close(f"rmsnorm rows={rows}", y.cpu().numpy(), ref, STEP_TOL)
+        G.gdn_gated_rmsnorm(od, dev(z), dev(w), 1e-6, od)   # y aliasing o
+        assert torch.equal(od, y)
+
+
+def test_empty_batch_is_a_no_op():
+    import torch
+    import gated_deltanet_mixer_gdn_amd as G
+    pool = G.StatePool(2)
+    pool.zero()
+    e = torch.empty(0, 1, 10240, device="cuda")
+    G.gdn_conv_silu_norm(pool, e, torch.zeros(10240, 4, device="cuda"), 1e-6, torch.empty_like(e))
+    G.gdn_decode_step(pool, e, torch.empty(0, 1, 48, device="cuda"), torch.empty(0, 1, 48, device="cuda"),
+                      torch.zeros(48, device="cuda"), torch.zeros(48, device="cuda"),
+                      torch.empty(0, 1, 48, 128, device="cuda"))
+    torch.cuda.synchronize()
+    assert int(torch.count_nonzero(pool.state)) == 0
+
+
+def test_abi_rejects_bad_arguments_on_device():
+    import torch
+    import gated_deltanet_mixer_gdn_amd as G
+    pool = G.StatePool(2)
+    x = torch.zeros(1, 1, 10240, device="cuda")
+    with pytest.raises(G.GdnError) as e:
+        G.gdn_conv_silu_norm(pool, x, torch.zeros(10240, 4, device="cuda"), 1e-6, x)   # h aliases qkv
+    assert e.value.code == G.GDN_ERR_ARG and "overlaps" in str(e.value)
+    with pytest.raises(G.GdnError):
+        G.gdn_decode_step(pool, torch.zeros(3, 1, 10240, device="cuda"), torch.zeros(3, 1, 48, device="cuda"),
+                          torch.zeros(3, 1, 48, device="cuda"), torch.zeros(48, device="cuda"),
+                          torch.zeros(48, device="cuda"), torch.zeros(3, 1, 48, 128, device="cuda"))  # B > n_slots
