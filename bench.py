@@ -174,21 +174,30 @@ def main():
 
     for _ in range(args.warmup):
         step()
-    torch.cuda.synchronize()
-    # wall-clock timed region (no events inside)
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    wall_s = time.perf_counter() - t0
-    # per-kernel durations: the same steps again with event pairs on the launch stream
+    # the timed region: K steps between two synchronisations, wall clock around it, and
+    # event pairs around every kernel launch on the stream the kernels run on
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
+    t0 = time.perf_counter()
     for k in range(args.steps):
         step(evs[k])
     torch.cuda.synchronize()
+    wall_s = time.perf_counter() - t0
     k_ms = {name: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs]))
             for i, name in enumerate(("conv", "step", "norm"))}
+    # context: a plain device-to-device copy of the state's size on the same stream
+    ref_src = pool.state.view(-1)
+    ref_dst = torch.empty_like(ref_src)
+    for _ in range(3):
+        ref_dst.copy_(ref_src)
+    ce = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ce[0].record(stream)
+    for _ in range(20):
+        ref_dst.copy_(ref_src)
+    ce[1].record(stream)
+    torch.cuda.synchronize()
+    copy_gbps = 2 * ref_src.numel() * 4 * 20 / (ce[0].elapsed_time(ce[1]) / 1000.0) / 1e9
+    del ref_dst
     flags = int(pool.flags.item())
     if flags:
         raise SystemExit(f"bench.py: device flag word set ({flags:#x})")
@@ -199,7 +208,8 @@ def main():
     achieved = nbytes["step"] / (k_ms["step"] / 1000.0) / 1e9
     mixer_gbps = sum(nbytes.values()) / (ms_per_step / 1000.0) / 1e9
     log(f"kernel ms: " + ", ".join(f"{k}={v * 1000:.1f}us" for k, v in k_ms.items()) +
-        f"; step {ms_per_step * 1000:.1f} us; decode kernel {achieved:.0f} GB/s; mixer {mixer_gbps:.0f} GB/s")
+        f"; step {ms_per_step * 1000:.1f} us; decode kernel {achieved:.0f} GB/s; mixer {mixer_gbps:.0f} GB/s; "
+        f"d2d copy {copy_gbps:.0f} GB/s")
     traffic = read_traffic() if args.config == "b256" else None
 
     cpu = None
@@ -227,6 +237,7 @@ def main():
         "hbm_gbps_mixer": mixer_gbps,
         "hbm_frac_mixer": mixer_gbps / HBM_PEAK_GBPS,
         "kernel_us": {k: v * 1000.0 for k, v in k_ms.items()},
+        "d2d_copy_gbps_same_size": copy_gbps,
         "roofline": {"kernel": "decode_step_kernel", "bound": "hbm", "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": traffic, "algorithmic_bytes_per_launch": nbytes["step"]},
