@@ -2,18 +2,22 @@
 """Benchmark of the GDN decode mixer on one MI355X.
 
 A step is one pass of the whole mixer (conv/SiLU/L2 -> gated delta rule -> gated
-RMSNorm, three kernels) over one batch: by default the bandwidth-bound decode of
-256 sequences x 1 token (768 MiB of fp32 state), inputs already in HBM.  Prints
-ONE JSON line on stdout; diagnostics go to stderr.
+RMSNorm) over one batch: by default the bandwidth-bound decode of 256 sequences x
+1 token (768 MiB of fp32 state), inputs already in HBM.  The timed step is two
+launches, gdn_conv_silu_norm and gdn_decode_step_norm (the recurrence with the
+norm fused into its epilogue, writing y only); the three-call form (o through
+HBM, separate gdn_gated_rmsnorm) is timed beside it.  Prints ONE JSON line on
+stdout; diagnostics go to stderr.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--config b256]
                   [--cpu-seconds S | --no-cpu-baseline] [--copy-probe-mib M]
 
-The `roofline` object is for the dominant kernel (decode_step_kernel): its
-algorithmic bytes per launch over its average launch time, measured with HIP
-events recorded on the stream the kernels run on.  `traffic` (HBM bytes per
+The `roofline` object is for the dominant kernel (decode_one_kernel<fused norm>):
+its algorithmic bytes per launch over its average launch time, measured with HIP
+events recorded on the stream the kernels run on, around the kernels of every
+8th step of the timed region.  `traffic` (HBM bytes per
 launch from rocprofv3 FETCH_SIZE / WRITE_SIZE counters, scaled by a copy-kernel
-calibration) is read from profiles/decode_step_b256_traffic.txt and reported only
+calibration) is read from profiles/decode_one_fused_b256_traffic.txt and reported only
 while the kernel source it was measured on is unchanged.
 """
 import argparse
@@ -28,7 +32,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0            # MI355X HBM3E, published peak
 KERNEL_SRC = os.path.join(ROOT, "gated_deltanet_mixer_gdn_amd", "csrc", "gdn_kernels.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_step_b256_traffic.txt")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_one_fused_b256_traffic.txt")
 
 
 def log(*a):
@@ -57,19 +61,23 @@ def read_traffic():
 
 
 def algorithmic_bytes(wl):
-    """Bytes each kernel must move at minimum (inputs read once, outputs written once)."""
+    """Bytes each kernel must move at minimum (inputs read once, outputs written once).
+    "step" is the recurrence writing o; "step_norm" the recurrence with the gated RMSNorm
+    fused in, reading z and writing y only."""
     g = wl.geom
-    C, V, S, hv = g.channels, g.value_dim, g.s, g.h_v
+    C, S, hv = g.channels, g.s, g.h_v
     tok = int(wl.B * wl.T if wl.n_tok is None else wl.n_tok.sum())
     seqs = int(wl.B if wl.n_tok is None else (wl.n_tok > 0).sum())
     all_tok = wl.B * wl.T
+    row = hv * S * 4                           # one token's o, z or y
     conv = tok * C * 4 + all_tok * C * 4 + seqs * C * (g.d_conv - 1) * 4 * 2 + C * g.d_conv * 4
-    step = (seqs * hv * S * S * 4 * 2          # state read + write, once per call
+    core = (seqs * hv * S * S * 4 * 2          # state read + write, once per call
             + tok * (C * 4 + 2 * hv * 4)       # h (q|k|v) and alpha / beta logits of each token
-            + all_tok * hv * S * 4             # o
             + 2 * hv * 4)                      # dt, ssm_a
-    norm = all_tok * hv * S * 4 * 3 + S * 4    # o, z in; y out; norm weight
-    return {"conv": conv, "step": step, "norm": norm}, tok * hv
+    return {"conv": conv,
+            "step": core + all_tok * row,                                  # o
+            "norm": all_tok * row * 3 + S * 4,                             # o, z in; y out; weight
+            "step_norm": core + tok * row + all_tok * row + S * 4}, tok * hv   # z in, y out
 
 
 def cpu_baseline(wl, seconds: float):
@@ -117,6 +125,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0)
+    ap.add_argument("--event-every", type=int, default=8,
+                    help="record per-kernel HIP events on every N-th timed step")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -159,7 +169,20 @@ def main():
     y = torch.empty(wl.B, wl.T, g.value_dim, device="cuda")
     stream = torch.cuda.current_stream()
 
-    def step(ev=None):
+    def step_fused(ev=None):
+        # the timed hot path: conv/SiLU/L2, then the recurrence with the gated RMSNorm
+        # fused into its epilogue (y only, like the pages' fused step + norm kernel)
+        if ev:
+            ev[0].record(stream)
+        G.gdn_conv_silu_norm(pool, qkv, conv_w, wl.eps, h, slots, n_tok)
+        if ev:
+            ev[1].record(stream)
+        G.gdn_decode_step_norm(pool, h, alpha, bl, dt, ssm_a, z, norm_w, wl.eps, y, None, slots, n_tok)
+        if ev:
+            ev[2].record(stream)
+
+    def step_three(ev=None):
+        # the same pass as three separate calls (o goes through HBM)
         if ev:
             ev[0].record(stream)
         G.gdn_conv_silu_norm(pool, qkv, conv_w, wl.eps, h, slots, n_tok)
@@ -172,19 +195,28 @@ def main():
         if ev:
             ev[3].record(stream)
 
-    for _ in range(args.warmup):
-        step()
-    # the timed region: K steps between two synchronisations, wall clock around it, and
-    # event pairs around every kernel launch on the stream the kernels run on
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for k in range(args.steps):
-        step(evs[k])
-    torch.cuda.synchronize()
-    wall_s = time.perf_counter() - t0
-    k_ms = {name: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs]))
-            for i, name in enumerate(("conv", "step", "norm"))}
+    def timed(fn, n_ev, names):
+        for _ in range(args.warmup):
+            fn()
+        # The timed region: K steps between two synchronisations, wall clock around it.
+        # HIP events on the launch stream bracket every kernel of every `every`-th step
+        # of this same region (an event record costs a few microseconds, so recording
+        # them on every step would inflate the step time it is meant to explain).
+        every = max(1, args.event_every)
+        sampled = range(0, args.steps, every)
+        evs = {k: [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for k in sampled}
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for k in range(args.steps):
+            fn(evs.get(k))
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        k_ms = {name: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs.values()]))
+                for i, name in enumerate(names)}
+        return wall * 1000.0 / args.steps, k_ms, len(evs)
+
+    three_ms, three_k, _ = timed(step_three, 4, ("conv", "step", "norm"))
+    ms_per_step, k_ms, n_samples = timed(step_fused, 3, ("conv", "step_norm"))
     # context: a plain device-to-device copy of the state's size on the same stream
     ref_src = pool.state.view(-1)
     ref_dst = torch.empty_like(ref_src)
@@ -202,14 +234,16 @@ def main():
     if flags:
         raise SystemExit(f"bench.py: device flag word set ({flags:#x})")
 
-    ms_per_step = wall_s * 1000.0 / args.steps
     nbytes, units = algorithmic_bytes(wl)
     value = units / (ms_per_step / 1000.0)
-    achieved = nbytes["step"] / (k_ms["step"] / 1000.0) / 1e9
-    mixer_gbps = sum(nbytes.values()) / (ms_per_step / 1000.0) / 1e9
-    log(f"kernel ms: " + ", ".join(f"{k}={v * 1000:.1f}us" for k, v in k_ms.items()) +
-        f"; step {ms_per_step * 1000:.1f} us; decode kernel {achieved:.0f} GB/s; mixer {mixer_gbps:.0f} GB/s; "
-        f"d2d copy {copy_gbps:.0f} GB/s")
+    achieved = nbytes["step_norm"] / (k_ms["step_norm"] / 1000.0) / 1e9
+    mixer_bytes = nbytes["conv"] + nbytes["step_norm"]
+    mixer_gbps = mixer_bytes / (ms_per_step / 1000.0) / 1e9
+    three_step_gbps = nbytes["step"] / (three_k["step"] / 1000.0) / 1e9
+    log("fused step: " + ", ".join(f"{k}={v * 1000:.1f}us" for k, v in k_ms.items()) +
+        f"; {ms_per_step * 1000:.1f} us/step; recurrence+norm kernel {achieved:.0f} GB/s; mixer {mixer_gbps:.0f} GB/s")
+    log("three calls: " + ", ".join(f"{k}={v * 1000:.1f}us" for k, v in three_k.items()) +
+        f"; {three_ms * 1000:.1f} us/step; recurrence kernel {three_step_gbps:.0f} GB/s; d2d copy {copy_gbps:.0f} GB/s")
     traffic = read_traffic() if args.config == "b256" else None
 
     cpu = None
@@ -234,13 +268,20 @@ def main():
         "config": {"workload": wl.name, "B": wl.B, "T": wl.T, "n_slots": wl.n_slots,
                    "h_k": g.h_k, "h_v": g.h_v, "S": g.s, "d_conv": g.d_conv,
                    "state_bytes": int(wl.n_slots * g.h_v * g.s * g.s * 4), "parallelism": "none"},
+        "path": "gdn_conv_silu_norm + gdn_decode_step_norm (gated RMSNorm fused, y only)",
         "hbm_gbps_mixer": mixer_gbps,
         "hbm_frac_mixer": mixer_gbps / HBM_PEAK_GBPS,
         "kernel_us": {k: v * 1000.0 for k, v in k_ms.items()},
+        "three_call_path": {"ms_per_step": three_ms, "kernel_us": {k: v * 1000.0 for k, v in three_k.items()},
+                            "value": units / (three_ms / 1000.0),
+                            "recurrence_kernel_gbps": three_step_gbps},
         "d2d_copy_gbps_same_size": copy_gbps,
-        "roofline": {"kernel": "decode_step_kernel", "bound": "hbm", "achieved": achieved,
-                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
-                     "traffic": traffic, "algorithmic_bytes_per_launch": nbytes["step"]},
+        "roofline": {"kernel": "decode_one_kernel<fused norm>" if wl.T == 1 else "decode_multi_kernel<fused norm>",
+                     "bound": "hbm",
+                     "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
+                     "algorithmic_bytes_per_launch": nbytes["step_norm"],
+                     "event_samples": n_samples},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -234,13 +234,21 @@ int gdn_conv_silu_norm(gdn_pool* p, const int32_t* slots, const int32_t* n_tok, 
     return launched(gdn::launch_conv_silu_norm(c, static_cast<hipStream_t>(stream)), fn);
 }
 
-int gdn_decode_step(gdn_pool* p, const int32_t* slots, const int32_t* n_tok, int32_t B, int32_t T,
-                    const float* h, const float* alpha, const float* beta_logit, const float* dt,
-                    const float* ssm_a, float* o, void* stream) {
-    const char* fn = "gdn_decode_step";
+}  // extern "C"
+
+namespace {
+
+// Shared by gdn_decode_step (o required, no epilogue) and gdn_decode_step_norm
+// (y required, o optional).
+int decode_common(const char* fn, gdn_pool* p, const int32_t* slots, const int32_t* n_tok, int32_t B,
+                  int32_t T, const float* h, const float* alpha, const float* beta_logit, const float* dt,
+                  const float* ssm_a, const float* z, const float* norm_w, float eps, float* o, float* y,
+                  void* stream) {
     if (int rc = check_pool(p, fn)) return rc;
     if (B < 0) return fail(GDN_ERR_ARG, fn, "B=%d is negative", B);
     if (T < 1) return fail(GDN_ERR_ARG, fn, "T=%d must be >= 1", T);
+    if (y && (!(eps >= 0.0f) || !std::isfinite(eps)))
+        return fail(GDN_ERR_ARG, fn, "eps must be finite and >= 0");
     if (B == 0) return ok();
     if ((int64_t) B * p->g.h_v > INT32_MAX) return fail(GDN_ERR_ARG, fn, "B*h_v too large");
     if (int rc = check_f4(h, fn, "h")) return rc;
@@ -248,7 +256,13 @@ int gdn_decode_step(gdn_pool* p, const int32_t* slots, const int32_t* n_tok, int
     if (int rc = check_f1(beta_logit, fn, "beta_logit")) return rc;
     if (int rc = check_f1(dt, fn, "dt")) return rc;
     if (int rc = check_f1(ssm_a, fn, "ssm_a")) return rc;
-    if (int rc = check_f4(o, fn, "o")) return rc;
+    if (o || !y)
+        if (int rc = check_f4(o, fn, "o")) return rc;
+    if (y) {
+        if (int rc = check_f4(z, fn, "z")) return rc;
+        if (int rc = check_f4(norm_w, fn, "norm_w")) return rc;
+        if (int rc = check_f4(y, fn, "y")) return rc;
+    }
     if (slots && !aligned(slots, 4)) return fail(GDN_ERR_ARG, fn, "slots is not 4-byte aligned");
     if (n_tok && !aligned(n_tok, 4)) return fail(GDN_ERR_ARG, fn, "n_tok is not 4-byte aligned");
     if (!slots && B > p->n_slots)
@@ -256,9 +270,15 @@ int gdn_decode_step(gdn_pool* p, const int32_t* slots, const int32_t* n_tok, int
                     (long long) p->n_slots);
     const size_t o_bytes = (size_t) B * T * p->g.h_v * p->g.s * sizeof(float);
     const size_t h_bytes = (size_t) B * T * channels(p->g) * sizeof(float);
-    if (overlap(o, o_bytes, h, h_bytes)) return fail(GDN_ERR_ARG, fn, "o overlaps h");
     const size_t pool_bytes = (size_t) ((p->base + p->bytes) - reinterpret_cast<char*>(p->state));
-    if (overlap(o, o_bytes, p->state, pool_bytes)) return fail(GDN_ERR_ARG, fn, "o overlaps the pool");
+    for (float* out : {o, y}) {
+        if (!out) continue;
+        const char* name = out == o ? "o" : "y";
+        if (overlap(out, o_bytes, h, h_bytes)) return fail(GDN_ERR_ARG, fn, "%s overlaps h", name);
+        if (overlap(out, o_bytes, p->state, pool_bytes)) return fail(GDN_ERR_ARG, fn, "%s overlaps the pool", name);
+    }
+    if (o && y && overlap(o, o_bytes, y, o_bytes)) return fail(GDN_ERR_ARG, fn, "o overlaps y");
+    if (y && overlap(y, o_bytes, z, o_bytes)) return fail(GDN_ERR_ARG, fn, "y overlaps z");
     gdn::StepParams s;
     s.state = p->state;
     s.slots = slots;
@@ -269,6 +289,9 @@ int gdn_decode_step(gdn_pool* p, const int32_t* slots, const int32_t* n_tok, int
     s.dt = dt;
     s.ssm_a = ssm_a;
     s.o = o;
+    s.z = y ? z : nullptr;
+    s.norm_w = y ? norm_w : nullptr;
+    s.y = y;
     s.flags = p->flags;
     s.n_slots = p->n_slots;
     s.B = B;
@@ -276,7 +299,29 @@ int gdn_decode_step(gdn_pool* p, const int32_t* slots, const int32_t* n_tok, int
     s.h_k = p->g.h_k;
     s.h_v = p->g.h_v;
     s.group = p->g.h_v / p->g.h_k;
+    s.eps = eps;
     return launched(gdn::launch_decode_step(s, static_cast<hipStream_t>(stream)), fn);
+}
+
+}  // namespace
+
+extern "C" {
+
+int gdn_decode_step(gdn_pool* p, const int32_t* slots, const int32_t* n_tok, int32_t B, int32_t T,
+                    const float* h, const float* alpha, const float* beta_logit, const float* dt,
+                    const float* ssm_a, float* o, void* stream) {
+    return decode_common("gdn_decode_step", p, slots, n_tok, B, T, h, alpha, beta_logit, dt, ssm_a, nullptr,
+                         nullptr, 0.0f, o, nullptr, stream);
+}
+
+int gdn_decode_step_norm(gdn_pool* p, const int32_t* slots, const int32_t* n_tok, int32_t B, int32_t T,
+                         const float* h, const float* alpha, const float* beta_logit, const float* dt,
+                         const float* ssm_a, const float* z, const float* norm_w, float eps, float* o,
+                         float* y, void* stream) {
+    const char* fn = "gdn_decode_step_norm";
+    if (!y) return fail(GDN_ERR_ARG, fn, "y is null");
+    return decode_common(fn, p, slots, n_tok, B, T, h, alpha, beta_logit, dt, ssm_a, z, norm_w, eps, o, y,
+                         stream);
 }
 
 int gdn_gated_rmsnorm(const float* o, const float* z, const float* w, float eps, int64_t rows, int32_t s,

@@ -42,10 +42,14 @@ struct StepParams {
     const float* beta_logit;
     const float* dt;        // [h_v]
     const float* ssm_a;     // [h_v]
-    float* o;               // [B][T][h_v][128]
+    float* o;               // [B][T][h_v][128], or null (fused form only)
+    const float* z;         // fused gated RMSNorm epilogue: [B][T][h_v*128], or null
+    const float* norm_w;    // [128]
+    float* y;               // [B][T][h_v*128], or null: no epilogue
     uint32_t* flags;
     long long n_slots;
     int B, T, h_k, h_v, group;  // group = h_v / h_k
+    float eps;              // RMSNorm epsilon (epilogue only)
 };
 
 struct NormParams {

@@ -21,7 +21,7 @@ EXPORTS = (
     "gdn_abi_version", "gdn_last_error", "gdn_state_pool_bytes", "gdn_state_pool_create",
     "gdn_state_pool_destroy", "gdn_state_pool_state", "gdn_state_pool_conv", "gdn_state_pool_flags",
     "gdn_state_pool_slots", "gdn_state_pool_zero", "gdn_conv_silu_norm", "gdn_decode_step",
-    "gdn_gated_rmsnorm",
+    "gdn_decode_step_norm", "gdn_gated_rmsnorm",
 )
 
 
@@ -80,6 +80,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "gdn_state_pool_zero": ([vp, vp, i32, vp], ctypes.c_int),
         "gdn_conv_silu_norm": ([vp, vp, vp, i32, i32, vp, vp, f32, vp, vp], ctypes.c_int),
         "gdn_decode_step": ([vp, vp, vp, i32, i32, vp, vp, vp, vp, vp, vp, vp], ctypes.c_int),
+        "gdn_decode_step_norm": ([vp, vp, vp, i32, i32, vp, vp, vp, vp, vp, vp, vp, f32, vp, vp, vp],
+                                 ctypes.c_int),
         "gdn_gated_rmsnorm": ([vp, vp, vp, f32, i64, i32, vp, vp], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
@@ -198,6 +200,21 @@ def gdn_decode_step(pool: StatePool, h, alpha, beta_logit, dt, ssm_a, o, slots=N
                                           *ptrs, _stream(h)))
 
 
+def gdn_decode_step_norm(pool: StatePool, h, alpha, beta_logit, dt, ssm_a, z, norm_w, eps: float, y,
+                         o=None, slots=None, n_tok=None):
+    """gdn_decode_step with the gated RMSNorm fused in; y [B][T][h_v*s]; o optional."""
+    g = pool.geom
+    B, T = h.shape[0], h.shape[1]
+    ptrs = (_f32(h, "h", (B, T, g.channels)), _f32(alpha, "alpha", (B, T, g.h_v)),
+            _f32(beta_logit, "beta_logit", (B, T, g.h_v)), _f32(dt, "dt", (g.h_v,)),
+            _f32(ssm_a, "ssm_a", (g.h_v,)), _f32(z, "z", (B, T, g.h_v * g.s)),
+            _f32(norm_w, "norm_w", (g.s,)))
+    o_ptr = None if o is None else _f32(o, "o", (B, T, g.h_v, g.s))
+    _check(load_library().gdn_decode_step_norm(pool.handle, _i32(slots, "slots", B), _i32(n_tok, "n_tok", B),
+                                               B, T, *ptrs, float(eps), o_ptr,
+                                               _f32(y, "y", (B, T, g.h_v * g.s)), _stream(h)))
+
+
 def gdn_gated_rmsnorm(o, z, w, eps: float, y):
     """o, z, y: any contiguous float32 layout whose last axis is s = 128 rows; w [s]."""
     s = w.shape[-1]
@@ -210,8 +227,12 @@ def gdn_gated_rmsnorm(o, z, w, eps: float, y):
 
 
 def gdn_mixer(pool: StatePool, qkv, alpha, beta_logit, z, conv_w, dt, ssm_a, norm_w, eps: float,
-              h, o, y, slots=None, n_tok=None):
-    """One pass of the whole mixer: the three ABI calls in the layer's order."""
+              h, o, y, slots=None, n_tok=None, fused: bool = False):
+    """One pass of the whole mixer in the layer's order: three ABI calls, or two with
+    the gated RMSNorm fused into the recurrence (o is then optional)."""
     gdn_conv_silu_norm(pool, qkv, conv_w, eps, h, slots, n_tok)
-    gdn_decode_step(pool, h, alpha, beta_logit, dt, ssm_a, o, slots, n_tok)
-    gdn_gated_rmsnorm(o, z, norm_w, eps, y)
+    if fused:
+        gdn_decode_step_norm(pool, h, alpha, beta_logit, dt, ssm_a, z, norm_w, eps, y, o, slots, n_tok)
+    else:
+        gdn_decode_step(pool, h, alpha, beta_logit, dt, ssm_a, o, slots, n_tok)
+        gdn_gated_rmsnorm(o, z, norm_w, eps, y)

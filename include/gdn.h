@@ -151,6 +151,18 @@ int gdn_decode_step(gdn_pool* p, const int32_t* slots, const int32_t* n_tok, int
                     const float* h, const float* alpha, const float* beta_logit, const float* dt,
                     const float* ssm_a, float* o, void* stream);
 
+/* gdn_decode_step with step 7 (the gated RMSNorm below) fused into its epilogue, as
+ * the pages' engine fuses its step and output norm (`fused_gdn_step_norm`, step 7 of
+ * gdn_layer).  Same arguments as gdn_decode_step plus
+ * z       [B][T][h_v*s]   gate input;  norm_w [s];  eps (>= 0)
+ * y       [B][T][h_v*s]   output: rms_norm(o) * norm_w * sigmoid(z)
+ * o       [B][T][h_v][s]  optional: NULL skips writing o (saves its HBM traffic)
+ * y and o may not overlap each other, h, z or the pool. */
+int gdn_decode_step_norm(gdn_pool* p, const int32_t* slots, const int32_t* n_tok, int32_t B,
+                         int32_t T, const float* h, const float* alpha, const float* beta_logit,
+                         const float* dt, const float* ssm_a, const float* z, const float* norm_w,
+                         float eps, float* o, float* y, void* stream);
+
 /* Step 7 of gdn_layer: per row of s values,
  *   y = o / sqrt(mean(o^2) + eps) * w * sigmoid(z)
  * o, z, y [rows][s] (rows = B*T*h_v); w [s], shared by all rows.  s must be 128.

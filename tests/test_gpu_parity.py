@@ -17,6 +17,18 @@ pytestmark = pytest.mark.gpu
 STEP_TOL = 1e-4
 LONG_TOL = 1e-3
 
+_ORACLE = {}
+
+
+def _workload_and_oracle(name):
+    """The workload and the oracle's results for all its sequences, computed once."""
+    if name not in _ORACLE:
+        wl = W.CONFIGS[name]()
+        _ORACLE[name] = (wl, oracle.run_workload(wl))
+    return _ORACLE[name]
+
+FUSED = pytest.mark.parametrize("fused", [False, True], ids=["3calls", "fused_norm"])
+
 
 def _stack(results, key, n=None):
     return np.stack([r[key] if n is None else r[key][:n] for r in results])
@@ -47,14 +59,15 @@ def _compare_all(gm, wl, res, tol, tag):
 
 
 # ------------------------------------------------------------------ the five workloads
-def test_tiny_b1_t8_every_step():
+@FUSED
+def test_tiny_b1_t8_every_step(fused):
     """One sequence, 8 sequential single-token calls, parity after every step."""
     wl = W.tiny()
-    log("tiny_b1_t8: start")
+    log(f"tiny_b1_t8 fused={fused}: start")
     gm = GpuMixer(wl)
     st, cs = wl.state[0], wl.conv_state[0]
     for t in range(wl.T):
-        h, o, y = gm.run(t, t + 1)
+        h, o, y = gm.run(t, t + 1, fused=fused)
         r = oracle.run_sequence(wl, 0, t, t + 1, state=st, conv_state=cs)
         st, cs = r["state"], r["conv_state"]
         assert_close(f"step {t} h", h.cpu().numpy()[0], r["h"], STEP_TOL)
@@ -65,52 +78,49 @@ def test_tiny_b1_t8_every_step():
     assert int(gm.pool.flags.item()) == 0
 
 
-def test_decode_b64_one_step():
-    wl = W.decode_b64()
-    log("decode_b64: start")
+@FUSED
+def test_decode_b64_one_step(fused):
+    log(f"decode_b64 fused={fused}: start")
+    wl, res = _workload_and_oracle("b64")
     gm = GpuMixer(wl)
-    gm.run()
-    res = oracle.run_workload(wl)
+    gm.run(fused=fused)
     _compare_all(gm, wl, res, STEP_TOL, "decode_b64")
     assert int(gm.pool.flags.item()) == 0
 
 
-def test_decode_b256_one_step():
+@FUSED
+def test_decode_b256_one_step(fused):
     """The bandwidth-bound decode: 256 sequences, 768 MiB of state, in the launch
     configuration the benchmark times."""
-    wl = W.decode_b256()
-    log("decode_b256: start")
+    log(f"decode_b256 fused={fused}: start")
+    wl, res = _workload_and_oracle("b256")
     gm = GpuMixer(wl)
-    gm.run()
-    log("decode_b256: gpu done, running oracle")
-    res = oracle.run_workload(wl)
+    gm.run(fused=fused)
     _compare_all(gm, wl, res, STEP_TOL, "decode_b256")
 
 
-def test_prefill_b16_t512_state_on_chip():
+@FUSED
+def test_prefill_b16_t512_state_on_chip(fused):
     """16 sequences x 512 tokens in ONE call: the state stays in VGPRs across the tokens."""
-    wl = W.prefill_b16_t512()
-    log("prefill_b16_t512: start")
+    log(f"prefill_b16_t512 fused={fused}: start")
+    wl, res = _workload_and_oracle("prefill")
     gm = GpuMixer(wl)
-    gm.run()
-    log("prefill_b16_t512: gpu done, running oracle")
-    res = oracle.run_workload(wl)
+    gm.run(fused=fused)
     # the first token is a plain decode step; after 512 steps the looser bound applies
     assert_close("prefill o[t=0]", gm.o[:, 0].cpu().numpy(), _stack(res, "o")[:, 0], STEP_TOL)
     assert_close("prefill h", gm.h.cpu().numpy(), _stack(res, "h"), STEP_TOL)
     _compare_all(gm, wl, res, LONG_TOL, "prefill_b16_t512")
 
 
-def test_ragged_pool2048_b1024():
+@FUSED
+def test_ragged_pool2048_b1024(fused):
     """2048-slot pool, 1024 sequences at random unique slots, U{1..8} tokens each, one call
     with per-sequence token counts. Untouched slots stay bit-identical."""
     import torch
-    wl = W.ragged_pool()
-    log(f"ragged: start, {int(wl.n_tok.sum())} seq-steps")
+    log(f"ragged fused={fused}: start")
+    wl, res = _workload_and_oracle("ragged")
     gm = GpuMixer(wl)
-    gm.run()
-    log("ragged: gpu done, running oracle")
-    res = oracle.run_workload(wl)
+    gm.run(fused=fused)
     st, _ = _compare_all(gm, wl, res, STEP_TOL, "ragged")
     untouched = np.setdiff1d(np.arange(wl.n_slots), wl.slots)
     assert np.array_equal(st[untouched], wl.state[untouched]), "an untouched slot changed"
@@ -132,7 +142,8 @@ def test_ragged_pool2048_b1024():
         o = torch.empty(B, 1, wl.geom.h_v, wl.geom.s, device="cuda")
         y = torch.empty(B, 1, wl.geom.value_dim, device="cuda")
         gm2.G.gdn_mixer(gm2.pool, sub(gm2.qkv), sub(gm2.alpha), sub(gm2.beta_logit), sub(gm2.z),
-                        gm2.conv_w, gm2.dt, gm2.ssm_a, gm2.norm_w, wl.eps, h, o, y, gm2.slots[idx].contiguous())
+                        gm2.conv_w, gm2.dt, gm2.ssm_a, gm2.norm_w, wl.eps, h, o, y, gm2.slots[idx].contiguous(),
+                        fused=fused)
         gm2.o[idx, t:t + 1] = o
         gm2.y[idx, t:t + 1] = y
     assert torch.equal(gm2.pool.state, gm.pool.state)
@@ -159,17 +170,18 @@ def test_small_geometries_several_tiles_ragged_tail(geom, B, T):
     _compare_all(gm, wl, res, STEP_TOL if T == 1 else 2 * STEP_TOL, "small")
 
 
-def test_chunked_calls_equal_one_call_bitwise():
+@FUSED
+def test_chunked_calls_equal_one_call_bitwise(fused):
     """T tokens in one call equal the same tokens split over several calls, bit for bit
     (the multi-token path must reproduce the single-token decode exactly)."""
     import torch
     wl = W.make("chunk", 4, 20, seed=50, state_std=0.02, conv_std=1.0)
-    log("chunked vs one call")
+    log(f"chunked vs one call, fused={fused}")
     a = GpuMixer(wl)
-    a.run()
+    a.run(fused=fused)
     b = GpuMixer(wl)
     for t0, t1 in [(0, 1), (1, 8), (8, 9), (9, 20)]:
-        b.run(t0, t1)
+        b.run(t0, t1, fused=fused)
     assert torch.equal(a.pool.state, b.pool.state)
     assert torch.equal(a.pool.conv, b.pool.conv)
     assert torch.equal(a.o, b.o) and torch.equal(a.y, b.y) and torch.equal(a.h, b.h)
@@ -323,3 +335,30 @@ def test_abi_rejects_bad_arguments_on_device():
         G.gdn_decode_step(pool, torch.zeros(3, 1, 10240, device="cuda"), torch.zeros(3, 1, 48, device="cuda"),
                           torch.zeros(3, 1, 48, device="cuda"), torch.zeros(48, device="cuda"),
                           torch.zeros(48, device="cuda"), torch.zeros(3, 1, 48, 128, device="cuda"))  # B > n_slots
+
+
+@pytest.mark.parametrize("T", [1, 6, 19])
+def test_fused_norm_equals_separate_norm(T):
+    """The fused epilogue computes the same norm as gdn_gated_rmsnorm, bit for bit, in both
+    the single-token and the multi-token kernel; o is optional."""
+    import torch
+    import gated_deltanet_mixer_gdn_amd as G
+    wl = W.make("fuse", 5, T, seed=59 + T, n_slots=7, state_std=0.02, conv_std=1.0, slot_choice="random")
+    wl.n_tok = np.minimum(np.array([6, 1, 0, 3, 19], np.int32), T).astype(np.int32)
+    a = GpuMixer(wl)
+    a.run()
+    b = GpuMixer(wl)
+    b.run(fused=True)
+    assert torch.equal(a.pool.state, b.pool.state) and torch.equal(a.o, b.o)
+    assert torch.equal(b.y, a.y)
+    # o = None: same y and state, o untouched
+    c = GpuMixer(wl)
+    h = torch.empty_like(c.h)
+    G.gdn_conv_silu_norm(c.pool, c.qkv, c.conv_w, wl.eps, h, c.slots, c.n_tok)
+    y = torch.full_like(c.y, 7.0)
+    G.gdn_decode_step_norm(c.pool, h, c.alpha, c.beta_logit, c.dt, c.ssm_a, c.z, c.norm_w, wl.eps, y,
+                           None, c.slots, c.n_tok)
+    assert torch.equal(y, b.y) and torch.equal(c.pool.state, b.pool.state)
+    with pytest.raises(G.GdnError):
+        G.gdn_decode_step_norm(c.pool, h, c.alpha, c.beta_logit, c.dt, c.ssm_a, c.z, c.norm_w, wl.eps, c.z,
+                               None, c.slots, c.n_tok)   # y aliases z
