@@ -5,20 +5,22 @@ A step is one pass of the whole mixer (conv/SiLU/L2 -> gated delta rule -> gated
 RMSNorm) over one batch: by default the bandwidth-bound decode of 256 sequences x
 1 token (768 MiB of fp32 state), inputs already in HBM.  The timed step is two
 launches, gdn_conv_silu_norm and gdn_decode_step_norm (the recurrence with the
-norm fused into its epilogue, writing y only); the three-call form (o through
-HBM, separate gdn_gated_rmsnorm) is timed beside it.  Prints ONE JSON line on
-stdout; diagnostics go to stderr.
+gated RMSNorm fused into its epilogue, writing y only), the fastest form at large
+batch.  The single-launch decode (gdn_decode_fused) and the three-call form are
+timed beside it for context.  Prints ONE JSON line on stdout; diagnostics go to
+stderr.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--config b256]
                   [--cpu-seconds S | --no-cpu-baseline] [--copy-probe-mib M]
 
-The `roofline` object is for the dominant kernel (decode_one_kernel<fused norm>):
-its algorithmic bytes per launch over its average launch time, measured with HIP
-events recorded on the stream the kernels run on, around the kernels of every
-8th step of the timed region.  `traffic` (HBM bytes per
-launch from rocprofv3 FETCH_SIZE / WRITE_SIZE counters, scaled by a copy-kernel
-calibration) is read from profiles/decode_one_fused_b256_traffic.txt and reported only
-while the kernel source it was measured on is unchanged.
+The `roofline` object is for the dominant kernel of the timed step
+(decode_one_kernel<fused norm> for the default workload): its algorithmic bytes per
+launch over its average launch time, measured with HIP events recorded on the
+stream the kernels run on, around the kernels of every 8th step of the timed
+region.  `traffic` (HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE
+counters, scaled by a copy-kernel calibration) is read from
+profiles/decode_one_norm_b256_traffic.txt and reported only while the kernel
+sources it was measured on are unchanged.
 """
 import argparse
 import hashlib
@@ -31,8 +33,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0            # MI355X HBM3E, published peak
-KERNEL_SRC = os.path.join(ROOT, "gated_deltanet_mixer_gdn_amd", "csrc", "gdn_kernels.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_one_fused_b256_traffic.txt")
+# the sources the recurrence kernel is built from (its counter record is void once they change)
+KERNEL_SRCS = [os.path.join(ROOT, "gated_deltanet_mixer_gdn_amd", "csrc", f)
+               for f in ("gdn_recurrence.hip", "gdn_device.h", "gdn_kernels.h")]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_one_norm_b256_traffic.txt")
 
 
 def log(*a):
@@ -40,7 +44,10 @@ def log(*a):
 
 
 def kernel_source_hash() -> str:
-    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for f in KERNEL_SRCS:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def read_traffic():
@@ -74,10 +81,13 @@ def algorithmic_bytes(wl):
     core = (seqs * hv * S * S * 4 * 2          # state read + write, once per call
             + tok * (C * 4 + 2 * hv * 4)       # h (q|k|v) and alpha / beta logits of each token
             + 2 * hv * 4)                      # dt, ssm_a
+    step_norm = core + tok * row + all_tok * row + S * 4                  # z in, y out
     return {"conv": conv,
             "step": core + all_tok * row,                                  # o
             "norm": all_tok * row * 3 + S * 4,                             # o, z in; y out; weight
-            "step_norm": core + tok * row + all_tok * row + S * 4}, tok * hv   # z in, y out
+            "step_norm": step_norm,
+            # single launch: conv without the h write, recurrence without the h read
+            "one": conv - all_tok * C * 4 + step_norm - tok * C * 4}, tok * hv
 
 
 def cpu_baseline(wl, seconds: float):
@@ -181,6 +191,14 @@ def main():
         if ev:
             ev[2].record(stream)
 
+    def step_one(ev=None):
+        # single launch: conv/SiLU/L2, recurrence and gated RMSNorm for one token
+        if ev:
+            ev[0].record(stream)
+        G.gdn_decode_fused(pool, qkv, conv_w, alpha, bl, dt, ssm_a, z, norm_w, wl.eps, y, None, slots)
+        if ev:
+            ev[1].record(stream)
+
     def step_three(ev=None):
         # the same pass as three separate calls (o goes through HBM)
         if ev:
@@ -216,7 +234,12 @@ def main():
         return wall * 1000.0 / args.steps, k_ms, len(evs)
 
     three_ms, three_k, _ = timed(step_three, 4, ("conv", "step", "norm"))
+    single = wl.T == 1 and wl.n_tok is None
+    one_ms, one_k = (timed(step_one, 2, ("one",))[:2]) if single else (None, None)
+    # the timed hot path: conv/SiLU/L2 + recurrence with the norm fused (two launches),
+    # the fastest form at large batch
     ms_per_step, k_ms, n_samples = timed(step_fused, 3, ("conv", "step_norm"))
+    two_ms, two_k, dominant = ms_per_step, k_ms, "step_norm"
     # context: a plain device-to-device copy of the state's size on the same stream
     ref_src = pool.state.view(-1)
     ref_dst = torch.empty_like(ref_src)
@@ -236,12 +259,16 @@ def main():
 
     nbytes, units = algorithmic_bytes(wl)
     value = units / (ms_per_step / 1000.0)
-    achieved = nbytes["step_norm"] / (k_ms["step_norm"] / 1000.0) / 1e9
+    achieved = nbytes[dominant] / (k_ms[dominant] / 1000.0) / 1e9
     mixer_bytes = nbytes["conv"] + nbytes["step_norm"]
     mixer_gbps = mixer_bytes / (ms_per_step / 1000.0) / 1e9
+    two_gbps = nbytes["step_norm"] / (two_k["step_norm"] / 1000.0) / 1e9
     three_step_gbps = nbytes["step"] / (three_k["step"] / 1000.0) / 1e9
-    log("fused step: " + ", ".join(f"{k}={v * 1000:.1f}us" for k, v in k_ms.items()) +
-        f"; {ms_per_step * 1000:.1f} us/step; recurrence+norm kernel {achieved:.0f} GB/s; mixer {mixer_gbps:.0f} GB/s")
+    one_gbps = nbytes["one"] / (one_k["one"] / 1000.0) / 1e9 if single else None
+    if single:
+        log(f"one launch: {one_k['one'] * 1000:.1f}us kernel; {one_ms * 1000:.1f} us/step; {one_gbps:.0f} GB/s")
+    log("two calls: " + ", ".join(f"{k}={v * 1000:.1f}us" for k, v in two_k.items()) +
+        f"; {two_ms * 1000:.1f} us/step; recurrence+norm kernel {two_gbps:.0f} GB/s")
     log("three calls: " + ", ".join(f"{k}={v * 1000:.1f}us" for k, v in three_k.items()) +
         f"; {three_ms * 1000:.1f} us/step; recurrence kernel {three_step_gbps:.0f} GB/s; d2d copy {copy_gbps:.0f} GB/s")
     traffic = read_traffic() if args.config == "b256" else None
@@ -272,6 +299,10 @@ def main():
         "hbm_gbps_mixer": mixer_gbps,
         "hbm_frac_mixer": mixer_gbps / HBM_PEAK_GBPS,
         "kernel_us": {k: v * 1000.0 for k, v in k_ms.items()},
+        "single_launch_path": (None if not single else
+                               {"ms_per_step": one_ms, "kernel_us": one_k["one"] * 1000.0,
+                                "value": units / (one_ms / 1000.0), "kernel_gbps": one_gbps,
+                                "algorithmic_bytes_per_launch": nbytes["one"]}),
         "three_call_path": {"ms_per_step": three_ms, "kernel_us": {k: v * 1000.0 for k, v in three_k.items()},
                             "value": units / (three_ms / 1000.0),
                             "recurrence_kernel_gbps": three_step_gbps},
@@ -280,7 +311,7 @@ def main():
                      "bound": "hbm",
                      "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
-                     "algorithmic_bytes_per_launch": nbytes["step_norm"],
+                     "algorithmic_bytes_per_launch": nbytes[dominant],
                      "event_samples": n_samples},
         "cpu_baseline": cpu,
     }

@@ -9,13 +9,16 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libgdn_hip.so")
-SOURCES = ["gdn_kernels.hip", "gdn_api.cpp"]
+SOURCES = ["gdn_conv.hip", "gdn_recurrence.hip", "gdn_norm.hip", "gdn_api.cpp"]
 
 # gfx950 only.  Packed fp32 instructions are switched off for device code (the
 # host pass ignores the feature with a warning).
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-mcode-object-version=5", "-O3", "-std=c++17", "-fPIC", "-shared", "-Wall",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # no implicit contraction: every multiply-add that should fuse is written as an
+    # FMA, so the same expression rounds the same way in every kernel
+    "-ffp-contract=off",
 ]
 
 

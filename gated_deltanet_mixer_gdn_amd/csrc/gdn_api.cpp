@@ -324,6 +324,69 @@ int gdn_decode_step_norm(gdn_pool* p, const int32_t* slots, const int32_t* n_tok
                          stream);
 }
 
+int gdn_decode_fused(gdn_pool* p, const int32_t* slots, int32_t B, const float* qkv, const float* conv_w,
+                     const float* alpha, const float* beta_logit, const float* dt, const float* ssm_a,
+                     const float* z, const float* norm_w, float eps, float* y, float* h, void* stream) {
+    const char* fn = "gdn_decode_fused";
+    if (int rc = check_pool(p, fn)) return rc;
+    if (B < 0) return fail(GDN_ERR_ARG, fn, "B=%d is negative", B);
+    if (!(eps >= 0.0f) || !std::isfinite(eps)) return fail(GDN_ERR_ARG, fn, "eps must be finite and >= 0");
+    const int group = p->g.h_v / p->g.h_k;
+    if (group > gdn::kFusedMaxGroup)
+        return fail(GDN_ERR_UNSUPPORTED, fn, "h_v/h_k=%d exceeds %d value heads per qk head", group,
+                    gdn::kFusedMaxGroup);
+    if (B == 0) return ok();
+    if ((int64_t) B * p->g.h_k > INT32_MAX) return fail(GDN_ERR_ARG, fn, "B*h_k too large");
+    if (int rc = check_f4(qkv, fn, "qkv")) return rc;
+    if (int rc = check_f4(conv_w, fn, "conv_w")) return rc;
+    if (int rc = check_f1(alpha, fn, "alpha")) return rc;
+    if (int rc = check_f1(beta_logit, fn, "beta_logit")) return rc;
+    if (int rc = check_f1(dt, fn, "dt")) return rc;
+    if (int rc = check_f1(ssm_a, fn, "ssm_a")) return rc;
+    if (int rc = check_f4(z, fn, "z")) return rc;
+    if (int rc = check_f4(norm_w, fn, "norm_w")) return rc;
+    if (int rc = check_f4(y, fn, "y")) return rc;
+    if (h && !aligned(h, 16)) return fail(GDN_ERR_ARG, fn, "h is not 16-byte aligned");
+    if (slots && !aligned(slots, 4)) return fail(GDN_ERR_ARG, fn, "slots is not 4-byte aligned");
+    if (!slots && B > p->n_slots)
+        return fail(GDN_ERR_ARG, fn, "slots is null and B=%d exceeds the pool's %lld slots", B,
+                    (long long) p->n_slots);
+    const size_t y_bytes = (size_t) B * p->g.h_v * p->g.s * sizeof(float);
+    const size_t c_bytes = (size_t) B * channels(p->g) * sizeof(float);
+    const size_t pool_bytes = (size_t) ((p->base + p->bytes) - reinterpret_cast<char*>(p->state));
+    if (overlap(y, y_bytes, qkv, c_bytes)) return fail(GDN_ERR_ARG, fn, "y overlaps qkv");
+    if (overlap(y, y_bytes, z, y_bytes)) return fail(GDN_ERR_ARG, fn, "y overlaps z");
+    if (overlap(y, y_bytes, p->state, pool_bytes)) return fail(GDN_ERR_ARG, fn, "y overlaps the pool");
+    if (h) {
+        if (overlap(h, c_bytes, qkv, c_bytes)) return fail(GDN_ERR_ARG, fn, "h overlaps qkv");
+        if (overlap(h, c_bytes, y, y_bytes)) return fail(GDN_ERR_ARG, fn, "h overlaps y");
+        if (overlap(h, c_bytes, p->state, pool_bytes)) return fail(GDN_ERR_ARG, fn, "h overlaps the pool");
+    }
+    gdn::FusedParams f;
+    f.state = p->state;
+    f.conv = p->conv;
+    f.slots = slots;
+    f.qkv = qkv;
+    f.w = conv_w;
+    f.alpha = alpha;
+    f.beta_logit = beta_logit;
+    f.dt = dt;
+    f.ssm_a = ssm_a;
+    f.z = z;
+    f.norm_w = norm_w;
+    f.y = y;
+    f.h = h;
+    f.flags = p->flags;
+    f.n_slots = p->n_slots;
+    f.B = B;
+    f.h_k = p->g.h_k;
+    f.h_v = p->g.h_v;
+    f.group = group;
+    f.eps = eps;
+    f.qscale = 1.0f / std::sqrt((float) p->g.s);
+    return launched(gdn::launch_decode_fused(f, static_cast<hipStream_t>(stream)), fn);
+}
+
 int gdn_gated_rmsnorm(const float* o, const float* z, const float* w, float eps, int64_t rows, int32_t s,
                       float* y, void* stream) {
     const char* fn = "gdn_gated_rmsnorm";

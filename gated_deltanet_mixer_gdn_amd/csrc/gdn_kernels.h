@@ -1,5 +1,6 @@
 // gdn_kernels.h - internal interface between the C-ABI layer (gdn_api.cpp) and the
-// gfx950 kernels (gdn_kernels.hip).  Not installed, not part of the ABI.
+// gfx950 kernels (gdn_conv.hip, gdn_recurrence.hip, gdn_norm.hip).  Not installed,
+// not part of the ABI.
 #pragma once
 
 #include <hip/hip_runtime_api.h>
@@ -15,7 +16,7 @@ constexpr int kDConv = 4;
 constexpr int kHist = kDConv - 1;
 // Tokens of one sequence handled by one conv workgroup (>= kHist, so only the
 // first token block of a sequence ever reads or writes the stored conv history).
-constexpr int kConvTokensPerBlock = 8;
+constexpr int kConvTokensPerBlock = 32;
 // Rows (value heads x tokens) per gated-RMSNorm workgroup: one half-wave per row.
 constexpr int kNormRowsPerBlock = 8;
 
@@ -52,6 +53,30 @@ struct StepParams {
     float eps;              // RMSNorm epsilon (epilogue only)
 };
 
+// Largest GQA group (h_v / h_k) the single-launch decode supports: the conv prologue
+// gives one 16-lane row to each of q_j, k_j and the group's value heads.
+constexpr int kFusedMaxGroup = 14;
+
+struct FusedParams {
+    float* state;           // pool state region
+    float* conv;            // pool conv region
+    const int32_t* slots;   // [B] or null
+    const float* qkv;       // [B][C] raw projections of one token
+    const float* w;         // [C][4]
+    const float* alpha;     // [B][h_v]
+    const float* beta_logit;
+    const float* dt;        // [h_v]
+    const float* ssm_a;     // [h_v]
+    const float* z;         // [B][h_v*128]
+    const float* norm_w;    // [128]
+    float* y;               // [B][h_v*128]
+    float* h;               // [B][C] or null: the conv/SiLU/L2 output, if wanted
+    uint32_t* flags;
+    long long n_slots;
+    int B, h_k, h_v, group;
+    float eps, qscale;
+};
+
 struct NormParams {
     const float* o;
     const float* z;
@@ -74,6 +99,7 @@ struct ZeroParams {
 
 hipError_t launch_conv_silu_norm(const ConvParams& p, hipStream_t stream);
 hipError_t launch_decode_step(const StepParams& p, hipStream_t stream);
+hipError_t launch_decode_fused(const FusedParams& p, hipStream_t stream);
 hipError_t launch_gated_rmsnorm(const NormParams& p, hipStream_t stream);
 hipError_t launch_zero(const ZeroParams& p, hipStream_t stream);
 

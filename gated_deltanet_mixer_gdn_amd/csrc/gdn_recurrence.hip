@@ -1,0 +1,421 @@
+// gdn_recurrence.hip - the gated delta-rule recurrence kernels (one token, many tokens).
+#include "gdn_device.h"
+
+namespace gdn {
+
+// ------------------------------------------------------------------ gated delta rule
+//
+// Both recurrence kernels use the one-pass form of a token's update: with the old
+// state S, PK[c] = sum_r S[r][c] k[r], PQ[c] = sum_r S[r][c] q[r] and KQ = k . q,
+//   d = beta (v - e^g PK);  o = e^g PQ + KQ d;  S <- e^g S + k d^T
+// which equals decay -> read -> write -> read of the recurrence in exact arithmetic
+// (o = S_new^T q expanded), so one read of S gives both column reductions.
+
+// The (sequence, value head) a workgroup works on.  Workgroups are dispatched
+// round-robin over the 8 XCDs; the remap gives each XCD a contiguous range of
+// (sequence, head) pairs, so the value heads sharing one q/k read it through the
+// same L2 and each XCD streams one region of the pool.
+struct HeadJob {
+    int b, i, j, slot, nt;
+};
+
+__device__ __forceinline__ HeadJob head_job(const StepParams& p, bool report) {
+    const unsigned nwg = gridDim.x;
+    unsigned wid = blockIdx.x;
+    if ((nwg & 7u) == 0) wid = (wid & 7u) * (nwg >> 3) + (wid >> 3);
+    HeadJob h;
+    h.b = (int) (wid / (unsigned) p.h_v);
+    h.i = (int) (wid - (unsigned) h.b * (unsigned) p.h_v);
+    h.j = h.i / p.group;
+    h.slot = read_slot(p.slots, h.b, p.n_slots, p.flags, report && h.i == 0);
+    h.nt = h.slot < 0 ? 0 : read_ntok(p.n_tok, h.b, p.T, p.flags, report && h.i == 0);
+    return h;
+}
+
+// LDS a 256-thread workgroup uses to reduce one head's column sums across its waves.
+struct HeadReduce {
+    f4 k[4][32];
+    f4 q[4][32];
+    float kq[4];
+};
+
+// One token of one head for a 256-thread workgroup whose thread tid holds columns
+// 4*cg..4*cg+3 (cg = tid % 32) of rows 16*rg..16*rg+15 (rg = tid / 32) of the old
+// state in s[] (16 float4 = 64 VGPRs).  qk: q as 32 float4, then k as 32 float4, in
+// LDS; v: this thread's 4 columns of v.  Reductions: a per-thread partial over 16
+// rows, a cross-half-wave fold, then the 4 waves through LDS (one barrier, so every
+// thread must call this).  Lanes 0-31 of wave 0 (rg == 0) then hold o for the whole
+// head and write o (if o_row) and the gated RMSNorm y (if kNorm); s[] becomes the new
+// state.  The operation sequence is the multi-token kernel's, so the two agree bit
+// for bit.
+template <bool kNorm>
+__device__ __forceinline__ void head_token_256(f4 (&s)[16], const f4* qk, f4 v, float beta, float eg,
+                                               HeadReduce& red, float* o_row, const float* z_row,
+                                               const float* norm_w, float* y_row, float eps) {
+    const int tid = threadIdx.x;
+    const int cg = tid & 31;
+    const int rg = tid >> 5;
+    const int wave = tid >> 6;
+    const float* qrow = (const float*) qk + rg * 16;
+    const float* krow = (const float*) qk + kS + rg * 16;
+    f4 pk = {0.f, 0.f, 0.f, 0.f}, pq = pk;
+    float kq = 0.f;
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+        const float kk = krow[m];
+        const float qq = qrow[m];
+        pk = fma4(s[m], kk, pk);
+        pq = fma4(s[m], qq, pq);
+        kq = __builtin_fmaf(kk, qq, kq);
+    }
+    // fold the two row groups of this wave (lanes l and l^32)
+    pk = add_xor32(pk);
+    pq = add_xor32(pq);
+    kq = add_xor32(kq);
+    if ((tid & 32) == 0) {
+        red.k[wave][cg] = pk;
+        red.q[wave][cg] = pq;
+        if (cg == 0) red.kq[wave] = kq;
+    }
+    __syncthreads();
+
+    // the 8 row groups summed as ((g0+g1)+(g2+g3))+((g4+g5)+(g6+g7))
+    const f4 PK = (red.k[0][cg] + red.k[1][cg]) + (red.k[2][cg] + red.k[3][cg]);
+    const f4 PQ = (red.q[0][cg] + red.q[1][cg]) + (red.q[2][cg] + red.q[3][cg]);
+    const float KQ = (red.kq[0] + red.kq[1]) + (red.kq[2] + red.kq[3]);
+    const f4 d = beta * fma4(-eg, PK, v);
+    if (rg == 0) {
+        const f4 out = fma4(KQ, d, eg * PQ);
+        if (o_row) *(f4*) (o_row + cg * 4) = out;
+        if (kNorm) {
+            // sum of o^2: 8-lane (32-column) blocks first, then ((b0+b1)+(b2+b3))
+            const float ss = halfwave_sum(sumsq4(out));
+            const float inv = rms_inv(ss, eps);
+            const f4 zz = *(const f4*) (z_row + cg * 4);
+            const f4 wn = *(const f4*) (norm_w + cg * 4);
+            *(f4*) (y_row + cg * 4) = out * inv * wn * sigmoid4(zz);
+        }
+    }
+#pragma unroll
+    for (int m = 0; m < 16; ++m) s[m] = fma4(krow[m], d, eg * s[m]);
+}
+
+__device__ __forceinline__ void load_tile(f4 (&s)[16], const float* tile) {
+#pragma unroll
+    for (int m = 0; m < 16; ++m) s[m] = __builtin_nontemporal_load((const f4*) (tile + m * kS));
+}
+
+__device__ __forceinline__ void store_tile(const f4 (&s)[16], float* tile) {
+#pragma unroll
+    for (int m = 0; m < 16; ++m) __builtin_nontemporal_store(s[m], (f4*) (tile + m * kS));
+}
+
+// Single-token decode (T == 1): bandwidth-bound.  One workgroup of 256 threads per
+// (sequence, value head) in the layout of head_token_256; a wave's tile loads cover
+// two 512-byte row segments per instruction.  kNorm: fused gated-RMSNorm epilogue.
+template <bool kNorm>
+__global__ __launch_bounds__(256) void decode_one_kernel(StepParams p) {
+    __shared__ f4 qk_lds[64];        // q as 32 float4, then k as 32 float4
+    __shared__ HeadReduce red;
+
+    const int tid = threadIdx.x;
+    const int cg = tid & 31;
+    const int rg = tid >> 5;
+    const HeadJob job = head_job(p, tid == 0);
+    const int i = job.i;
+    const long long C = (long long) (2 * p.h_k + p.h_v) * kS;
+    const long long e = (long long) job.b * p.h_v + i;   // (sequence, token 0, head)
+
+    if (job.nt == 0) {   // no token (or an unknown slot): outputs zero, state untouched
+        if (rg == 0) {
+            const f4 zero = {0.f, 0.f, 0.f, 0.f};
+            if (!kNorm || p.o) *(f4*) (p.o + e * kS + cg * 4) = zero;
+            if (kNorm) *(f4*) (p.y + e * kS + cg * 4) = zero;
+        }
+        return;
+    }
+    float* tile = p.state + ((long long) job.slot * p.h_v + i) * (kS * kS) + (rg * 16) * kS + cg * 4;
+    f4 s[16];
+    load_tile(s, tile);
+
+    const float* ht = p.h + (long long) job.b * C;
+    if (tid < 64) {
+        const long long off = tid < 32 ? (long long) job.j * kS + tid * 4
+                                       : (long long) (p.h_k + job.j) * kS + (tid - 32) * 4;
+        qk_lds[tid] = *(const f4*) (ht + off);
+    }
+    const f4 v = *(const f4*) (ht + (long long) (2 * p.h_k + i) * kS + cg * 4);
+    const float beta = sigmoid_f(p.beta_logit[e]);
+    const float eg = expf(softplus_f(p.alpha[e] + p.dt[i]) * p.ssm_a[i]);
+    __syncthreads();
+
+    head_token_256<kNorm>(s, qk_lds, v, beta, eg, red, (!kNorm || p.o) ? p.o + e * kS : nullptr,
+                          kNorm ? p.z + e * kS : nullptr, p.norm_w, kNorm ? p.y + e * kS : nullptr, p.eps);
+    store_tile(s, tile);
+}
+
+// The whole mixer for one decode token in one launch.  One workgroup of 256 threads
+// per (sequence b, qk head j): it owns the conv channels of q_j, k_j and of the
+// group's value heads i = g*j .. g*j+g-1 (g = h_v / h_k), so it is the only reader
+// and writer of their conv history.  Prologue: 16-lane rows run the conv + SiLU + L2
+// norm exactly as conv_silu_norm_kernel does (row 0: q_j, row 1: k_j, row 2+n: v of
+// head g*j+n) into LDS; then the workgroup steps the g heads one after another with
+// head_token_256 and the fused gated RMSNorm.  Head 0's tile loads are issued before
+// the prologue; each later head's loads follow the previous head's stores.  Results
+// equal gdn_conv_silu_norm followed by gdn_decode_step_norm bit for bit.
+__global__ __launch_bounds__(256) void decode_fused_kernel(FusedParams p) {
+    __shared__ f4 qk_lds[64];
+    __shared__ f4 v_lds[kFusedMaxGroup][32];
+    __shared__ HeadReduce red[2];
+
+    const int tid = threadIdx.x;
+    const int cg = tid & 31;
+    const int rg = tid >> 5;
+    const unsigned nwg = gridDim.x;
+    unsigned wid = blockIdx.x;
+    if ((nwg & 7u) == 0) wid = (wid & 7u) * (nwg >> 3) + (wid >> 3);
+    const int b = (int) (wid / (unsigned) p.h_k);
+    const int j = (int) (wid - (unsigned) b * (unsigned) p.h_k);
+    const int g = p.group;
+    const long long C = (long long) (2 * p.h_k + p.h_v) * kS;
+    const int slot = read_slot(p.slots, b, p.n_slots, p.flags, tid == 0 && j == 0);
+    const int crow = tid >> 4;   // conv row: 0 = q_j, 1 = k_j, 2 + n = v of head g*j + n
+    const int cl = tid & 15;
+    const int hd = crow == 0 ? j : crow == 1 ? p.h_k + j : 2 * p.h_k + g * j + (crow - 2);
+    const long long ca = (long long) hd * kS + 4 * cl;
+    const long long cb = ca + 64;
+
+    if (slot < 0) {   // unknown slot: outputs zero, pool untouched
+        const f4 zero = {0.f, 0.f, 0.f, 0.f};
+        if (rg == 0)
+            for (int n = 0; n < g; ++n) *(f4*) (p.y + ((long long) b * p.h_v + g * j + n) * kS + cg * 4) = zero;
+        if (p.h && crow < 2 + g) {
+            *(f4*) (p.h + (long long) b * C + ca) = zero;
+            *(f4*) (p.h + (long long) b * C + cb) = zero;
+        }
+        return;
+    }
+
+    const float* tile_base = p.state + ((long long) slot * p.h_v + g * j) * (kS * kS) + (rg * 16) * kS + cg * 4;
+    f4 s[16];
+    load_tile(s, tile_base);
+
+    if (crow < 2 + g) {
+        float* X = p.conv + (long long) slot * C * kHist;
+        const float* xq = p.qkv + (long long) b * C;
+        ConvGroup ga, gb;
+        ga.load_taps(p.w, ca);
+        gb.load_taps(p.w, cb);
+        ga.load_history(X + ca * kHist);
+        gb.load_history(X + cb * kHist);
+        const f4 ua = ga.step(*(const f4*) (xq + ca));
+        const f4 ub = gb.step(*(const f4*) (xq + cb));
+        f4 ha = ua * sigmoid4(ua);
+        f4 hb = ub * sigmoid4(ub);
+        if (crow < 2) {
+            const float ss = add_xor8(block8_sum(sumsq4(ha) + sumsq4(hb)));
+            const float sc = (crow == 0 ? p.qscale : 1.0f) / sqrtf(ss + p.eps);
+            ha *= sc;
+            hb *= sc;
+        }
+        ConvGroup::store_history(X + ca * kHist, ga.x3, ga.x2, ga.x1);
+        ConvGroup::store_history(X + cb * kHist, gb.x3, gb.x2, gb.x1);
+        if (p.h) {
+            *(f4*) (p.h + (long long) b * C + ca) = ha;
+            *(f4*) (p.h + (long long) b * C + cb) = hb;
+        }
+        f4* dst = crow < 2 ? qk_lds + 32 * crow : v_lds[crow - 2];
+        dst[cl] = ha;
+        dst[16 + cl] = hb;
+    }
+    __syncthreads();
+
+    for (int n = 0; n < g; ++n) {
+        const int i = g * j + n;
+        const long long e = (long long) b * p.h_v + i;
+        float* tile = (float*) tile_base + (long long) n * (kS * kS);
+        if (n > 0) load_tile(s, tile);
+        const float beta = sigmoid_f(p.beta_logit[e]);
+        const float eg = expf(softplus_f(p.alpha[e] + p.dt[i]) * p.ssm_a[i]);
+        head_token_256<true>(s, qk_lds, v_lds[n][cg], beta, eg, red[n & 1], nullptr, p.z + e * kS, p.norm_w,
+                             p.y + e * kS, p.eps);
+        store_tile(s, tile);
+    }
+}
+
+// Multi-token recurrence (T > 1): the state stays in VGPRs for all the call's tokens
+// and the per-token chain is what bounds it.  One workgroup of 4 waves per
+// (sequence, value head); wave w owns the 32-column block 32w..32w+31 for ALL 128
+// rows: lane l has columns 32w + 4*(l % 8) .. +3 of rows 16*(l / 8) .. +15.  The
+// column sums then reduce inside the wave (xor-shuffles over the 8 row groups), the
+// q/k rows are staged in a wave-private LDS slot, and each token's inputs are
+// loaded one token ahead, so the token loop itself has no barrier.
+// kNorm: each wave parks its o columns and its sum of o^2 in an 8-token LDS ring;
+// every 8 tokens the workgroup synchronises once and normalises that chunk
+// cooperatively (thread -> token tid/32, columns 4*(tid%32)..+3), with the chunk's
+// z loaded one chunk ahead.
+constexpr int kNormChunk = 8;
+
+template <bool kNorm>
+__global__ __launch_bounds__(256) void decode_multi_kernel(StepParams p) {
+    __shared__ f4 qk_lds[4][64];                    // per wave: q as 32 float4, then k as 32 float4
+    __shared__ f4 o_ring[2][kNormChunk][32];        // [chunk parity][token][float4 column group]
+    __shared__ float ss_ring[2][kNormChunk][4];     // [chunk parity][token][wave]
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int cg = lane & 7;
+    const int rg = lane >> 3;
+    const int col = wave * 32 + cg * 4;
+    const HeadJob job = head_job(p, tid == 0);
+    const int i = job.i;
+    const int nt = job.nt;
+    const long long C = (long long) (2 * p.h_k + p.h_v) * kS;
+    const long long tok0 = (long long) job.b * p.T;
+    const long long q_off = (long long) job.j * kS + (lane & 31) * 4 + (lane < 32 ? 0 : (long long) p.h_k * kS);
+    const long long v_off = (long long) (2 * p.h_k + i) * kS + col;
+    // chunk normalisation: this thread's token within a chunk and columns
+    const int n_tt = tid >> 5;
+    const int n_c4 = (tid & 31) * 4;
+
+    float* tile = nullptr;
+    f4 s[16];
+    if (nt > 0) {
+        tile = p.state + ((long long) job.slot * p.h_v + i) * (kS * kS) + (rg * 16) * kS + col;
+#pragma unroll
+        for (int m = 0; m < 16; ++m) s[m] = __builtin_nontemporal_load((const f4*) (tile + m * kS));
+    }
+    const float dt_i = p.dt[i];
+    const float a_i = p.ssm_a[i];
+
+    // q|k and v of the next token, loaded one token ahead
+    f4 qk_n = {0.f, 0.f, 0.f, 0.f}, v_n = qk_n;
+    auto fetch = [&](int t) {
+        const float* ht = p.h + (tok0 + t) * C;
+        qk_n = *(const f4*) (ht + q_off);
+        v_n = *(const f4*) (ht + v_off);
+    };
+    // beta and the decay e^g are the same for the whole head: lane l evaluates them for
+    // token t0 + l of a 64-token window, and each token reads its pair with readlane
+    float beta_w = 0.f, eg_w = 0.f;
+    auto gates = [&](int t0) {
+        if (t0 + lane < nt) {
+            const long long e = (tok0 + t0 + lane) * p.h_v + i;
+            beta_w = sigmoid_f(p.beta_logit[e]);
+            eg_w = expf(softplus_f(p.alpha[e] + dt_i) * a_i);
+        }
+    };
+    // z of this thread's token in the next chunk, loaded one chunk ahead
+    f4 z_n = {0.f, 0.f, 0.f, 0.f};
+    auto fetch_z = [&](int t0c) {
+        if (t0c + n_tt < nt) z_n = *(const f4*) (p.z + ((tok0 + t0c + n_tt) * p.h_v + i) * kS + n_c4);
+    };
+    if (nt > 0) {
+        fetch(0);
+        if (kNorm) fetch_z(0);
+    }
+
+    f4* buf = qk_lds[wave];
+    const float* qrow = (const float*) buf + rg * 16;
+    const float* krow = (const float*) buf + kS + rg * 16;
+    for (int t = 0; t < nt; ++t) {
+        if ((t & 63) == 0) gates(t);
+        const float beta = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(beta_w), t & 63));
+        const float eg = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(eg_w), t & 63));
+        buf[lane] = qk_n;
+        const f4 v = v_n;
+        if (t + 1 < nt) fetch(t + 1);
+        // the staging above is wave-private: order it against this wave's reads
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+        f4 pk = {0.f, 0.f, 0.f, 0.f}, pq = pk;
+        float kq = 0.f;
+#pragma unroll
+        for (int m = 0; m < 16; ++m) {
+            const float kk = krow[m];
+            const float qq = qrow[m];
+            pk = fma4(s[m], kk, pk);
+            pq = fma4(s[m], qq, pq);
+            kq = __builtin_fmaf(kk, qq, kq);
+        }
+        // sum over the 8 row groups of the wave (lane bits 3..5):
+        // ((g0+g1)+(g2+g3))+((g4+g5)+(g6+g7)), as in the single-token kernel
+        pk = add_xor32(add_xor16(add_xor8(pk)));
+        pq = add_xor32(add_xor16(add_xor8(pq)));
+        kq = add_xor32(add_xor16(add_xor8(kq)));
+        const f4 d = beta * fma4(-eg, pk, v);
+        const f4 out = fma4(kq, d, eg * pq);
+        if ((!kNorm || p.o) && rg == 0) *(f4*) (p.o + ((tok0 + t) * p.h_v + i) * kS + col) = out;
+        if (kNorm) {
+            const int par = (t / kNormChunk) & 1;
+            const int slot8 = t % kNormChunk;
+            // sum of o^2 over this wave's 32 columns (lane bits 0..2)
+            const float ss = block8_sum(sumsq4(out));
+            if (rg == 0) o_ring[par][slot8][wave * 8 + cg] = out;
+            if (lane == 0) ss_ring[par][slot8][wave] = ss;
+            if (slot8 == kNormChunk - 1 || t == nt - 1) {   // uniform over the workgroup
+                __syncthreads();
+                const int t0c = t - slot8;
+                const f4 zz = z_n;
+                if (t0c + kNormChunk < nt) fetch_z(t0c + kNormChunk);
+                if (n_tt <= slot8) {
+                    const float tot = (ss_ring[par][n_tt][0] + ss_ring[par][n_tt][1]) +
+                                      (ss_ring[par][n_tt][2] + ss_ring[par][n_tt][3]);
+                    const float inv = rms_inv(tot, p.eps);
+                    const f4 wn = *(const f4*) (p.norm_w + n_c4);
+                    *(f4*) (p.y + ((tok0 + t0c + n_tt) * p.h_v + i) * kS + n_c4) =
+                        o_ring[par][n_tt][n_c4 / 4] * inv * wn * sigmoid4(zz);
+                }
+            }
+        }
+        // re-read k from LDS rather than keeping 16 rows live across the reduction (the
+        // fence stops the compiler from reusing the values loaded above)
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        const f4* k4 = (const f4*) krow;
+#pragma unroll
+        for (int m4 = 0; m4 < 4; ++m4) {
+            const f4 kk = k4[m4];
+            s[4 * m4 + 0] = fma4(kk.x, d, eg * s[4 * m4 + 0]);
+            s[4 * m4 + 1] = fma4(kk.y, d, eg * s[4 * m4 + 1]);
+            s[4 * m4 + 2] = fma4(kk.z, d, eg * s[4 * m4 + 2]);
+            s[4 * m4 + 3] = fma4(kk.w, d, eg * s[4 * m4 + 3]);
+        }
+    }
+    if (rg == 0) {
+        const f4 zero = {0.f, 0.f, 0.f, 0.f};
+        for (int t = nt; t < p.T; ++t) {
+            const long long e = ((tok0 + t) * p.h_v + i) * kS + col;
+            if (!kNorm || p.o) *(f4*) (p.o + e) = zero;
+            if (kNorm) *(f4*) (p.y + e) = zero;
+        }
+    }
+    if (nt > 0) {
+#pragma unroll
+        for (int m = 0; m < 16; ++m) __builtin_nontemporal_store(s[m], (f4*) (tile + m * kS));
+    }
+}
+
+// ------------------------------------------------------------------ launch
+hipError_t launch_decode_fused(const FusedParams& p, hipStream_t stream) {
+    const dim3 grid((unsigned) ((long long) p.B * p.h_k));
+    hipLaunchKernelGGL(decode_fused_kernel, grid, dim3(256), 0, stream, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_step(const StepParams& p, hipStream_t stream) {
+    const dim3 grid((unsigned) ((long long) p.B * p.h_v));
+    const bool one = p.T == 1;
+    if (p.y) {
+        if (one) hipLaunchKernelGGL((decode_one_kernel<true>), grid, dim3(256), 0, stream, p);
+        else hipLaunchKernelGGL((decode_multi_kernel<true>), grid, dim3(256), 0, stream, p);
+    } else {
+        if (one) hipLaunchKernelGGL((decode_one_kernel<false>), grid, dim3(256), 0, stream, p);
+        else hipLaunchKernelGGL((decode_multi_kernel<false>), grid, dim3(256), 0, stream, p);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace gdn

@@ -21,7 +21,7 @@ EXPORTS = (
     "gdn_abi_version", "gdn_last_error", "gdn_state_pool_bytes", "gdn_state_pool_create",
     "gdn_state_pool_destroy", "gdn_state_pool_state", "gdn_state_pool_conv", "gdn_state_pool_flags",
     "gdn_state_pool_slots", "gdn_state_pool_zero", "gdn_conv_silu_norm", "gdn_decode_step",
-    "gdn_decode_step_norm", "gdn_gated_rmsnorm",
+    "gdn_decode_step_norm", "gdn_decode_fused", "gdn_gated_rmsnorm",
 )
 
 
@@ -82,6 +82,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "gdn_decode_step": ([vp, vp, vp, i32, i32, vp, vp, vp, vp, vp, vp, vp], ctypes.c_int),
         "gdn_decode_step_norm": ([vp, vp, vp, i32, i32, vp, vp, vp, vp, vp, vp, vp, f32, vp, vp, vp],
                                  ctypes.c_int),
+        "gdn_decode_fused": ([vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, f32, vp, vp, vp], ctypes.c_int),
         "gdn_gated_rmsnorm": ([vp, vp, vp, f32, i64, i32, vp, vp], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
@@ -213,6 +214,27 @@ def gdn_decode_step_norm(pool: StatePool, h, alpha, beta_logit, dt, ssm_a, z, no
     _check(load_library().gdn_decode_step_norm(pool.handle, _i32(slots, "slots", B), _i32(n_tok, "n_tok", B),
                                                B, T, *ptrs, float(eps), o_ptr,
                                                _f32(y, "y", (B, T, g.h_v * g.s)), _stream(h)))
+
+
+def gdn_decode_fused(pool: StatePool, qkv, conv_w, alpha, beta_logit, dt, ssm_a, z, norm_w, eps: float, y,
+                     h=None, slots=None):
+    """One decode token of the whole mixer in one launch. qkv [B][C] (or [B][1][C]);
+    alpha, beta_logit [B][h_v]; z, y [B][h_v*s]; h optional [B][C]."""
+    g = pool.geom
+    B = qkv.shape[0]
+
+    def ptr(t, name, n):
+        p_ = _f32(t, name)
+        if t.numel() != n:
+            raise ValueError(f"{name} must hold {n} elements, not {t.numel()}")
+        return p_
+    args = (ptr(qkv, "qkv", B * g.channels), _f32(conv_w, "conv_w", (g.channels, g.d_conv)),
+            ptr(alpha, "alpha", B * g.h_v), ptr(beta_logit, "beta_logit", B * g.h_v),
+            _f32(dt, "dt", (g.h_v,)), _f32(ssm_a, "ssm_a", (g.h_v,)), ptr(z, "z", B * g.h_v * g.s),
+            _f32(norm_w, "norm_w", (g.s,)))
+    _check(load_library().gdn_decode_fused(pool.handle, _i32(slots, "slots", B), B, *args, float(eps),
+                                           ptr(y, "y", B * g.h_v * g.s),
+                                           None if h is None else ptr(h, "h", B * g.channels), _stream(qkv)))
 
 
 def gdn_gated_rmsnorm(o, z, w, eps: float, y):

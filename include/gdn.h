@@ -163,6 +163,22 @@ int gdn_decode_step_norm(gdn_pool* p, const int32_t* slots, const int32_t* n_tok
                          const float* dt, const float* ssm_a, const float* z, const float* norm_w,
                          float eps, float* o, float* y, void* stream);
 
+/* One decode token of the whole mixer (steps 3-7 of gdn_layer) in a single launch:
+ * gdn_conv_silu_norm, then gdn_decode_step_norm, for B sequences x 1 token, with
+ * identical results (bit for bit).  One workgroup per (sequence, qk head) owns the
+ * conv channels of q, k and the value heads that share them, so h never goes
+ * through HBM unless asked for.
+ * slots   int32 [B] (NULL: slot b for sequence b)
+ * qkv     [B][C];  conv_w [C][d_conv];  alpha, beta_logit [B][h_v];  dt, ssm_a [h_v]
+ * z       [B][h_v*s];  norm_w [s];  eps (>= 0, used by both norms)
+ * y       [B][h_v*s]   output
+ * h       [B][C]       optional: NULL skips writing the conv/SiLU/L2 output
+ * h_v/h_k must be at most 14 (GDN_ERR_UNSUPPORTED otherwise). */
+int gdn_decode_fused(gdn_pool* p, const int32_t* slots, int32_t B, const float* qkv,
+                     const float* conv_w, const float* alpha, const float* beta_logit,
+                     const float* dt, const float* ssm_a, const float* z, const float* norm_w,
+                     float eps, float* y, float* h, void* stream);
+
 /* Step 7 of gdn_layer: per row of s values,
  *   y = o / sqrt(mean(o^2) + eps) * w * sigmoid(z)
  * o, z, y [rows][s] (rows = B*T*h_v); w [s], shared by all rows.  s must be 128.

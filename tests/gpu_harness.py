@@ -60,9 +60,10 @@ class GpuMixer:
         self.o = torch.empty(B, T, g.h_v, g.s, device="cuda")
         self.y = torch.empty(B, T, g.h_v * g.s, device="cuda")
 
-    def run(self, t0: int = 0, t1=None, slots=None, n_tok="default", fused: bool = False):
-        """One mixer pass over tokens [t0, t1) of every sequence (one call per kernel;
-        fused: the gated RMSNorm runs as the recurrence's epilogue)."""
+    def run(self, t0: int = 0, t1=None, slots=None, n_tok="default", fused=False):
+        """One mixer pass over tokens [t0, t1) of every sequence.  fused: False = three
+        calls; True or "norm" = conv + recurrence with the norm fused in; "one" = the
+        single-launch decode (one token, every sequence)."""
         import torch
         t1 = self.wl.T if t1 is None else t1
         sl = lambda x: x[:, t0:t1].contiguous()
@@ -74,8 +75,14 @@ class GpuMixer:
         y = torch.empty(B, T, g.h_v * g.s, device="cuda")
         slots = self.slots if slots is None else slots
         n_tok = self.n_tok if isinstance(n_tok, str) else n_tok
-        self.G.gdn_mixer(self.pool, qkv, alpha, bl, z, self.conv_w, self.dt, self.ssm_a, self.norm_w,
-                         self.wl.eps, h, o, y, slots, n_tok, fused=fused)
+        if fused == "one":
+            assert T == 1 and n_tok is None, "the single-launch decode takes one token per sequence"
+            o.zero_()
+            self.G.gdn_decode_fused(self.pool, qkv, self.conv_w, alpha, bl, self.dt, self.ssm_a, z, self.norm_w,
+                                    self.wl.eps, y, h, slots)
+        else:
+            self.G.gdn_mixer(self.pool, qkv, alpha, bl, z, self.conv_w, self.dt, self.ssm_a, self.norm_w,
+                             self.wl.eps, h, o, y, slots, n_tok, fused=bool(fused))
         self.h[:, t0:t1] = h
         self.o[:, t0:t1] = o
         self.y[:, t0:t1] = y

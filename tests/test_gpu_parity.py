@@ -28,13 +28,15 @@ def _workload_and_oracle(name):
     return _ORACLE[name]
 
 FUSED = pytest.mark.parametrize("fused", [False, True], ids=["3calls", "fused_norm"])
+# single-token workloads also run through the single-launch decode
+DECODE_MODES = pytest.mark.parametrize("fused", [False, True, "one"], ids=["3calls", "fused_norm", "one_launch"])
 
 
 def _stack(results, key, n=None):
     return np.stack([r[key] if n is None else r[key][:n] for r in results])
 
 
-def _compare_all(gm, wl, res, tol, tag):
+def _compare_all(gm, wl, res, tol, tag, keys=("o", "y", "h")):
     """Compare o, y, h for every valid token and the final state / conv of every slot."""
     o = gm.o.cpu().numpy()
     y = gm.y.cpu().numpy()
@@ -43,6 +45,8 @@ def _compare_all(gm, wl, res, tol, tag):
     cv = gm.pool.conv.cpu().numpy()
     errs = {}
     for key, arr in (("o", o), ("y", y), ("h", h)):
+        if key not in keys:
+            continue
         g_parts, r_parts = [], []
         for b in range(wl.B):
             n = wl.tokens_of(b)
@@ -59,7 +63,7 @@ def _compare_all(gm, wl, res, tol, tag):
 
 
 # ------------------------------------------------------------------ the five workloads
-@FUSED
+@DECODE_MODES
 def test_tiny_b1_t8_every_step(fused):
     """One sequence, 8 sequential single-token calls, parity after every step."""
     wl = W.tiny()
@@ -71,24 +75,25 @@ def test_tiny_b1_t8_every_step(fused):
         r = oracle.run_sequence(wl, 0, t, t + 1, state=st, conv_state=cs)
         st, cs = r["state"], r["conv_state"]
         assert_close(f"step {t} h", h.cpu().numpy()[0], r["h"], STEP_TOL)
-        assert_close(f"step {t} o", o.cpu().numpy()[0], r["o"], STEP_TOL)
+        if fused != "one":
+            assert_close(f"step {t} o", o.cpu().numpy()[0], r["o"], STEP_TOL)
         assert_close(f"step {t} y", y.cpu().numpy()[0], r["y"], STEP_TOL)
         assert_close(f"step {t} state", gm.slot_state(0), st, STEP_TOL)
         assert_close(f"step {t} conv", gm.slot_conv(0), cs, STEP_TOL)
     assert int(gm.pool.flags.item()) == 0
 
 
-@FUSED
+@DECODE_MODES
 def test_decode_b64_one_step(fused):
     log(f"decode_b64 fused={fused}: start")
     wl, res = _workload_and_oracle("b64")
     gm = GpuMixer(wl)
     gm.run(fused=fused)
-    _compare_all(gm, wl, res, STEP_TOL, "decode_b64")
+    _compare_all(gm, wl, res, STEP_TOL, "decode_b64", keys=("y", "h") if fused == "one" else ("o", "y", "h"))
     assert int(gm.pool.flags.item()) == 0
 
 
-@FUSED
+@DECODE_MODES
 def test_decode_b256_one_step(fused):
     """The bandwidth-bound decode: 256 sequences, 768 MiB of state, in the launch
     configuration the benchmark times."""
@@ -96,7 +101,7 @@ def test_decode_b256_one_step(fused):
     wl, res = _workload_and_oracle("b256")
     gm = GpuMixer(wl)
     gm.run(fused=fused)
-    _compare_all(gm, wl, res, STEP_TOL, "decode_b256")
+    _compare_all(gm, wl, res, STEP_TOL, "decode_b256", keys=("y", "h") if fused == "one" else ("o", "y", "h"))
 
 
 @FUSED
@@ -362,3 +367,57 @@ def test_fused_norm_equals_separate_norm(T):
     with pytest.raises(G.GdnError):
         G.gdn_decode_step_norm(c.pool, h, c.alpha, c.beta_logit, c.dt, c.ssm_a, c.z, c.norm_w, wl.eps, c.z,
                                None, c.slots, c.n_tok)   # y aliases z
+
+
+@FUSED
+def test_token_counts_across_conv_blocks(fused):
+    """Ragged counts that end before, at and across the conv kernel's 32-token blocks
+    (the history of later blocks comes from qkv, the stored history is written once)."""
+    wl = W.make("blocks", 6, 70, seed=60, n_slots=9, state_std=0.02, conv_std=1.0, slot_choice="random")
+    wl.n_tok = np.array([0, 1, 3, 33, 64, 70], np.int32)
+    log(f"conv token blocks, fused={fused}")
+    gm = GpuMixer(wl)
+    gm.run(fused=fused)
+    res = oracle.run_workload(wl)
+    _compare_all(gm, wl, res, 3 * STEP_TOL, "blocks")
+
+
+@pytest.mark.parametrize("geom", [W.Geom(), W.Geom(h_k=2, h_v=6), W.Geom(h_k=2, h_v=4), W.Geom(h_k=1, h_v=14)],
+                         ids=lambda g: f"hk{g.h_k}hv{g.h_v}")
+def test_single_launch_decode_equals_two_calls_bitwise(geom):
+    """gdn_decode_fused == gdn_conv_silu_norm + gdn_decode_step_norm, bit for bit, and
+    matches the oracle; without h it writes the same y and state."""
+    import torch
+    import gated_deltanet_mixer_gdn_amd as G
+    wl = W.make("one", 5, 1, seed=61 + geom.h_v, geom=geom, n_slots=8, state_std=0.02, conv_std=1.0,
+                slot_choice="random")
+    log(f"single-launch decode h_k={geom.h_k} h_v={geom.h_v}")
+    a = GpuMixer(wl)
+    a.run(fused=True)
+    b = GpuMixer(wl)
+    b.run(fused="one")
+    assert torch.equal(a.h, b.h) and torch.equal(a.y, b.y)
+    assert torch.equal(a.pool.state, b.pool.state) and torch.equal(a.pool.conv, b.pool.conv)
+    res = oracle.run_workload(wl)
+    _compare_all(b, wl, res, STEP_TOL, "one-launch", keys=("y", "h"))
+    c = GpuMixer(wl)
+    y = torch.empty_like(c.y[:, 0])
+    G.gdn_decode_fused(c.pool, c.qkv[:, 0].contiguous(), c.conv_w, c.alpha[:, 0].contiguous(),
+                       c.beta_logit[:, 0].contiguous(), c.dt, c.ssm_a, c.z[:, 0].contiguous(), c.norm_w, wl.eps, y,
+                       None, c.slots)
+    assert torch.equal(y, b.y[:, 0]) and torch.equal(c.pool.state, b.pool.state)
+
+
+def test_single_launch_decode_bad_slot():
+    import torch
+    wl = W.make("one-bad", 3, 1, seed=62, n_slots=4, state_std=0.02, conv_std=1.0)
+    gm = GpuMixer(wl)
+    before_s, before_c = gm.pool.state.clone(), gm.pool.conv.clone()
+    gm.run(fused="one", slots=dev(np.array([2, 9, -4], np.int32)))
+    assert int(gm.pool.flags.item()) & gm.G.GDN_FLAG_BAD_SLOT
+    assert (gm.y[1:] == 0).all() and (gm.h[1:] == 0).all()
+    keep = [0, 1, 3]
+    assert torch.equal(gm.pool.state[keep], before_s[keep]) and torch.equal(gm.pool.conv[keep], before_c[keep])
+    wl.slots = np.array([2, 0, 0], np.int32)
+    res = oracle.run_workload(wl, seqs=[0])
+    assert_close("one-bad y", gm.y[0].cpu().numpy(), res[0]["y"], STEP_TOL)
