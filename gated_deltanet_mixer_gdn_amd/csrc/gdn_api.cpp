@@ -195,9 +195,14 @@ int gdn_state_pool_zero(gdn_pool* p, const int32_t* slots, int32_t n, void* stre
     return launched(gdn::launch_zero(z, static_cast<hipStream_t>(stream)), fn);
 }
 
-int gdn_conv_silu_norm(gdn_pool* p, const int32_t* slots, const int32_t* n_tok, int32_t B, int32_t T,
-                       const float* qkv, const float* conv_w, float eps, float* h, void* stream) {
-    const char* fn = "gdn_conv_silu_norm";
+}  // extern "C"
+
+namespace {
+
+// Shared by gdn_conv_silu_norm (persist, h required), gdn_verify_window (no persist)
+// and gdn_commit (persist, h = null: history only).
+int conv_common(const char* fn, gdn_pool* p, const int32_t* slots, const int32_t* n_tok, int32_t B, int32_t T,
+                const float* qkv, const float* conv_w, float eps, float* h, bool persist, void* stream) {
     if (int rc = check_pool(p, fn)) return rc;
     if (B < 0) return fail(GDN_ERR_ARG, fn, "B=%d is negative", B);
     if (T < 1) return fail(GDN_ERR_ARG, fn, "T=%d must be >= 1", T);
@@ -206,15 +211,17 @@ int gdn_conv_silu_norm(gdn_pool* p, const int32_t* slots, const int32_t* n_tok, 
     const int n_tb = (T + gdn::kConvTokensPerBlock - 1) / gdn::kConvTokensPerBlock;
     if ((int64_t) B * n_tb > INT32_MAX) return fail(GDN_ERR_ARG, fn, "B*T too large");
     if (int rc = check_f4(qkv, fn, "qkv")) return rc;
-    if (int rc = check_f4(conv_w, fn, "conv_w")) return rc;
-    if (int rc = check_f4(h, fn, "h")) return rc;
+    if (h) {
+        if (int rc = check_f4(conv_w, fn, "conv_w")) return rc;
+        if (int rc = check_f4(h, fn, "h")) return rc;
+    }
     if (slots && !aligned(slots, 4)) return fail(GDN_ERR_ARG, fn, "slots is not 4-byte aligned");
     if (n_tok && !aligned(n_tok, 4)) return fail(GDN_ERR_ARG, fn, "n_tok is not 4-byte aligned");
     if (!slots && B > p->n_slots)
         return fail(GDN_ERR_ARG, fn, "slots is null and B=%d exceeds the pool's %lld slots", B,
                     (long long) p->n_slots);
     const size_t io = (size_t) B * T * channels(p->g) * sizeof(float);
-    if (overlap(qkv, io, h, io)) return fail(GDN_ERR_ARG, fn, "h overlaps qkv");
+    if (h && overlap(qkv, io, h, io)) return fail(GDN_ERR_ARG, fn, "h overlaps qkv");
     gdn::ConvParams c;
     c.conv = p->conv;
     c.slots = slots;
@@ -229,21 +236,18 @@ int gdn_conv_silu_norm(gdn_pool* p, const int32_t* slots, const int32_t* n_tok, 
     c.h_k = p->g.h_k;
     c.n_heads = 2 * p->g.h_k + p->g.h_v;
     c.n_tb = n_tb;
+    c.persist = persist ? 1 : 0;
     c.eps = eps;
     c.qscale = 1.0f / std::sqrt((float) p->g.s);
     return launched(gdn::launch_conv_silu_norm(c, static_cast<hipStream_t>(stream)), fn);
 }
 
-}  // extern "C"
-
-namespace {
-
-// Shared by gdn_decode_step (o required, no epilogue) and gdn_decode_step_norm
-// (y required, o optional).
+// Shared by gdn_decode_step (o required, no epilogue), gdn_decode_step_norm (y
+// required, o optional), gdn_verify_window (y, no persist) and gdn_commit (no outputs).
 int decode_common(const char* fn, gdn_pool* p, const int32_t* slots, const int32_t* n_tok, int32_t B,
                   int32_t T, const float* h, const float* alpha, const float* beta_logit, const float* dt,
                   const float* ssm_a, const float* z, const float* norm_w, float eps, float* o, float* y,
-                  void* stream) {
+                  bool persist, bool outputs, void* stream) {
     if (int rc = check_pool(p, fn)) return rc;
     if (B < 0) return fail(GDN_ERR_ARG, fn, "B=%d is negative", B);
     if (T < 1) return fail(GDN_ERR_ARG, fn, "T=%d must be >= 1", T);
@@ -256,7 +260,7 @@ int decode_common(const char* fn, gdn_pool* p, const int32_t* slots, const int32
     if (int rc = check_f1(beta_logit, fn, "beta_logit")) return rc;
     if (int rc = check_f1(dt, fn, "dt")) return rc;
     if (int rc = check_f1(ssm_a, fn, "ssm_a")) return rc;
-    if (o || !y)
+    if (o || (!y && outputs))
         if (int rc = check_f4(o, fn, "o")) return rc;
     if (y) {
         if (int rc = check_f4(z, fn, "z")) return rc;
@@ -299,6 +303,7 @@ int decode_common(const char* fn, gdn_pool* p, const int32_t* slots, const int32
     s.h_k = p->g.h_k;
     s.h_v = p->g.h_v;
     s.group = p->g.h_v / p->g.h_k;
+    s.persist = persist ? 1 : 0;
     s.eps = eps;
     return launched(gdn::launch_decode_step(s, static_cast<hipStream_t>(stream)), fn);
 }
@@ -311,7 +316,36 @@ int gdn_decode_step(gdn_pool* p, const int32_t* slots, const int32_t* n_tok, int
                     const float* h, const float* alpha, const float* beta_logit, const float* dt,
                     const float* ssm_a, float* o, void* stream) {
     return decode_common("gdn_decode_step", p, slots, n_tok, B, T, h, alpha, beta_logit, dt, ssm_a, nullptr,
-                         nullptr, 0.0f, o, nullptr, stream);
+                         nullptr, 0.0f, o, nullptr, true, true, stream);
+}
+
+int gdn_conv_silu_norm(gdn_pool* p, const int32_t* slots, const int32_t* n_tok, int32_t B, int32_t T,
+                       const float* qkv, const float* conv_w, float eps, float* h, void* stream) {
+    const char* fn = "gdn_conv_silu_norm";
+    if (B > 0 && !h) return fail(GDN_ERR_ARG, fn, "h is null");
+    return conv_common(fn, p, slots, n_tok, B, T, qkv, conv_w, eps, h, true, stream);
+}
+
+int gdn_verify_window(gdn_pool* p, const int32_t* slots, const int32_t* n_tok, int32_t B, int32_t T,
+                      const float* qkv, const float* conv_w, const float* alpha, const float* beta_logit,
+                      const float* dt, const float* ssm_a, const float* z, const float* norm_w, float eps,
+                      float* h, float* y, void* stream) {
+    const char* fn = "gdn_verify_window";
+    if (B > 0 && !h) return fail(GDN_ERR_ARG, fn, "h is null");
+    if (B > 0 && !y) return fail(GDN_ERR_ARG, fn, "y is null");
+    if (int rc = conv_common(fn, p, slots, n_tok, B, T, qkv, conv_w, eps, h, false, stream)) return rc;
+    return decode_common(fn, p, slots, n_tok, B, T, h, alpha, beta_logit, dt, ssm_a, z, norm_w, eps, nullptr, y,
+                         false, true, stream);
+}
+
+int gdn_commit(gdn_pool* p, const int32_t* slots, const int32_t* n_keep, int32_t B, int32_t T, const float* qkv,
+               const float* h, const float* alpha, const float* beta_logit, const float* dt, const float* ssm_a,
+               void* stream) {
+    const char* fn = "gdn_commit";
+    if (B > 0 && !h) return fail(GDN_ERR_ARG, fn, "h is null");
+    if (int rc = conv_common(fn, p, slots, n_keep, B, T, qkv, nullptr, 0.0f, nullptr, true, stream)) return rc;
+    return decode_common(fn, p, slots, n_keep, B, T, h, alpha, beta_logit, dt, ssm_a, nullptr, nullptr, 0.0f,
+                         nullptr, nullptr, true, false, stream);
 }
 
 int gdn_decode_step_norm(gdn_pool* p, const int32_t* slots, const int32_t* n_tok, int32_t B, int32_t T,
@@ -319,9 +353,9 @@ int gdn_decode_step_norm(gdn_pool* p, const int32_t* slots, const int32_t* n_tok
                          const float* ssm_a, const float* z, const float* norm_w, float eps, float* o,
                          float* y, void* stream) {
     const char* fn = "gdn_decode_step_norm";
-    if (!y) return fail(GDN_ERR_ARG, fn, "y is null");
+    if (B > 0 && !y) return fail(GDN_ERR_ARG, fn, "y is null");
     return decode_common(fn, p, slots, n_tok, B, T, h, alpha, beta_logit, dt, ssm_a, z, norm_w, eps, o, y,
-                         stream);
+                         true, true, stream);
 }
 
 int gdn_decode_fused(gdn_pool* p, const int32_t* slots, int32_t B, const float* qkv, const float* conv_w,

@@ -26,11 +26,13 @@ struct ConvParams {
     const int32_t* n_tok;   // [B] or null
     const float* qkv;       // [B][T][C]
     const float* w;         // [C][4]
-    float* h;               // [B][T][C]
+    float* h;               // [B][T][C], or null: history-only mode (advance the stored
+                            // history by n_tok raw rows, compute nothing)
     uint32_t* flags;        // pool flag word
     long long n_slots;
     int B, T, h_k, n_heads; // n_heads = 2*h_k + h_v (128-channel heads)
     int n_tb;               // token blocks per sequence
+    int persist;            // 0: leave the stored history untouched (speculative window)
     float eps, qscale;
 };
 
@@ -43,13 +45,14 @@ struct StepParams {
     const float* beta_logit;
     const float* dt;        // [h_v]
     const float* ssm_a;     // [h_v]
-    float* o;               // [B][T][h_v][128], or null (fused form only)
+    float* o;               // [B][T][h_v][128], or null: not written
     const float* z;         // fused gated RMSNorm epilogue: [B][T][h_v*128], or null
     const float* norm_w;    // [128]
     float* y;               // [B][T][h_v*128], or null: no epilogue
     uint32_t* flags;
     long long n_slots;
     int B, T, h_k, h_v, group;  // group = h_v / h_k
+    int persist;            // 0: leave the state untouched (speculative window)
     float eps;              // RMSNorm epsilon (epilogue only)
 };
 

@@ -129,7 +129,7 @@ __global__ __launch_bounds__(256) void decode_one_kernel(StepParams p) {
     if (job.nt == 0) {   // no token (or an unknown slot): outputs zero, state untouched
         if (rg == 0) {
             const f4 zero = {0.f, 0.f, 0.f, 0.f};
-            if (!kNorm || p.o) *(f4*) (p.o + e * kS + cg * 4) = zero;
+            if (p.o) *(f4*) (p.o + e * kS + cg * 4) = zero;
             if (kNorm) *(f4*) (p.y + e * kS + cg * 4) = zero;
         }
         return;
@@ -149,9 +149,9 @@ __global__ __launch_bounds__(256) void decode_one_kernel(StepParams p) {
     const float eg = expf(softplus_f(p.alpha[e] + p.dt[i]) * p.ssm_a[i]);
     __syncthreads();
 
-    head_token_256<kNorm>(s, qk_lds, v, beta, eg, red, (!kNorm || p.o) ? p.o + e * kS : nullptr,
+    head_token_256<kNorm>(s, qk_lds, v, beta, eg, red, p.o ? p.o + e * kS : nullptr,
                           kNorm ? p.z + e * kS : nullptr, p.norm_w, kNorm ? p.y + e * kS : nullptr, p.eps);
-    store_tile(s, tile);
+    if (p.persist) store_tile(s, tile);
 }
 
 // The whole mixer for one decode token in one launch.  One workgroup of 256 threads
@@ -348,7 +348,7 @@ __global__ __launch_bounds__(256) void decode_multi_kernel(StepParams p) {
         kq = add_xor32(add_xor16(add_xor8(kq)));
         const f4 d = beta * fma4(-eg, pk, v);
         const f4 out = fma4(kq, d, eg * pq);
-        if ((!kNorm || p.o) && rg == 0) *(f4*) (p.o + ((tok0 + t) * p.h_v + i) * kS + col) = out;
+        if (p.o && rg == 0) *(f4*) (p.o + ((tok0 + t) * p.h_v + i) * kS + col) = out;
         if (kNorm) {
             const int par = (t / kNormChunk) & 1;
             const int slot8 = t % kNormChunk;
@@ -388,14 +388,11 @@ __global__ __launch_bounds__(256) void decode_multi_kernel(StepParams p) {
         const f4 zero = {0.f, 0.f, 0.f, 0.f};
         for (int t = nt; t < p.T; ++t) {
             const long long e = ((tok0 + t) * p.h_v + i) * kS + col;
-            if (!kNorm || p.o) *(f4*) (p.o + e) = zero;
+            if (p.o) *(f4*) (p.o + e) = zero;
             if (kNorm) *(f4*) (p.y + e) = zero;
         }
     }
-    if (nt > 0) {
-#pragma unroll
-        for (int m = 0; m < 16; ++m) __builtin_nontemporal_store(s[m], (f4*) (tile + m * kS));
-    }
+    if (nt > 0 && p.persist) store_tile(s, tile);
 }
 
 // ------------------------------------------------------------------ launch

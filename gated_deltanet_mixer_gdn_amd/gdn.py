@@ -21,7 +21,7 @@ EXPORTS = (
     "gdn_abi_version", "gdn_last_error", "gdn_state_pool_bytes", "gdn_state_pool_create",
     "gdn_state_pool_destroy", "gdn_state_pool_state", "gdn_state_pool_conv", "gdn_state_pool_flags",
     "gdn_state_pool_slots", "gdn_state_pool_zero", "gdn_conv_silu_norm", "gdn_decode_step",
-    "gdn_decode_step_norm", "gdn_decode_fused", "gdn_gated_rmsnorm",
+    "gdn_decode_step_norm", "gdn_decode_fused", "gdn_verify_window", "gdn_commit", "gdn_gated_rmsnorm",
 )
 
 
@@ -83,6 +83,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "gdn_decode_step_norm": ([vp, vp, vp, i32, i32, vp, vp, vp, vp, vp, vp, vp, f32, vp, vp, vp],
                                  ctypes.c_int),
         "gdn_decode_fused": ([vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, f32, vp, vp, vp], ctypes.c_int),
+        "gdn_verify_window": ([vp, vp, vp, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, f32, vp, vp, vp],
+                              ctypes.c_int),
+        "gdn_commit": ([vp, vp, vp, i32, i32, vp, vp, vp, vp, vp, vp, vp], ctypes.c_int),
         "gdn_gated_rmsnorm": ([vp, vp, vp, f32, i64, i32, vp, vp], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
@@ -235,6 +238,33 @@ def gdn_decode_fused(pool: StatePool, qkv, conv_w, alpha, beta_logit, dt, ssm_a,
     _check(load_library().gdn_decode_fused(pool.handle, _i32(slots, "slots", B), B, *args, float(eps),
                                            ptr(y, "y", B * g.h_v * g.s),
                                            None if h is None else ptr(h, "h", B * g.channels), _stream(qkv)))
+
+
+def gdn_verify_window(pool: StatePool, qkv, conv_w, alpha, beta_logit, dt, ssm_a, z, norm_w, eps: float, h, y,
+                      slots=None, n_tok=None):
+    """A speculative window of T tokens from the untouched pool: writes h [B][T][C] and
+    y [B][T][h_v*s]; persists nothing."""
+    g = pool.geom
+    B, T = qkv.shape[0], qkv.shape[1]
+    ptrs = (_f32(qkv, "qkv", (B, T, g.channels)), _f32(conv_w, "conv_w", (g.channels, g.d_conv)),
+            _f32(alpha, "alpha", (B, T, g.h_v)), _f32(beta_logit, "beta_logit", (B, T, g.h_v)),
+            _f32(dt, "dt", (g.h_v,)), _f32(ssm_a, "ssm_a", (g.h_v,)), _f32(z, "z", (B, T, g.h_v * g.s)),
+            _f32(norm_w, "norm_w", (g.s,)))
+    _check(load_library().gdn_verify_window(pool.handle, _i32(slots, "slots", B), _i32(n_tok, "n_tok", B), B, T,
+                                            *ptrs, float(eps), _f32(h, "h", (B, T, g.channels)),
+                                            _f32(y, "y", (B, T, g.h_v * g.s)), _stream(qkv)))
+
+
+def gdn_commit(pool: StatePool, qkv, h, alpha, beta_logit, dt, ssm_a, n_keep=None, slots=None):
+    """Commit the first n_keep[b] tokens of a window: advance the conv history by their
+    raw qkv rows and replay their recurrence from the window's h into the state."""
+    g = pool.geom
+    B, T = qkv.shape[0], qkv.shape[1]
+    ptrs = (_f32(qkv, "qkv", (B, T, g.channels)), _f32(h, "h", (B, T, g.channels)),
+            _f32(alpha, "alpha", (B, T, g.h_v)), _f32(beta_logit, "beta_logit", (B, T, g.h_v)),
+            _f32(dt, "dt", (g.h_v,)), _f32(ssm_a, "ssm_a", (g.h_v,)))
+    _check(load_library().gdn_commit(pool.handle, _i32(slots, "slots", B), _i32(n_keep, "n_keep", B), B, T,
+                                     *ptrs, _stream(qkv)))
 
 
 def gdn_gated_rmsnorm(o, z, w, eps: float, y):

@@ -179,6 +179,29 @@ int gdn_decode_fused(gdn_pool* p, const int32_t* slots, int32_t B, const float* 
                      const float* dt, const float* ssm_a, const float* z, const float* norm_w,
                      float eps, float* y, float* h, void* stream);
 
+/* ---------------------------------------------------------------- speculative window
+ * The pages' second GDN workload: a verify window runs T drafted tokens from the
+ * UNTOUCHED state and conv history (outputs only), and a commit then advances each
+ * sequence by the n_keep tokens it accepted (verify.cpp: the GDN branch of the window,
+ * and capture_commit's gdn_conv_commit + replay).  Window then commit equals decoding
+ * the n_keep tokens directly, bit for bit. */
+
+/* gdn_conv_silu_norm + gdn_decode_step_norm over the window, persisting nothing:
+ * h [B][T][C] (keep it for the commit) and y [B][T][h_v*s] are written; the pool is
+ * read only.  n_tok as in gdn_decode_step (NULL: all T). */
+int gdn_verify_window(gdn_pool* p, const int32_t* slots, const int32_t* n_tok, int32_t B, int32_t T,
+                      const float* qkv, const float* conv_w, const float* alpha,
+                      const float* beta_logit, const float* dt, const float* ssm_a, const float* z,
+                      const float* norm_w, float eps, float* h, float* y, void* stream);
+
+/* Commit the first n_keep[b] tokens of a window (n_keep int32 [B] in [0, T], NULL = T):
+ * the conv history advances by those tokens' raw qkv rows, and the recurrence replays
+ * them from the window's h, writing the state.  Nothing else is written.  qkv, h,
+ * alpha and beta_logit are the window's arrays. */
+int gdn_commit(gdn_pool* p, const int32_t* slots, const int32_t* n_keep, int32_t B, int32_t T,
+               const float* qkv, const float* h, const float* alpha, const float* beta_logit,
+               const float* dt, const float* ssm_a, void* stream);
+
 /* Step 7 of gdn_layer: per row of s values,
  *   y = o / sqrt(mean(o^2) + eps) * w * sigmoid(z)
  * o, z, y [rows][s] (rows = B*T*h_v); w [s], shared by all rows.  s must be 128.

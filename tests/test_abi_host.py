@@ -169,3 +169,19 @@ def test_import_without_gpu_does_not_load_library():
             "assert g._lib is None; print('ok')")
     out = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True)
     assert out.returncode == 0 and "ok" in out.stdout, out.stderr
+
+
+def test_new_entry_points_reject_null_pool(L):
+    from gated_deltanet_mixer_gdn_amd.gdn import GDN_ERR_ARG, GDN_OK
+    assert L.gdn_decode_step_norm(None, None, None, 1, 1, 16, 16, 16, 16, 16, 16, 16, 1e-6, None, 16, None) == GDN_ERR_ARG
+    assert L.gdn_last_error().startswith(b"gdn_decode_step_norm: pool is null")
+    assert L.gdn_decode_step_norm(None, None, None, 1, 1, 16, 16, 16, 16, 16, 16, 16, 1e-6, None, None, None) == GDN_ERR_ARG
+    assert b"y is null" in L.gdn_last_error()
+    assert L.gdn_decode_fused(None, None, 1, 16, 16, 16, 16, 16, 16, 16, 16, 1e-6, 16, None, None) == GDN_ERR_ARG
+    assert L.gdn_last_error().startswith(b"gdn_decode_fused: pool is null")
+    assert L.gdn_verify_window(None, None, None, 1, 2, 16, 16, 16, 16, 16, 16, 16, 16, 1e-6, 16, 16, None) == GDN_ERR_ARG
+    assert L.gdn_last_error().startswith(b"gdn_verify_window: pool is null")
+    assert L.gdn_verify_window(None, None, None, 1, 2, 16, 16, 16, 16, 16, 16, 16, 16, 1e-6, None, 16, None) == GDN_ERR_ARG
+    assert b"h is null" in L.gdn_last_error()
+    assert L.gdn_commit(None, None, None, 1, 2, 16, 16, 16, 16, 16, 16, None) == GDN_ERR_ARG
+    assert L.gdn_last_error().startswith(b"gdn_commit: pool is null")

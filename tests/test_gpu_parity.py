@@ -421,3 +421,45 @@ def test_single_launch_decode_bad_slot():
     wl.slots = np.array([2, 0, 0], np.int32)
     res = oracle.run_workload(wl, seqs=[0])
     assert_close("one-bad y", gm.y[0].cpu().numpy(), res[0]["y"], STEP_TOL)
+
+
+@pytest.mark.parametrize("T", [1, 4, 37])
+def test_verify_window_then_commit(T):
+    """A window of T drafted tokens from the untouched state, then a commit of n_keep
+    accepted tokens per sequence, equals decoding those tokens directly, bit for bit
+    (the pages' speculative window and commit)."""
+    import torch
+    import gated_deltanet_mixer_gdn_amd as G
+    wl = W.make("window", 5, T, seed=70 + T, n_slots=8, state_std=0.02, conv_std=1.0, slot_choice="random")
+    n_keep = np.minimum(np.array([T, 0, 1, max(T - 1, 0), 2], np.int32), T).astype(np.int32)
+    log(f"verify window T={T} n_keep={n_keep.tolist()}")
+    win = GpuMixer(wl)
+    before_s, before_c = win.pool.state.clone(), win.pool.conv.clone()
+    h = torch.empty_like(win.h)
+    y = torch.empty_like(win.y)
+    G.gdn_verify_window(win.pool, win.qkv, win.conv_w, win.alpha, win.beta_logit, win.dt, win.ssm_a, win.z,
+                        win.norm_w, wl.eps, h, y, win.slots)
+    torch.cuda.synchronize()
+    assert torch.equal(win.pool.state, before_s) and torch.equal(win.pool.conv, before_c), "window wrote the pool"
+    direct = GpuMixer(wl)
+    direct.run(fused=True)                        # all T tokens, persisted
+    assert torch.equal(y, direct.y) and torch.equal(h, direct.h)
+    res = oracle.run_workload(wl)
+    assert_close("window y", y.cpu().numpy(), np.stack([r["y"] for r in res]), 2 * STEP_TOL)
+
+    G.gdn_commit(win.pool, win.qkv, h, win.alpha, win.beta_logit, win.dt, win.ssm_a, dev(n_keep), win.slots)
+    kept = GpuMixer(wl)
+    kept.run(fused=True, n_tok=dev(n_keep))       # only the accepted tokens, persisted
+    assert torch.equal(win.pool.state, kept.pool.state)
+    assert torch.equal(win.pool.conv, kept.pool.conv)
+    assert int(win.pool.flags.item()) == 0
+    # the next decode token continues identically from both pools
+    nxt = W.make("window-next", 5, 1, seed=90 + T, n_slots=8, state_std=0.02, conv_std=1.0)
+    for gm in (win, kept):
+        q, a_, b_, z_ = dev(nxt.qkv), dev(nxt.alpha), dev(nxt.beta_logit), dev(nxt.z)
+        hh = torch.empty(5, 1, wl.geom.channels, device="cuda")
+        yy = torch.empty(5, 1, wl.geom.value_dim, device="cuda")
+        G.gdn_conv_silu_norm(gm.pool, q, gm.conv_w, wl.eps, hh, gm.slots)
+        G.gdn_decode_step_norm(gm.pool, hh, a_, b_, gm.dt, gm.ssm_a, z_, gm.norm_w, wl.eps, yy, None, gm.slots)
+        gm.next_y = yy
+    assert torch.equal(win.next_y, kept.next_y)
