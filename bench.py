@@ -240,6 +240,24 @@ def main():
     # the fastest form at large batch
     ms_per_step, k_ms, n_samples = timed(step_fused, 3, ("conv", "step_norm"))
     two_ms, two_k, dominant = ms_per_step, k_ms, "step_norm"
+    # context: the alpha / beta projections that feed this step (n_embd = 2560, bf16 weights)
+    ab = W.make_ab(wl.B, wl.T, seed=11)
+    ab_x = dev(ab.x)
+    ab_wa = torch.from_numpy(ab.w_alpha.view(np.int16)).cuda()
+    ab_wb = torch.from_numpy(ab.w_beta.view(np.int16)).cuda()
+    ab_a, ab_b = torch.empty_like(alpha), torch.empty_like(bl)
+    for _ in range(5):
+        G.gdn_ab_project(ab_x, ab_wa, ab_wb, ab_a, ab_b)
+    ae = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ae[0].record(stream)
+    for _ in range(50):
+        G.gdn_ab_project(ab_x, ab_wa, ab_wb, ab_a, ab_b)
+    ae[1].record(stream)
+    torch.cuda.synchronize()
+    ab_us = ae[0].elapsed_time(ae[1]) / 50 * 1000.0
+    ab_bytes = ab.x.nbytes + ab.w_alpha.nbytes + ab.w_beta.nbytes + 2 * ab_a.numel() * 4
+    del ab_x, ab_a, ab_b
+
     # context: a plain device-to-device copy of the state's size on the same stream
     ref_src = pool.state.view(-1)
     ref_dst = torch.empty_like(ref_src)
@@ -269,6 +287,7 @@ def main():
         log(f"one launch: {one_k['one'] * 1000:.1f}us kernel; {one_ms * 1000:.1f} us/step; {one_gbps:.0f} GB/s")
     log("two calls: " + ", ".join(f"{k}={v * 1000:.1f}us" for k, v in two_k.items()) +
         f"; {two_ms * 1000:.1f} us/step; recurrence+norm kernel {two_gbps:.0f} GB/s")
+    log(f"ab projection: {ab_us:.1f} us for {wl.B * wl.T} rows ({ab_bytes / ab_us / 1e3:.0f} GB/s)")
     log("three calls: " + ", ".join(f"{k}={v * 1000:.1f}us" for k, v in three_k.items()) +
         f"; {three_ms * 1000:.1f} us/step; recurrence kernel {three_step_gbps:.0f} GB/s; d2d copy {copy_gbps:.0f} GB/s")
     traffic = read_traffic() if args.config == "b256" else None
@@ -307,6 +326,8 @@ def main():
                             "value": units / (three_ms / 1000.0),
                             "recurrence_kernel_gbps": three_step_gbps},
         "d2d_copy_gbps_same_size": copy_gbps,
+        "ab_projection": {"us": ab_us, "algorithmic_bytes": int(ab_bytes), "gbps": ab_bytes / ab_us / 1e3,
+                          "rows": wl.B * wl.T, "n_embd": W.N_EMBD},
         "roofline": {"kernel": "decode_one_kernel<fused norm>" if wl.T == 1 else "decode_multi_kernel<fused norm>",
                      "bound": "hbm",
                      "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",

@@ -15,6 +15,7 @@
 
 #include "gdn.h"
 #include "gdn_kernels.h"
+#include "gdn_proj.h"
 
 struct gdn_pool {
     gdn_geom g;
@@ -419,6 +420,37 @@ int gdn_decode_fused(gdn_pool* p, const int32_t* slots, int32_t B, const float* 
     f.eps = eps;
     f.qscale = 1.0f / std::sqrt((float) p->g.s);
     return launched(gdn::launch_decode_fused(f, static_cast<hipStream_t>(stream)), fn);
+}
+
+int gdn_ab_project(const float* x, const uint16_t* w_alpha, const uint16_t* w_beta, int64_t rows, int32_t n_embd,
+                   int32_t h_v, float* alpha, float* beta_logit, void* stream) {
+    const char* fn = "gdn_ab_project";
+    if (rows < 0) return fail(GDN_ERR_ARG, fn, "rows=%lld is negative", (long long) rows);
+    if (n_embd <= 0 || h_v <= 0) return fail(GDN_ERR_ARG, fn, "n_embd=%d and h_v=%d must be positive", n_embd, h_v);
+    if (n_embd % 4 != 0) return fail(GDN_ERR_UNSUPPORTED, fn, "n_embd=%d is not a multiple of 4", n_embd);
+    if (rows == 0) return ok();
+    const long long jobs = (rows + gdn::kAbRows - 1) / gdn::kAbRows * ((2LL * h_v + gdn::kAbCols - 1) / gdn::kAbCols);
+    if ((jobs + 3) / 4 > INT32_MAX) return fail(GDN_ERR_ARG, fn, "rows too large");
+    if (int rc = check_f4(x, fn, "x")) return rc;
+    if (!w_alpha || !aligned(w_alpha, 8)) return fail(GDN_ERR_ARG, fn, "w_alpha is null or not 8-byte aligned");
+    if (!w_beta || !aligned(w_beta, 8)) return fail(GDN_ERR_ARG, fn, "w_beta is null or not 8-byte aligned");
+    if (int rc = check_f1(alpha, fn, "alpha")) return rc;
+    if (int rc = check_f1(beta_logit, fn, "beta_logit")) return rc;
+    const size_t out = (size_t) rows * h_v * sizeof(float);
+    const size_t xin = (size_t) rows * n_embd * sizeof(float);
+    if (overlap(alpha, out, beta_logit, out)) return fail(GDN_ERR_ARG, fn, "alpha overlaps beta_logit");
+    if (overlap(alpha, out, x, xin) || overlap(beta_logit, out, x, xin))
+        return fail(GDN_ERR_ARG, fn, "an output overlaps x");
+    gdn::AbParams a;
+    a.x = x;
+    a.w_alpha = w_alpha;
+    a.w_beta = w_beta;
+    a.alpha = alpha;
+    a.beta_logit = beta_logit;
+    a.rows = rows;
+    a.n_embd = n_embd;
+    a.h_v = h_v;
+    return launched(gdn::launch_ab_project(a, static_cast<hipStream_t>(stream)), fn);
 }
 
 int gdn_gated_rmsnorm(const float* o, const float* z, const float* w, float eps, int64_t rows, int32_t s,

@@ -22,6 +22,7 @@ EXPORTS = (
     "gdn_state_pool_destroy", "gdn_state_pool_state", "gdn_state_pool_conv", "gdn_state_pool_flags",
     "gdn_state_pool_slots", "gdn_state_pool_zero", "gdn_conv_silu_norm", "gdn_decode_step",
     "gdn_decode_step_norm", "gdn_decode_fused", "gdn_verify_window", "gdn_commit", "gdn_gated_rmsnorm",
+    "gdn_ab_project",
 )
 
 
@@ -87,6 +88,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                               ctypes.c_int),
         "gdn_commit": ([vp, vp, vp, i32, i32, vp, vp, vp, vp, vp, vp, vp], ctypes.c_int),
         "gdn_gated_rmsnorm": ([vp, vp, vp, f32, i64, i32, vp, vp], ctypes.c_int),
+        "gdn_ab_project": ([vp, vp, vp, i64, i32, i32, vp, vp, vp], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -288,3 +290,21 @@ def gdn_mixer(pool: StatePool, qkv, alpha, beta_logit, z, conv_w, dt, ssm_a, nor
     else:
         gdn_decode_step(pool, h, alpha, beta_logit, dt, ssm_a, o, slots, n_tok)
         gdn_gated_rmsnorm(o, z, norm_w, eps, y)
+
+
+def gdn_ab_project(x, w_alpha, w_beta, alpha, beta_logit):
+    """x [.., n_embd] fp32; w_alpha, w_beta [h_v][n_embd] bf16 bits (torch.int16 or
+    torch.uint16 tensors); alpha, beta_logit [.., h_v] fp32 outputs."""
+    import torch
+    n_embd = x.shape[-1]
+    rows = x.numel() // n_embd
+    h_v = w_alpha.shape[0]
+    for t, name in ((w_alpha, "w_alpha"), (w_beta, "w_beta")):
+        if t.dtype not in (torch.int16, torch.uint16) or not t.is_cuda or not t.is_contiguous() \
+                or tuple(t.shape) != (h_v, n_embd):
+            raise ValueError(f"{name} must be a contiguous 16-bit CUDA tensor of shape {(h_v, n_embd)}")
+    for t, name in ((alpha, "alpha"), (beta_logit, "beta_logit")):
+        if t.numel() != rows * h_v:
+            raise ValueError(f"{name} must hold {rows * h_v} elements")
+    _check(load_library().gdn_ab_project(_f32(x, "x"), w_alpha.data_ptr(), w_beta.data_ptr(), rows, n_embd, h_v,
+                                         _f32(alpha, "alpha"), _f32(beta_logit, "beta_logit"), _stream(x)))

@@ -165,3 +165,31 @@ CONFIGS = {
     "prefill": prefill_b16_t512,
     "ragged": ragged_pool,
 }
+
+
+# ------------------------------------------------------------------ the alpha / beta projections
+N_EMBD = 2560   # hidden size of the pages' model (each of the 48 projection rows walks 2,560 elements)
+
+
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> bf16 bit patterns, round to nearest even (input generation only)."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return u.astype(np.uint16)
+
+
+@dataclass
+class AbWorkload:
+    x: np.ndarray          # [B][T][n_embd] fp32 hidden states
+    w_alpha: np.ndarray    # [h_v][n_embd] bf16 bits
+    w_beta: np.ndarray     # [h_v][n_embd] bf16 bits
+
+
+def make_ab(B: int, T: int, seed: int, n_embd: int = N_EMBD, h_v: int = H_V) -> AbWorkload:
+    """x ~ N(0, 1); weights ~ N(0, 1/sqrt(n_embd)) rounded to bf16."""
+    rng = np.random.default_rng(seed)
+    std = 1.0 / np.sqrt(n_embd)
+    w_alpha = bf16_bits(_normal(rng, (h_v, n_embd), std))
+    w_beta = bf16_bits(_normal(rng, (h_v, n_embd), std))
+    x = _normal(rng, (B, T, n_embd))
+    return AbWorkload(x, w_alpha, w_beta)

@@ -209,6 +209,19 @@ int gdn_commit(gdn_pool* p, const int32_t* slots, const int32_t* n_keep, int32_t
 int gdn_gated_rmsnorm(const float* o, const float* z, const float* w, float eps, int64_t rows,
                       int32_t s, float* y, void* stream);
 
+/* ---------------------------------------------------------------- the step before the mixer
+ * The alpha / beta projections of step 5 of gdn_layer ("The weights are BF16";
+ * the native path consumes F32 activations): for every row r of x (one token),
+ *   alpha[r][i]      = sum_e w_alpha[i][e] * x[r][e]
+ *   beta_logit[r][i] = sum_e w_beta[i][e]  * x[r][e]
+ * x [rows][n_embd] fp32 (16-byte aligned, n_embd a multiple of 4);
+ * w_alpha, w_beta [h_v][n_embd] bf16 bit patterns (8-byte aligned);
+ * alpha, beta_logit [rows][h_v] fp32 outputs, laid out as gdn_decode_step's inputs
+ * ([B][T][h_v] when the rows are the B x T tokens).  The sigmoid / softplus that
+ * follow them run inside the recurrence kernels.  rows = 0 is a no-op. */
+int gdn_ab_project(const float* x, const uint16_t* w_alpha, const uint16_t* w_beta, int64_t rows,
+                   int32_t n_embd, int32_t h_v, float* alpha, float* beta_logit, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -54,6 +54,11 @@ def lib():
         L.gdn_oracle_delta_rule.argtypes = [i, i, i, i, _D, _D, _D, _D, _D]
         L.gdn_oracle_gated_rmsnorm.argtypes = [i64, i, _D, _D, _D, d, _D]
         L.gdn_oracle_mixer.argtypes = [i, i, i, i, i] + [_D] * 8 + [d] + [_D] * 6
+        U16 = ctypes.POINTER(ctypes.c_uint16)
+        L.gdn_oracle_bf16_value.argtypes = [ctypes.c_uint16]
+        L.gdn_oracle_bf16_value.restype = d
+        L.gdn_oracle_ab_project.argtypes = [i64, i, i, _D, U16, U16, _D, _D]
+        L.gdn_oracle_ab_project.restype = i
         for f in ("conv_silu_norm", "beta_gate", "delta_rule", "gated_rmsnorm", "mixer"):
             getattr(L, "gdn_oracle_" + f).restype = i
         _lib = L
@@ -142,6 +147,27 @@ def mixer(geom, qkv, conv_w, alpha, beta_logit, dt, ssm_a, z, norm_w, eps, conv_
                                   float(eps), _p(cs), _p(st), _p(h), _p(o), _p(y), _p(scratch)),
            "mixer")
     return {"h": h, "o": o, "y": y, "state": st, "conv_state": cs}
+
+
+def bf16_value(bits: int) -> float:
+    return lib().gdn_oracle_bf16_value(int(bits))
+
+
+def ab_project(x, w_alpha_bits, w_beta_bits):
+    """x [..][n_embd]; w_* [h_v][n_embd] uint16 bf16 bits -> (alpha, beta_logit) [..][h_v]."""
+    x = _f64(x)
+    shape = x.shape[:-1]
+    n_embd = x.shape[-1]
+    x2 = x.reshape(-1, n_embd)
+    wa = np.ascontiguousarray(w_alpha_bits, dtype=np.uint16)
+    wb = np.ascontiguousarray(w_beta_bits, dtype=np.uint16)
+    h_v = wa.shape[0]
+    alpha = np.zeros((x2.shape[0], h_v))
+    beta = np.zeros((x2.shape[0], h_v))
+    U16 = ctypes.POINTER(ctypes.c_uint16)
+    _check(lib().gdn_oracle_ab_project(x2.shape[0], n_embd, h_v, _p(x2), wa.ctypes.data_as(U16),
+                                       wb.ctypes.data_as(U16), _p(alpha), _p(beta)), "ab_project")
+    return alpha.reshape(*shape, h_v), beta.reshape(*shape, h_v)
 
 
 def run_sequence(wl, b: int, t0: int = 0, t1: Optional[int] = None, state=None, conv_state=None):

@@ -42,6 +42,7 @@
 #include <math.h>
 #include <stdint.h>
 #include <stddef.h>
+#include <string.h>
 
 #define GDN_ORACLE_OK 0
 #define GDN_ORACLE_BAD_ARG (-1)
@@ -232,6 +233,43 @@ int gdn_oracle_mixer(int h_k, int h_v, int s, int d_conv, int T,
         if (rc) return rc;
         rc = gdn_oracle_gated_rmsnorm(h_v, s, o + t * V, z + t * V, norm_w, eps, y + t * V);
         if (rc) return rc;
+    }
+    return GDN_ORACLE_OK;
+}
+
+/*
+ * The step before the mixer: the alpha and beta projections of step 5 of gdn_layer
+ * ("beta and the gate. The weights are BF16"; the native path consumes F32
+ * activations).  For every row r of x:
+ *   alpha[r][i]      = sum_e w_alpha[i][e] * x[r][e]
+ *   beta_logit[r][i] = sum_e w_beta[i][e]  * x[r][e]
+ * The weights are bf16 bit patterns: a bf16 value is the upper half of an IEEE
+ * binary32, so its value is that of the float with those 16 bits followed by 16
+ * zero bits.
+ *   x [rows][n_embd];  w_alpha, w_beta [h_v][n_embd] (uint16 bits);  outputs [rows][h_v]
+ */
+double gdn_oracle_bf16_value(uint16_t bits) {
+    const uint32_t u = (uint32_t) bits << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double) f;
+}
+
+int gdn_oracle_ab_project(int64_t rows, int n_embd, int h_v, const double* x, const uint16_t* w_alpha,
+                          const uint16_t* w_beta, double* alpha, double* beta_logit) {
+    if (rows < 0 || n_embd <= 0 || h_v <= 0 || !x || !w_alpha || !w_beta || !alpha || !beta_logit)
+        return GDN_ORACLE_BAD_ARG;
+    for (int64_t r = 0; r < rows; ++r) {
+        const double* xr = x + r * n_embd;
+        for (int i = 0; i < h_v; ++i) {
+            double a = 0.0, b = 0.0;
+            for (int e = 0; e < n_embd; ++e) {
+                a += gdn_oracle_bf16_value(w_alpha[(int64_t) i * n_embd + e]) * xr[e];
+                b += gdn_oracle_bf16_value(w_beta[(int64_t) i * n_embd + e]) * xr[e];
+            }
+            alpha[r * h_v + i] = a;
+            beta_logit[r * h_v + i] = b;
+        }
     }
     return GDN_ORACLE_OK;
 }

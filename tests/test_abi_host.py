@@ -185,3 +185,17 @@ def test_new_entry_points_reject_null_pool(L):
     assert b"h is null" in L.gdn_last_error()
     assert L.gdn_commit(None, None, None, 1, 2, 16, 16, 16, 16, 16, 16, None) == GDN_ERR_ARG
     assert L.gdn_last_error().startswith(b"gdn_commit: pool is null")
+
+
+def test_ab_project_argument_errors(L):
+    from gated_deltanet_mixer_gdn_amd.gdn import GDN_ERR_ARG, GDN_ERR_UNSUPPORTED, GDN_OK
+    assert L.gdn_ab_project(16, 16, 16, -1, 2560, 48, 16, 16, None) == GDN_ERR_ARG
+    assert L.gdn_ab_project(16, 16, 16, 4, 2562, 48, 16, 16, None) == GDN_ERR_UNSUPPORTED
+    assert L.gdn_ab_project(16, 16, 16, 4, 0, 48, 16, 16, None) == GDN_ERR_ARG
+    assert L.gdn_ab_project(None, 16, 16, 4, 2560, 48, 16, 16, None) == GDN_ERR_ARG
+    assert b"x is null" in L.gdn_last_error()
+    assert L.gdn_ab_project(16, 12, 16, 4, 2560, 48, 16, 16, None) == GDN_ERR_ARG
+    assert b"w_alpha" in L.gdn_last_error()
+    assert L.gdn_ab_project(16, 16, 16, 4, 2560, 48, 1 << 20, 1 << 20, None) == GDN_ERR_ARG
+    assert b"overlaps" in L.gdn_last_error()
+    assert L.gdn_ab_project(None, None, None, 0, 2560, 48, None, None, None) == GDN_OK

@@ -463,3 +463,48 @@ def test_verify_window_then_commit(T):
         G.gdn_decode_step_norm(gm.pool, hh, a_, b_, gm.dt, gm.ssm_a, z_, gm.norm_w, wl.eps, yy, None, gm.slots)
         gm.next_y = yy
     assert torch.equal(win.next_y, kept.next_y)
+
+
+# ------------------------------------------------------------------ alpha / beta projections
+@pytest.mark.parametrize("B,T,n_embd,h_v", [(1, 1, 2560, 48), (3, 1, 2560, 48), (256, 1, 2560, 48),
+                                            (16, 512, 2560, 48), (5, 2, 260, 6), (2, 3, 4, 3)])
+def test_ab_projection(B, T, n_embd, h_v):
+    """alpha / beta logits from bf16 weights and fp32 activations vs the oracle; rows not a
+    multiple of the 4-row block, a partial 8-column group and an n_embd tail included."""
+    import torch
+    import gated_deltanet_mixer_gdn_amd as G
+    ab = W.make_ab(B, T, seed=80 + B + T, n_embd=n_embd, h_v=h_v)
+    log(f"ab projection B={B} T={T} n_embd={n_embd} h_v={h_v}")
+    x = dev(ab.x)
+    wa = torch.from_numpy(ab.w_alpha.view(np.int16)).cuda()
+    wb = torch.from_numpy(ab.w_beta.view(np.int16)).cuda()
+    alpha = torch.full((B, T, h_v), 7.0, device="cuda")
+    beta = torch.full((B, T, h_v), 7.0, device="cuda")
+    G.gdn_ab_project(x, wa, wb, alpha, beta)
+    ra, rb = oracle.ab_project(ab.x, ab.w_alpha, ab.w_beta)
+    assert_close("alpha", alpha.cpu().numpy(), ra, STEP_TOL)
+    assert_close("beta_logit", beta.cpu().numpy(), rb, STEP_TOL)
+
+
+def test_ab_projection_feeds_the_recurrence():
+    """Projection -> gdn_decode_step_norm equals the oracle's projection -> mixer."""
+    import torch
+    import gated_deltanet_mixer_gdn_amd as G
+    wl = W.make("proj", 4, 3, seed=85, state_std=0.02, conv_std=1.0)
+    ab = W.make_ab(4, 3, seed=86)
+    ra, rb = oracle.ab_project(ab.x, ab.w_alpha, ab.w_beta)
+    wl.alpha, wl.beta_logit = ra.astype(np.float32), rb.astype(np.float32)
+    gm = GpuMixer(wl)
+    G.gdn_ab_project(dev(ab.x), torch.from_numpy(ab.w_alpha.view(np.int16)).cuda(),
+                     torch.from_numpy(ab.w_beta.view(np.int16)).cuda(), gm.alpha, gm.beta_logit)
+    gm.run(fused=True)
+    res = oracle.run_workload(wl)
+    _compare_all(gm, wl, res, 2 * STEP_TOL, "proj->mixer", keys=("y", "h"))
+
+
+def test_ab_projection_empty_is_a_no_op():
+    import torch
+    import gated_deltanet_mixer_gdn_amd as G
+    x = torch.empty(0, 2560, device="cuda")
+    w = torch.zeros(48, 2560, dtype=torch.int16, device="cuda")
+    G.gdn_ab_project(x, w, w, torch.empty(0, 48, device="cuda"), torch.empty(0, 48, device="cuda"))

@@ -16,6 +16,7 @@ import pytest
 from scipy.special import expit
 
 import oracle
+import gdn_workloads as W
 from gdn_workloads import Geom, make
 
 GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "hand_worked.json")))
@@ -370,3 +371,36 @@ def test_oracle_rejects_bad_geometry():
     with pytest.raises(ValueError):
         oracle.delta_rule(Geom(h_k=2, h_v=5, s=4), np.zeros((1, 2 * 2 * 4 + 5 * 4)), np.zeros((1, 5)),
                           np.zeros((1, 5)), np.zeros((5, 4, 4)))
+
+
+# ---------------------------------------------------------------- alpha / beta projections
+def test_bf16_values_of_known_bit_patterns():
+    # sign | 8 exponent bits | 7 mantissa bits, bias 127 (the upper half of a binary32)
+    assert oracle.bf16_value(0x3F80) == 1.0
+    assert oracle.bf16_value(0xC040) == -3.0
+    assert oracle.bf16_value(0x4049) == 3.140625
+    assert oracle.bf16_value(0x3E80) == 0.25
+    assert oracle.bf16_value(0x0000) == 0.0
+    assert math.copysign(1.0, oracle.bf16_value(0x8000)) == -1.0
+    assert oracle.bf16_value(0x7F80) == math.inf
+    assert oracle.bf16_value(0x0001) == 2.0 ** -133          # smallest subnormal
+    assert oracle.bf16_value(0x7F7F) == (2 - 2 ** -7) * 2.0 ** 127
+
+
+def test_ab_project_hand_worked():
+    # alpha = 0.5 * 1 + (-1) * 2 = -1.5 ;  beta = 0.25 * 1 + 3 * 2 = 6.25
+    x = np.array([[1.0, 2.0]])
+    wa = np.array([[0x3F00, 0xBF80]], np.uint16)     # 0.5, -1
+    wb = np.array([[0x3E80, 0x4040]], np.uint16)     # 0.25, 3
+    a, b = oracle.ab_project(x, wa, wb)
+    assert a[0, 0] == -1.5 and b[0, 0] == 6.25
+
+
+def test_ab_project_matches_numpy_matmul():
+    wl = W.make_ab(3, 2, seed=31, n_embd=256, h_v=6)
+    a, b = oracle.ab_project(wl.x, wl.w_alpha, wl.w_beta)
+    dec = lambda bits: (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    np.testing.assert_allclose(a, wl.x.astype(np.float64) @ dec(wl.w_alpha).T, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(b, wl.x.astype(np.float64) @ dec(wl.w_beta).T, rtol=1e-12, atol=1e-12)
+    a2, _ = oracle.ab_project(2.0 * wl.x, wl.w_alpha, wl.w_beta)
+    np.testing.assert_array_equal(a2, 2.0 * a)
