@@ -193,3 +193,16 @@ def make_ab(B: int, T: int, seed: int, n_embd: int = N_EMBD, h_v: int = H_V) -> 
     w_beta = bf16_bits(_normal(rng, (h_v, n_embd), std))
     x = _normal(rng, (B, T, n_embd))
     return AbWorkload(x, w_alpha, w_beta)
+
+
+# ------------------------------------------------------------------ the qkv / z / out projections
+# (rows, k, n) of the three projections around the mixer at the pages' sizes
+PROJECTIONS = {"qkv": (N_EMBD, 2 * H_K * S + H_V * S), "z": (N_EMBD, H_V * S), "out": (H_V * S, N_EMBD)}
+
+
+def make_proj(rows: int, k: int, n: int, seed: int):
+    """x [rows][k] ~ N(0, 1); w [n][k] ~ N(0, 1/sqrt(k)) rounded to bf16 bits."""
+    rng = np.random.default_rng(seed)
+    w = bf16_bits(_normal(rng, (n, k), 1.0 / np.sqrt(k)))
+    x = _normal(rng, (rows, k))
+    return x, w

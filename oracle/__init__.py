@@ -59,6 +59,8 @@ def lib():
         L.gdn_oracle_bf16_value.restype = d
         L.gdn_oracle_ab_project.argtypes = [i64, i, i, _D, U16, U16, _D, _D]
         L.gdn_oracle_ab_project.restype = i
+        L.gdn_oracle_project.argtypes = [i64, i, i, _D, U16, _D]
+        L.gdn_oracle_project.restype = i
         for f in ("conv_silu_norm", "beta_gate", "delta_rule", "gated_rmsnorm", "mixer"):
             getattr(L, "gdn_oracle_" + f).restype = i
         _lib = L
@@ -168,6 +170,31 @@ def ab_project(x, w_alpha_bits, w_beta_bits):
     _check(lib().gdn_oracle_ab_project(x2.shape[0], n_embd, h_v, _p(x2), wa.ctypes.data_as(U16),
                                        wb.ctypes.data_as(U16), _p(alpha), _p(beta)), "ab_project")
     return alpha.reshape(*shape, h_v), beta.reshape(*shape, h_v)
+
+
+def project(x, w_bits, threads: Optional[int] = None):
+    """x [..][k]; w [n][k] uint16 bf16 bits -> out [..][n] (rows split over threads)."""
+    x = _f64(x)
+    shape = x.shape[:-1]
+    k = x.shape[-1]
+    x2 = x.reshape(-1, k)
+    w = np.ascontiguousarray(w_bits, dtype=np.uint16)
+    n = w.shape[0]
+    out = np.zeros((x2.shape[0], n))
+    U16 = ctypes.POINTER(ctypes.c_uint16)
+    rows = x2.shape[0]
+    threads = max(1, min(threads or (os.cpu_count() or 1), rows))
+    bounds = np.linspace(0, rows, threads + 1).astype(int)
+
+    def part(i):
+        a, b = bounds[i], bounds[i + 1]
+        if b > a:
+            xs, os_ = x2[a:b], out[a:b]
+            _check(lib().gdn_oracle_project(b - a, k, n, _p(xs), w.ctypes.data_as(U16), _p(os_)), "project")
+    lib()
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        list(ex.map(part, range(threads)))
+    return out.reshape(*shape, n)
 
 
 def run_sequence(wl, b: int, t0: int = 0, t1: Optional[int] = None, state=None, conv_state=None):

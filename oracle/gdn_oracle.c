@@ -273,3 +273,20 @@ int gdn_oracle_ab_project(int64_t rows, int n_embd, int h_v, const double* x, co
     }
     return GDN_ORACLE_OK;
 }
+
+/*
+ * The projections either side of the mixer (steps 2, 7 and 8 of gdn_layer: qkv =
+ * wqkv @ x, z = attn_gate @ x, out = ssm_out @ y), with bf16 weights:
+ *   out[r][j] = sum_e w[j][e] * x[r][e]
+ *   x [rows][k];  w [n][k] (uint16 bf16 bits);  out [rows][n]
+ */
+int gdn_oracle_project(int64_t rows, int k, int n, const double* x, const uint16_t* w, double* out) {
+    if (rows < 0 || k <= 0 || n <= 0 || !x || !w || !out) return GDN_ORACLE_BAD_ARG;
+    for (int64_t r = 0; r < rows; ++r)
+        for (int j = 0; j < n; ++j) {
+            double acc = 0.0;
+            for (int e = 0; e < k; ++e) acc += gdn_oracle_bf16_value(w[(int64_t) j * k + e]) * x[r * k + e];
+            out[r * n + j] = acc;
+        }
+    return GDN_ORACLE_OK;
+}

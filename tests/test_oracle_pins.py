@@ -404,3 +404,12 @@ def test_ab_project_matches_numpy_matmul():
     np.testing.assert_allclose(b, wl.x.astype(np.float64) @ dec(wl.w_beta).T, rtol=1e-12, atol=1e-12)
     a2, _ = oracle.ab_project(2.0 * wl.x, wl.w_alpha, wl.w_beta)
     np.testing.assert_array_equal(a2, 2.0 * a)
+
+
+def test_project_matches_numpy_and_hand_example():
+    x = np.array([[1.0, 2.0, -1.0]])
+    w = np.array([[0x3F00, 0xBF80, 0x4000], [0x0000, 0x3F80, 0x3F80]], np.uint16)   # [0.5,-1,2], [0,1,1]
+    np.testing.assert_array_equal(oracle.project(x, w), [[0.5 - 2.0 - 2.0, 2.0 - 1.0]])
+    xr, wr = W.make_proj(7, 64, 40, seed=33)
+    dec = (wr.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    np.testing.assert_allclose(oracle.project(xr, wr, threads=3), xr.astype(np.float64) @ dec.T, rtol=1e-12, atol=1e-12)
