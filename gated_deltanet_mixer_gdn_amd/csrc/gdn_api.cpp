@@ -16,6 +16,7 @@
 #include "gdn.h"
 #include "gdn_kernels.h"
 #include "gdn_proj.h"
+#include "gdn_gemm.h"
 
 struct gdn_pool {
     gdn_geom g;
@@ -451,6 +452,78 @@ int gdn_ab_project(const float* x, const uint16_t* w_alpha, const uint16_t* w_be
     a.n_embd = n_embd;
     a.h_v = h_v;
     return launched(gdn::launch_ab_project(a, static_cast<hipStream_t>(stream)), fn);
+}
+
+int64_t gdn_split_bf16_bytes(int64_t rows, int32_t k) {
+    if (rows < 0 || k <= 0 || k % 8 != 0 || rows > (INT64_MAX / 8) / gdn::pad_up(k, gdn::kTileK)) return -1;
+    return gdn::pad_up(rows, gdn::kTileRows) * gdn::pad_up(k, gdn::kTileK) * 4;
+}
+
+int64_t gdn_pack_bf16_bytes(int32_t n, int32_t k) {
+    if (n <= 0 || k <= 0 || k % 8 != 0) return -1;
+    return gdn::pad_up(n, gdn::kTileRows) * gdn::pad_up(k, gdn::kTileK) * 2;
+}
+
+int gdn_split_bf16(const float* x, int64_t rows, int32_t k, uint16_t* xs, void* stream) {
+    const char* fn = "gdn_split_bf16";
+    if (rows < 0) return fail(GDN_ERR_ARG, fn, "rows=%lld is negative", (long long) rows);
+    if (k <= 0 || k % 8 != 0) return fail(GDN_ERR_ARG, fn, "k=%d must be a positive multiple of 8", k);
+    if (rows == 0) return ok();
+    const int64_t xs_bytes = gdn_split_bf16_bytes(rows, k);
+    if (xs_bytes < 0) return fail(GDN_ERR_ARG, fn, "rows too large");
+    if (int rc = check_f4(x, fn, "x")) return rc;
+    if (int rc = check_f4(xs, fn, "xs")) return rc;
+    if (overlap(xs, (size_t) xs_bytes, x, (size_t) rows * k * sizeof(float)))
+        return fail(GDN_ERR_ARG, fn, "xs overlaps x");
+    gdn::SplitParams sp;
+    sp.x = x;
+    sp.xs = xs;
+    sp.rows = (long long) rows;
+    sp.k = k;
+    return launched(gdn::launch_split_bf16(sp, static_cast<hipStream_t>(stream)), fn);
+}
+
+int gdn_pack_bf16(const uint16_t* w, int32_t n, int32_t k, uint16_t* wp, void* stream) {
+    const char* fn = "gdn_pack_bf16";
+    if (n <= 0) return fail(GDN_ERR_ARG, fn, "n=%d must be positive", n);
+    if (k <= 0 || k % 8 != 0) return fail(GDN_ERR_ARG, fn, "k=%d must be a positive multiple of 8", k);
+    if (int rc = check_f4(w, fn, "w")) return rc;
+    if (int rc = check_f4(wp, fn, "wp")) return rc;
+    if (overlap(wp, (size_t) gdn_pack_bf16_bytes(n, k), w, (size_t) n * k * 2))
+        return fail(GDN_ERR_ARG, fn, "wp overlaps w");
+    gdn::PackParams pp;
+    pp.w = w;
+    pp.wp = wp;
+    pp.n = n;
+    pp.k = k;
+    return launched(gdn::launch_pack_bf16(pp, static_cast<hipStream_t>(stream)), fn);
+}
+
+int gdn_project_bf16(const uint16_t* xs, const uint16_t* wp, int64_t rows, int32_t k, int32_t n, float* out,
+                     void* stream) {
+    const char* fn = "gdn_project_bf16";
+    if (rows < 0) return fail(GDN_ERR_ARG, fn, "rows=%lld is negative", (long long) rows);
+    if (k <= 0 || k % 8 != 0) return fail(GDN_ERR_ARG, fn, "k=%d must be a positive multiple of 8", k);
+    if (n <= 0) return fail(GDN_ERR_ARG, fn, "n=%d must be positive", n);
+    if (rows == 0) return ok();
+    const int64_t xs_bytes = gdn_split_bf16_bytes(rows, k);
+    if (xs_bytes < 0 || rows > INT64_MAX / 4 / n) return fail(GDN_ERR_ARG, fn, "rows too large");
+    if (int rc = check_f4(xs, fn, "xs")) return rc;
+    if (int rc = check_f4(wp, fn, "wp")) return rc;
+    if (int rc = check_f1(out, fn, "out")) return rc;
+    const size_t out_bytes = (size_t) rows * n * sizeof(float);
+    if (overlap(out, out_bytes, xs, (size_t) xs_bytes)) return fail(GDN_ERR_ARG, fn, "out overlaps xs");
+    if (overlap(out, out_bytes, wp, (size_t) gdn_pack_bf16_bytes(n, k))) return fail(GDN_ERR_ARG, fn, "out overlaps wp");
+    gdn::GemmParams gp;
+    gp.xs = xs;
+    gp.wp = wp;
+    gp.out = out;
+    gp.rows = (long long) rows;
+    gp.k = k;
+    gp.n = n;
+    const gdn::GemmConfig cfg = gdn::choose_gemm_config(gp.rows, k, n);
+    if (gdn::gemm_workgroups(gp, cfg) > INT32_MAX) return fail(GDN_ERR_ARG, fn, "rows x n too large");
+    return launched(gdn::launch_project_bf16(gp, cfg, static_cast<hipStream_t>(stream)), fn);
 }
 
 int gdn_gated_rmsnorm(const float* o, const float* z, const float* w, float eps, int64_t rows, int32_t s,

@@ -1,0 +1,322 @@
+// gdn_gemm.hip - the dense projections either side of the mixer: qkv = wqkv x and
+// z = attn_gate x before it, out = ssm_out y after it (steps 2, 7 and 8 of
+// `gdn_layer` on the "src/core/layer.cpp" page), as plain products with bf16
+// weights:
+//
+//   out[r][j] = sum_e w[j][e] * x[r][e]     x [rows][k] fp32, w [n][k] bf16
+//
+// At a decode batch this is the one dense contraction around the mixer (rows =
+// sequences, k and n in the thousands), so it runs on the matrix cores with
+// v_mfma_f32_32x32x16_bf16.  The activations are not rounded to bf16: a first
+// pass splits each fp32 value into hi = bf16(x) and lo = bf16(x - hi), and every
+// weight tile meets both halves, so the product carries x to within 2^-16 |x|
+// and sums in fp32.  The split runs once per activation matrix and serves every
+// projection that reads it (qkv and z read the same x), the way the pages'
+// engine converts an activation once for the GEMVs that follow.
+#include <hip/hip_runtime.h>
+
+#include "gdn_gemm.h"
+
+namespace gdn {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f16v __attribute__((ext_vector_type(16)));
+typedef float f4v __attribute__((ext_vector_type(4)));
+typedef unsigned u4v __attribute__((ext_vector_type(4)));
+
+// fp32 -> bf16 bits, round to nearest even.  NaN stays a quiet NaN; a finite value
+// that would round up to infinity is truncated instead (stays finite).
+__device__ __forceinline__ unsigned bf16_rne(float x) {
+    const unsigned u = __float_as_uint(x);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+    const unsigned r = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+    const bool finite = (u & 0x7f800000u) != 0x7f800000u;
+    return (finite && (r & 0x7f80u) == 0x7f80u) ? (u >> 16) : r;
+}
+
+// ------------------------------------------------------------------ split and pack
+// One thread per fragment position (tile, step, lane) of the output layout, so the
+// writes of a wave are contiguous; positions outside [rows] x [k] are written as zeros.
+__global__ __launch_bounds__(256) void split_bf16_kernel(SplitParams p) {
+    const int n_chunks = (int) (pad_up(p.k, kTileK) / kTileK);
+    const long long total = pad_up(p.rows, kTileRows) / kTileRows * n_chunks * 256;
+    const long long stride = (long long) gridDim.x * blockDim.x;
+    for (long long f = (long long) blockIdx.x * blockDim.x + threadIdx.x; f < total; f += stride) {
+        const long long tile = f >> 8;
+        const int s = (int) (f >> 6) & 3, lane = (int) f & 63;
+        const long long row = tile / n_chunks * kTileRows + (lane & 31);
+        const int kk = (int) (tile % n_chunks) * kTileK + 32 * (lane >> 5) + 8 * s;
+        u4v H = {0u, 0u, 0u, 0u}, L = H;
+        if (row < p.rows && kk < p.k) {
+            const float* src = p.x + row * p.k + kk;
+            const f4v a = *(const f4v*) src;
+            const f4v b = *(const f4v*) (src + 4);
+            const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+            unsigned hi[8], lo[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                hi[j] = bf16_rne(v[j]);
+                // x - hi is exact in fp32; an infinite or NaN hi carries the whole value
+                lo[j] = (hi[j] & 0x7f80u) == 0x7f80u ? 0u : bf16_rne(v[j] - __uint_as_float(hi[j] << 16));
+            }
+            H = u4v{hi[0] | hi[1] << 16, hi[2] | hi[3] << 16, hi[4] | hi[5] << 16, hi[6] | hi[7] << 16};
+            L = u4v{lo[0] | lo[1] << 16, lo[2] | lo[3] << 16, lo[4] | lo[5] << 16, lo[6] | lo[7] << 16};
+        }
+        u4v* dst = (u4v*) p.xs + tile * 512 + lane;
+        dst[(2 * s) * 64] = H;
+        dst[(2 * s + 1) * 64] = L;
+    }
+}
+
+__global__ __launch_bounds__(256) void pack_bf16_kernel(PackParams p) {
+    const int n_chunks = (int) (pad_up(p.k, kTileK) / kTileK);
+    const long long total = pad_up(p.n, kTileRows) / kTileRows * n_chunks * 256;
+    const long long stride = (long long) gridDim.x * blockDim.x;
+    for (long long f = (long long) blockIdx.x * blockDim.x + threadIdx.x; f < total; f += stride) {
+        const long long tile = f >> 8;
+        const int lane = (int) f & 63;
+        const long long col = tile / n_chunks * kTileRows + (lane & 31);
+        const int kk = (int) (tile % n_chunks) * kTileK + 32 * (lane >> 5) + 8 * ((int) (f >> 6) & 3);
+        u4v v = {0u, 0u, 0u, 0u};
+        if (col < p.n && kk < p.k) v = *(const u4v*) (p.w + col * p.k + kk);
+        ((u4v*) p.wp)[f] = v;
+    }
+}
+
+// ------------------------------------------------------------------ projection
+//
+// Workgroup = 4 waves; wave (wn, wk) computes the (32 WM) x (32 WN) block of out at
+// rows m0.., columns n0 + wn*32*WN.., over the k chunks c = wk, wk + KW, ... of the
+// tiled operands.  Per chunk a lane loads, for each of its WM row tiles, the hi and
+// lo fragment of each of the 4 steps and, for each of its WN column tiles, the
+// weight fragment of each step: every load instruction reads 1 KiB of contiguous
+// memory.  Accumulator element e of lane (i, h) holds out row 8(e/4) + 4h + e%4,
+// column i of the block.  The next chunk is loaded while the current one runs
+// (two register sets, loads issued unconditionally so the waits count exactly).
+// Waves that split k add their partial blocks through LDS in a fixed order
+// (wk = 0, 1, ...), so results do not depend on timing.  Row and column tiles past
+// the padded operands are clamped to the last one; their outputs are not stored.
+template <int WM, int WN>
+struct Frag {
+    bf16x8 a[WM][4][2];  // [row tile][step][hi, lo]
+    bf16x8 b[WN][4];     // [column tile][step]
+};
+
+template <int WM, int WN, int KW>
+__global__ __launch_bounds__(256) void project_bf16_kernel(GemmParams p, int tiles_m, int tiles_total, int n_chunks) {
+    constexpr int kWavesN = 4 / KW;
+    constexpr int BM = 32 * WM;
+    constexpr int BN = 32 * WN * kWavesN;
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int i = lane & 31;
+    const int h = lane >> 5;
+    const int wn = wave % kWavesN;
+    const int wk = wave / kWavesN;
+
+    // Workgroups are dispatched to the 8 XCDs round robin; give each XCD a
+    // contiguous run of tiles, in which the row blocks of one column tile are
+    // neighbours and share their weight tiles in that XCD's L2.
+    const int b = blockIdx.x;
+    const int per = tiles_total >> 3, extra = tiles_total & 7, xcd = b & 7;
+    const int t = xcd * per + min(xcd, extra) + (b >> 3);
+    const int tm = t % tiles_m;
+    const int tn = t / tiles_m;
+    const long long m0 = (long long) tm * BM;
+    const int n0 = tn * BN + wn * 32 * WN;
+    const long long last_rt = (p.rows + kTileRows - 1) / kTileRows - 1;
+    const int last_ct = (p.n + kTileRows - 1) / kTileRows - 1;
+
+    const bf16x8* abase[WM];
+#pragma unroll
+    for (int r = 0; r < WM; ++r) {
+        const long long rt = min((long long) tm * WM + r, last_rt);
+        abase[r] = (const bf16x8*) p.xs + rt * n_chunks * 512 + lane;
+    }
+    const bf16x8* bbase[WN];
+#pragma unroll
+    for (int c = 0; c < WN; ++c) {
+        const long long ct = min(n0 / 32 + c, last_ct);
+        bbase[c] = (const bf16x8*) p.wp + ct * n_chunks * 256 + lane;
+    }
+
+    auto load = [&](int ch, Frag<WM, WN>& f) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+#pragma unroll
+            for (int r = 0; r < WM; ++r) {
+                f.a[r][s][0] = abase[r][ch * 512 + (2 * s) * 64];
+                f.a[r][s][1] = abase[r][ch * 512 + (2 * s + 1) * 64];
+            }
+#pragma unroll
+            for (int c = 0; c < WN; ++c) f.b[c][s] = bbase[c][ch * 256 + s * 64];
+        }
+    };
+
+    f16v acc[WM][WN];
+#pragma unroll
+    for (int r = 0; r < WM; ++r)
+#pragma unroll
+        for (int c = 0; c < WN; ++c) acc[r][c] = f16v{};
+    auto compute = [&](const Frag<WM, WN>& f) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int r = 0; r < WM; ++r)
+#pragma unroll
+                for (int c = 0; c < WN; ++c) {
+                    acc[r][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[r][s][0], f.b[c][s], acc[r][c], 0, 0, 0);
+                    acc[r][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[r][s][1], f.b[c][s], acc[r][c], 0, 0, 0);
+                }
+    };
+
+    // Two chunks per trip: f0 holds chunk it on entry, f1 is loaded while f0 runs and
+    // f0 reloaded while f1 runs.  The scheduling barriers keep the compiler from
+    // sinking the loads of the next chunk down to their first use.
+    const int cnt = wk < n_chunks ? (n_chunks - wk + KW - 1) / KW : 0;
+    if (cnt > 0) {
+        Frag<WM, WN> f0, f1;
+        load(wk, f0);
+        int it = 0;
+        for (; it + 2 <= cnt; it += 2) {
+            load(wk + KW * (it + 1), f1);
+            __builtin_amdgcn_sched_barrier(0);
+            compute(f0);
+            __builtin_amdgcn_sched_barrier(0);
+            load(wk + KW * min(it + 2, cnt - 1), f0);
+            __builtin_amdgcn_sched_barrier(0);
+            compute(f1);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (it < cnt) compute(f0);
+    }
+
+    if constexpr (KW > 1) {
+        constexpr int kVals = WM * WN * 16;
+        __shared__ float red[(KW - 1) * kWavesN * kVals * 64];
+        if (wk > 0) {
+            float* dst = red + ((wk - 1) * kWavesN + wn) * kVals * 64 + lane;
+#pragma unroll
+            for (int r = 0; r < WM; ++r)
+#pragma unroll
+                for (int c = 0; c < WN; ++c)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) dst[((r * WN + c) * 16 + e) * 64] = acc[r][c][e];
+        }
+        __syncthreads();
+        if (wk > 0) return;
+#pragma unroll
+        for (int j = 1; j < KW; ++j) {
+            const float* src = red + ((j - 1) * kWavesN + wn) * kVals * 64 + lane;
+#pragma unroll
+            for (int r = 0; r < WM; ++r)
+#pragma unroll
+                for (int c = 0; c < WN; ++c)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) acc[r][c][e] += src[((r * WN + c) * 16 + e) * 64];
+        }
+    }
+
+#pragma unroll
+    for (int r = 0; r < WM; ++r)
+#pragma unroll
+        for (int c = 0; c < WN; ++c) {
+            const int col = n0 + 32 * c + i;
+            if (col >= p.n) continue;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const long long row = m0 + 32 * r + 8 * (e >> 2) + 4 * h + (e & 3);
+                if (row < p.rows) p.out[row * p.n + col] = acc[r][c][e];
+            }
+        }
+}
+
+// the instantiated tile shapes: {wm, wn, kw}
+constexpr GemmConfig kConfigs[] = {
+    {1, 1, 4}, {1, 2, 4}, {1, 2, 2}, {1, 2, 1}, {2, 1, 4}, {2, 2, 4}, {2, 2, 2}, {2, 2, 1}, {2, 4, 2}, {2, 4, 1},
+};
+
+template <int WM, int WN, int KW>
+hipError_t launch_tile(const GemmParams& p, hipStream_t stream) {
+    constexpr int BM = 32 * WM, BN = 32 * WN * (4 / KW);
+    const long long tm = (p.rows + BM - 1) / BM, tn = ((long long) p.n + BN - 1) / BN;
+    hipLaunchKernelGGL((project_bf16_kernel<WM, WN, KW>), dim3((unsigned) (tm * tn)), dim3(256), 0, stream, p,
+                       (int) tm, (int) (tm * tn), (int) (pad_up(p.k, kTileK) / kTileK));
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool gemm_config_supported(const GemmConfig& c) {
+    for (const GemmConfig& k : kConfigs)
+        if (k.wm == c.wm && k.wn == c.wn && k.kw == c.kw) return true;
+    return false;
+}
+
+long long gemm_workgroups(const GemmParams& p, const GemmConfig& c) {
+    const long long bm = 32LL * c.wm, bn = 32LL * c.wn * (4 / c.kw);
+    return (p.rows + bm - 1) / bm * (((long long) p.n + bn - 1) / bn);
+}
+
+// Fewest rows per tile that cover the batch, then the widest tile that still
+// gives every compute unit a workgroup; when none does, the tile with the most
+// workgroups.
+GemmConfig choose_gemm_config(long long rows, int k, int n) {
+    (void) k;
+    const int wm = rows <= 32 ? 1 : 2;
+    GemmParams p{};
+    p.rows = rows;
+    p.n = n;
+    GemmConfig best{0, 0, 0};
+    long long best_wg = -1;
+    for (const GemmConfig& c : kConfigs) {
+        if (c.wm != wm) continue;
+        const long long wg = gemm_workgroups(p, c);
+        const long long cols = 32LL * c.wn * (4 / c.kw);
+        const long long best_cols = 32LL * best.wn * (best.kw ? 4 / best.kw : 0);
+        if (wg >= 256) {
+            if (best_wg < 256 || cols > best_cols || (cols == best_cols && c.kw < best.kw)) {
+                best = c;
+                best_wg = wg;
+            }
+        } else if (best_wg < 256 && wg > best_wg) {
+            best = c;
+            best_wg = wg;
+        }
+    }
+    return best;
+}
+
+hipError_t launch_split_bf16(const SplitParams& p, hipStream_t stream) {
+    const long long frags = pad_up(p.rows, kTileRows) * pad_up(p.k, kTileK) / 8;
+    const long long blocks = std::min<long long>((frags + 255) / 256, 1LL << 16);
+    hipLaunchKernelGGL(split_bf16_kernel, dim3((unsigned) blocks), dim3(256), 0, stream, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_pack_bf16(const PackParams& p, hipStream_t stream) {
+    const long long frags = pad_up(p.n, kTileRows) * pad_up(p.k, kTileK) / 8;
+    const long long blocks = std::min<long long>((frags + 255) / 256, 1LL << 16);
+    hipLaunchKernelGGL(pack_bf16_kernel, dim3((unsigned) blocks), dim3(256), 0, stream, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_project_bf16(const GemmParams& p, const GemmConfig& c, hipStream_t stream) {
+#define GDN_TILE(A, B, C) \
+    if (c.wm == A && c.wn == B && c.kw == C) return launch_tile<A, B, C>(p, stream);
+    GDN_TILE(1, 1, 4)
+    GDN_TILE(1, 2, 4)
+    GDN_TILE(1, 2, 2)
+    GDN_TILE(1, 2, 1)
+    GDN_TILE(2, 1, 4)
+    GDN_TILE(2, 2, 4)
+    GDN_TILE(2, 2, 2)
+    GDN_TILE(2, 2, 1)
+    GDN_TILE(2, 4, 2)
+    GDN_TILE(2, 4, 1)
+#undef GDN_TILE
+    return hipErrorInvalidValue;
+}
+
+}  // namespace gdn

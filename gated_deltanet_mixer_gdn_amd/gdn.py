@@ -22,7 +22,8 @@ EXPORTS = (
     "gdn_state_pool_destroy", "gdn_state_pool_state", "gdn_state_pool_conv", "gdn_state_pool_flags",
     "gdn_state_pool_slots", "gdn_state_pool_zero", "gdn_conv_silu_norm", "gdn_decode_step",
     "gdn_decode_step_norm", "gdn_decode_fused", "gdn_verify_window", "gdn_commit", "gdn_gated_rmsnorm",
-    "gdn_ab_project",
+    "gdn_ab_project", "gdn_split_bf16_bytes", "gdn_pack_bf16_bytes", "gdn_split_bf16", "gdn_pack_bf16",
+    "gdn_project_bf16",
 )
 
 
@@ -89,6 +90,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "gdn_commit": ([vp, vp, vp, i32, i32, vp, vp, vp, vp, vp, vp, vp], ctypes.c_int),
         "gdn_gated_rmsnorm": ([vp, vp, vp, f32, i64, i32, vp, vp], ctypes.c_int),
         "gdn_ab_project": ([vp, vp, vp, i64, i32, i32, vp, vp, vp], ctypes.c_int),
+        "gdn_split_bf16_bytes": ([i64, i32], ctypes.c_int64),
+        "gdn_pack_bf16_bytes": ([i32, i32], ctypes.c_int64),
+        "gdn_split_bf16": ([vp, i64, i32, vp, vp], ctypes.c_int),
+        "gdn_pack_bf16": ([vp, i32, i32, vp, vp], ctypes.c_int),
+        "gdn_project_bf16": ([vp, vp, i64, i32, i32, vp, vp], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -308,3 +314,73 @@ def gdn_ab_project(x, w_alpha, w_beta, alpha, beta_logit):
             raise ValueError(f"{name} must hold {rows * h_v} elements")
     _check(load_library().gdn_ab_project(_f32(x, "x"), w_alpha.data_ptr(), w_beta.data_ptr(), rows, n_embd, h_v,
                                          _f32(alpha, "alpha"), _f32(beta_logit, "beta_logit"), _stream(x)))
+
+
+def _bits16(t, name: str, shape):
+    import torch
+    if not isinstance(t, torch.Tensor) or t.dtype not in (torch.int16, torch.uint16, torch.bfloat16) \
+            or not t.is_cuda or not t.is_contiguous() or tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must be a contiguous 16-bit CUDA tensor of shape {tuple(shape)}")
+    return t.data_ptr()
+
+
+class SplitX:
+    """Split fp32 activations [rows][k] in the library's tiled layout (gdn_split_bf16)."""
+
+    def __init__(self, data, rows: int, k: int):
+        self.data, self.rows, self.k = data, rows, k
+
+
+class PackedW:
+    """A bf16 weight matrix [n][k] rearranged by gdn_pack_bf16."""
+
+    def __init__(self, data, n: int, k: int):
+        self.data, self.n, self.k = data, n, k
+
+
+def gdn_split_bf16(x, xs: Optional[SplitX] = None) -> SplitX:
+    """x [.., k] fp32 -> its bf16 (hi, lo) split in the tiled layout."""
+    import torch
+    k = x.shape[-1]
+    rows = x.numel() // k if k else 0
+    nbytes = load_library().gdn_split_bf16_bytes(rows, k)
+    if nbytes < 0:
+        raise ValueError(f"cannot split [{rows}][{k}]: k must be a positive multiple of 8")
+    if xs is None:
+        xs = SplitX(torch.empty(nbytes // 2, dtype=torch.int16, device=x.device), rows, k)
+    elif (xs.rows, xs.k) != (rows, k) or xs.data.numel() * 2 < nbytes:
+        raise ValueError("xs was made for another shape")
+    _check(load_library().gdn_split_bf16(_f32(x, "x"), rows, k, xs.data.data_ptr(), _stream(x)))
+    return xs
+
+
+def gdn_pack_bf16(w) -> PackedW:
+    """w [n][k] bf16 bits (int16 / uint16 / bfloat16 tensor) -> packed weights."""
+    import torch
+    n, k = w.shape
+    nbytes = load_library().gdn_pack_bf16_bytes(n, k)
+    if nbytes < 0:
+        raise ValueError(f"cannot pack [{n}][{k}]: k must be a positive multiple of 8")
+    wp = torch.empty(nbytes // 2, dtype=torch.int16, device=w.device)
+    _check(load_library().gdn_pack_bf16(_bits16(w, "w", (n, k)), n, k, wp.data_ptr(), _stream(w)))
+    return PackedW(wp, n, k)
+
+
+def gdn_project_bf16(xs: SplitX, wp: PackedW, out=None):
+    """out [rows][n] fp32 = x @ w^T from the split activations and the packed weights."""
+    import torch
+    if xs.k != wp.k:
+        raise ValueError(f"x has k={xs.k}, w has k={wp.k}")
+    if out is None:
+        out = torch.empty(xs.rows, wp.n, dtype=torch.float32, device=xs.data.device)
+    if out.numel() != xs.rows * wp.n:
+        raise ValueError(f"out must hold {xs.rows * wp.n} elements")
+    _check(load_library().gdn_project_bf16(xs.data.data_ptr(), wp.data.data_ptr(), xs.rows, xs.k, wp.n,
+                                           _f32(out, "out"), _stream(xs.data)))
+    return out
+
+
+def gdn_project(x, wp: PackedW, out=None):
+    """out [.., n] = x @ w^T for fp32 x [.., k] through a split and the product."""
+    res = gdn_project_bf16(gdn_split_bf16(x), wp, out)
+    return res.view(*x.shape[:-1], wp.n) if out is None else res

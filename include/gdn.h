@@ -222,6 +222,49 @@ int gdn_gated_rmsnorm(const float* o, const float* z, const float* w, float eps,
 int gdn_ab_project(const float* x, const uint16_t* w_alpha, const uint16_t* w_beta, int64_t rows,
                    int32_t n_embd, int32_t h_v, float* alpha, float* beta_logit, void* stream);
 
+/* ---------------------------------------------------------------- the dense projections
+ * qkv = wqkv x and z = attn_gate x before the mixer, out = ssm_out y after it (steps
+ * 2, 7 and 8 of gdn_layer), as products with bf16 weights and fp32 activations:
+ *   out[r][j] = sum_e w[j][e] * x[r][e]      x [rows][k], w [n][k]
+ * Both operands are handed to the matrix cores in a tiled layout of their own:
+ *   gdn_pack_bf16   rearranges a weight matrix once (when the weights are loaded);
+ *   gdn_split_bf16  writes each fp32 activation as two bf16 values hi = bf16(x),
+ *                   lo = bf16(x - hi) (round to nearest even; hi + lo equals x to
+ *                   within 2^-16 |x| while lo is a normal number), in the same tiling;
+ *                   one split serves every projection of the same activations (qkv
+ *                   and z share theirs);
+ *   gdn_project_bf16 multiplies them, summing in fp32.
+ * The tile is 32 rows x 64 k: rows are padded to a multiple of 32 and k to a
+ * multiple of 64 with zeros.  For step s (0..3) of a tile and lane l = i + 32h
+ * (i < 32, h < 2), the 8 values of element [32R + i][64C + 32h + 8s + j], j = 0..7,
+ * form a 16-byte fragment.  Packed weights: tile (R, C) of R-major order holds the
+ * fragments (s, l) at index s*64 + l (4 KiB per tile).  Split activations: tile
+ * (R, C) holds the hi fragment (s, l) at index (2s)*64 + l and the lo fragment at
+ * (2s + 1)*64 + l (8 KiB per tile).  k must be a positive multiple of 8. */
+
+/* Bytes of the split activations for [rows][k]: ceil(rows/32)*32 * ceil(k/64)*64 * 4,
+ * or -1 for a negative rows or a k that is not a positive multiple of 8. */
+int64_t gdn_split_bf16_bytes(int64_t rows, int32_t k);
+
+/* Bytes of the packed weights for [n][k]: ceil(n/32)*32 * ceil(k/64)*64 * 2, or -1. */
+int64_t gdn_pack_bf16_bytes(int32_t n, int32_t k);
+
+/* x [rows][k] fp32, 16-byte aligned -> xs (gdn_split_bf16_bytes(rows, k) bytes,
+ * 16-byte aligned, not overlapping x).  rows = 0 is a no-op.  Non-finite x gives hi =
+ * the value, lo = 0. */
+int gdn_split_bf16(const float* x, int64_t rows, int32_t k, uint16_t* xs, void* stream);
+
+/* w [n][k] bf16 bit patterns, 16-byte aligned -> wp (gdn_pack_bf16_bytes(n, k)
+ * bytes, 16-byte aligned, not overlapping w).  n >= 1. */
+int gdn_pack_bf16(const uint16_t* w, int32_t n, int32_t k, uint16_t* wp, void* stream);
+
+/* xs from gdn_split_bf16 for [rows][k]; wp from gdn_pack_bf16 for [n][k]; out
+ * [rows][n] fp32, 4-byte aligned, overlapping neither input.  rows = 0 is a no-op.
+ * For one (rows, k, n) the result is the same on every call (a fixed summation
+ * order). */
+int gdn_project_bf16(const uint16_t* xs, const uint16_t* wp, int64_t rows, int32_t k, int32_t n, float* out,
+                     void* stream);
+
 #ifdef __cplusplus
 }
 #endif

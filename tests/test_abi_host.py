@@ -199,3 +199,34 @@ def test_ab_project_argument_errors(L):
     assert L.gdn_ab_project(16, 16, 16, 4, 2560, 48, 1 << 20, 1 << 20, None) == GDN_ERR_ARG
     assert b"overlaps" in L.gdn_last_error()
     assert L.gdn_ab_project(None, None, None, 0, 2560, 48, None, None, None) == GDN_OK
+
+
+def test_projection_argument_errors(L):
+    from gated_deltanet_mixer_gdn_amd.gdn import GDN_ERR_ARG, GDN_OK
+    assert L.gdn_split_bf16_bytes(70, 2560) == 96 * 2560 * 4
+    assert L.gdn_split_bf16_bytes(1, 8) == 32 * 64 * 4
+    assert L.gdn_split_bf16_bytes(-1, 64) == -1 and L.gdn_split_bf16_bytes(4, 12) == -1
+    assert L.gdn_pack_bf16_bytes(100, 136) == 128 * 192 * 2
+    assert L.gdn_pack_bf16_bytes(0, 64) == -1 and L.gdn_pack_bf16_bytes(4, 0) == -1
+    assert L.gdn_split_bf16(16, -1, 64, 16, None) == GDN_ERR_ARG
+    assert L.gdn_split_bf16(16, 4, 60, 16, None) == GDN_ERR_ARG
+    assert b"multiple of 8" in L.gdn_last_error()
+    assert L.gdn_split_bf16(None, 4, 64, 1 << 20, None) == GDN_ERR_ARG
+    assert L.gdn_split_bf16(1 << 20, 4, 64, (1 << 20) + 512, None) == GDN_ERR_ARG
+    assert b"xs overlaps x" in L.gdn_last_error()
+    assert L.gdn_split_bf16(16, 4, 64, 8, None) == GDN_ERR_ARG       # misaligned xs
+    assert L.gdn_split_bf16(None, 0, 64, None, None) == GDN_OK
+    assert L.gdn_pack_bf16(16, 0, 64, 1 << 20, None) == GDN_ERR_ARG
+    assert L.gdn_pack_bf16(24, 4, 64, 1 << 20, None) == GDN_ERR_ARG
+    assert L.gdn_pack_bf16(1 << 20, 32, 64, (1 << 20) + 64, None) == GDN_ERR_ARG
+    assert b"wp overlaps w" in L.gdn_last_error()
+    assert L.gdn_project_bf16(16, 16, -1, 64, 32, 16, None) == GDN_ERR_ARG
+    assert L.gdn_project_bf16(16, 16, 4, 12, 32, 1 << 20, None) == GDN_ERR_ARG
+    assert L.gdn_project_bf16(16, 16, 4, 64, 0, 1 << 20, None) == GDN_ERR_ARG
+    assert L.gdn_project_bf16(16, 24, 4, 64, 32, 1 << 20, None) == GDN_ERR_ARG
+    assert b"wp is not 16-byte aligned" in L.gdn_last_error()
+    assert L.gdn_project_bf16(1 << 20, 1 << 24, 4, 64, 32, (1 << 20) + 64, None) == GDN_ERR_ARG
+    assert b"out overlaps xs" in L.gdn_last_error()
+    assert L.gdn_project_bf16(1 << 24, 1 << 20, 4, 64, 32, (1 << 20) + 64, None) == GDN_ERR_ARG
+    assert b"out overlaps wp" in L.gdn_last_error()
+    assert L.gdn_project_bf16(None, None, 0, 64, 32, None, None) == GDN_OK

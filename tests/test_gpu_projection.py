@@ -1,0 +1,157 @@
+"""Parity of the qkv / z / out projections (gdn_split_bf16 + gdn_project_bf16) with the
+fp64 oracle on MI355X, through the C ABI.
+
+Tolerance: max |gpu - ref| <= 1e-4 x max |ref| (the per-step bar of the mixer). The
+split of x into bf16 hi + lo keeps each activation to within 2^-16 |x| and the
+matrix cores sum in fp32, so the expected error is near 1e-6 of max |ref|.
+"""
+import numpy as np
+import pytest
+
+import gdn_workloads as W
+import oracle
+from gpu_harness import GpuMixer, assert_close, dev, log
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-4
+
+
+def _w(bits):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda()
+
+
+def _untile(data, rows, k, parts):
+    """The library's tiled layout back to [parts][rows][k] (parts = 2 for split x, 1 for
+    packed weights): tile (R, C), fragment (s, p, lane = i + 32h) holds the 8 values
+    [32R + i][64C + 32h + 8s + j]."""
+    r32, k64 = -(-rows // 32) * 32, -(-k // 64) * 64
+    t = data.reshape(r32 // 32, k64 // 64, 4, parts, 2, 32, 8)          # R C s p h i j
+    full = t.transpose(3, 0, 5, 1, 4, 2, 6).reshape(parts, r32, k64)   # p (R i) (C h s j)
+    return full, full[:, :rows, :k]
+
+
+def test_split_is_round_to_nearest_and_exact_to_2e16():
+    """hi is the round-to-nearest-even bf16 of x (torch's own conversion decides), hi + lo
+    equals x to within 2^-16 |x|, and the padding of the tiles is zero."""
+    import torch
+    import gated_deltanet_mixer_gdn_amd as G
+    rng = np.random.default_rng(90)
+    rows, k = 37, 264
+    x = (rng.standard_normal((rows, k)) * np.exp(rng.uniform(-20, 20, (rows, k)))).astype(np.float32)
+    x[0, :8] = [0.0, -0.0, 1.0, -1.5, 3.3895314e38, -3.3895314e38, 1e-38, 65504.0]
+    xd = dev(x)
+    xs = G.gdn_split_bf16(xd)
+    torch.cuda.synchronize()
+    full, parts = _untile(xs.data.cpu().numpy().view(np.uint16), rows, k, 2)
+    hi, lo = parts
+    assert not full[:, rows:, :].any() and not full[:, :, k:].any()
+    ref_hi = xd.to(torch.bfloat16).view(torch.int16).cpu().numpy().view(np.uint16)
+    big = np.abs(x) >= 3.3e38   # values that round up to infinity are truncated instead
+    np.testing.assert_array_equal(hi[~big], ref_hi[~big])
+    f = lambda b: (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    err = np.abs(f(hi) + f(lo) - x.astype(np.float64))
+    # relative bound while lo is a normal number; below that the error is under 2^-126
+    bound = np.maximum(2.0 ** -16 * np.abs(x.astype(np.float64)), 2.0 ** -126)
+    assert (err <= bound).all(), np.argwhere(err > bound)[:5]
+
+
+def test_pack_is_a_permutation_with_zero_padding():
+    import torch
+    import gated_deltanet_mixer_gdn_amd as G
+    n, k = 70, 200
+    w = np.random.default_rng(89).integers(0, 1 << 16, (n, k), dtype=np.uint16)
+    wp = G.gdn_pack_bf16(_w(w))
+    torch.cuda.synchronize()
+    full, (back,) = _untile(wp.data.cpu().numpy().view(np.uint16), n, k, 1)
+    np.testing.assert_array_equal(back, w)
+    assert not full[:, n:, :].any() and not full[:, :, k:].any()
+
+
+# (rows, k, n): a single row, ragged rows / columns / k, several tiles of each shape
+SHAPES = [(1, 64, 32), (3, 72, 40), (33, 136, 100), (64, 2560, 256), (70, 520, 300), (200, 520, 1030),
+          (37, 6144, 96), (1, 2560, 10240), (16, 2560, 6144), (300, 128, 4100)]
+
+
+@pytest.mark.parametrize("rows,k,n", SHAPES)
+def test_projection_matches_oracle(rows, k, n):
+    import torch
+    import gated_deltanet_mixer_gdn_amd as G
+    log(f"projection rows={rows} k={k} n={n}")
+    x, w = W.make_proj(rows, k, n, seed=91 + rows + k + n)
+    out = torch.full((rows, n), 7.0, device="cuda")
+    G.gdn_project(dev(x), G.gdn_pack_bf16(_w(w)), out)
+    torch.cuda.synchronize()
+    assert_close("out", out.cpu().numpy(), oracle.project(x, w), TOL)
+
+
+@pytest.mark.parametrize("name", ["qkv", "z", "out"])
+def test_projection_full_size_sampled(name):
+    """The pages' shapes at a 256-sequence decode batch; rows sampled across every row
+    tile (first, last and in between), all n columns of each."""
+    import torch
+    import gated_deltanet_mixer_gdn_amd as G
+    k, n = W.PROJECTIONS[name]
+    rows = 256
+    log(f"projection {name} rows={rows} k={k} n={n}")
+    x, w = W.make_proj(rows, k, n, seed={"qkv": 95, "z": 96, "out": 97}[name])
+    out = G.gdn_project(dev(x), G.gdn_pack_bf16(_w(w)))
+    torch.cuda.synchronize()
+    pick = np.array([0, 1, 31, 32, 63, 64, 100, 127, 128, 191, 200, 223, 224, 254, 255])
+    assert_close(name, out.cpu().numpy()[pick], oracle.project(x[pick], w), TOL)
+
+
+def test_projection_is_deterministic():
+    import torch
+    import gated_deltanet_mixer_gdn_amd as G
+    x, w = W.make_proj(256, 6144, 2560, seed=98)
+    xs = G.gdn_split_bf16(dev(x))
+    wp = G.gdn_pack_bf16(_w(w))
+    a = G.gdn_project_bf16(xs, wp)
+    b = G.gdn_project_bf16(xs, wp)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_projection_empty_is_a_no_op():
+    import torch
+    import gated_deltanet_mixer_gdn_amd as G
+    x = torch.empty(0, 2560, device="cuda")
+    out = G.gdn_project(x, G.gdn_pack_bf16(torch.zeros(64, 2560, dtype=torch.int16, device="cuda")))
+    torch.cuda.synchronize()
+    assert out.shape == (0, 64)
+
+
+def test_projections_around_the_mixer():
+    """x -> qkv, z, alpha, beta projections -> mixer -> out projection, against the
+    oracle's projections and mixer on the same x (small geometry, 3 tokens)."""
+    import torch
+    import gated_deltanet_mixer_gdn_amd as G
+    geom = W.Geom(h_k=2, h_v=4)
+    B, T, n_embd = 5, 3, 256
+    wl = W.make("layer", B, T, seed=99, geom=geom, state_std=0.02, conv_std=1.0)
+    xq, wqkv = W.make_proj(B * T, n_embd, geom.channels, seed=100)
+    _, wgate = W.make_proj(1, n_embd, geom.value_dim, seed=101)
+    _, wout = W.make_proj(1, geom.value_dim, n_embd, seed=102)
+    ab = W.make_ab(B, T, seed=103, n_embd=n_embd, h_v=geom.h_v)
+    ab.x = xq.reshape(B, T, n_embd)
+    # the oracle's chain
+    wl.qkv = oracle.project(xq, wqkv).reshape(B, T, -1).astype(np.float32)
+    wl.z = oracle.project(xq, wgate).reshape(B, T, -1).astype(np.float32)
+    ra, rb = oracle.ab_project(ab.x, ab.w_alpha, ab.w_beta)
+    wl.alpha, wl.beta_logit = ra.astype(np.float32), rb.astype(np.float32)
+    res = oracle.run_workload(wl)
+    y_ref = np.stack([r["y"] for r in res])
+    out_ref = oracle.project(y_ref.reshape(B * T, -1), wout)
+    # the HIP chain
+    gm = GpuMixer(wl)
+    xs = G.gdn_split_bf16(dev(xq))
+    G.gdn_project_bf16(xs, G.gdn_pack_bf16(_w(wqkv)), gm.qkv.view(B * T, -1))
+    G.gdn_project_bf16(xs, G.gdn_pack_bf16(_w(wgate)), gm.z.view(B * T, -1))
+    G.gdn_ab_project(dev(ab.x), _w(ab.w_alpha), _w(ab.w_beta), gm.alpha, gm.beta_logit)
+    gm.run(fused=True)
+    out = G.gdn_project(gm.y.view(B * T, -1), G.gdn_pack_bf16(_w(wout)))
+    torch.cuda.synchronize()
+    assert_close("y", gm.y.cpu().numpy().reshape(y_ref.shape), y_ref, 2 * TOL)
+    assert_close("out", out.cpu().numpy(), out_ref, 2 * TOL)
