@@ -499,31 +499,55 @@ int gdn_pack_bf16(const uint16_t* w, int32_t n, int32_t k, uint16_t* wp, void* s
     return launched(gdn::launch_pack_bf16(pp, static_cast<hipStream_t>(stream)), fn);
 }
 
-int gdn_project_bf16(const uint16_t* xs, const uint16_t* wp, int64_t rows, int32_t k, int32_t n, float* out,
-                     void* stream) {
-    const char* fn = "gdn_project_bf16";
+namespace {
+
+int project_common(const char* fn, const uint16_t* xs, const uint16_t* wp, int64_t rows, int32_t k, int32_t n1,
+                   float* out1, int32_t n2, float* out2, void* stream) {
     if (rows < 0) return fail(GDN_ERR_ARG, fn, "rows=%lld is negative", (long long) rows);
     if (k <= 0 || k % 8 != 0) return fail(GDN_ERR_ARG, fn, "k=%d must be a positive multiple of 8", k);
-    if (n <= 0) return fail(GDN_ERR_ARG, fn, "n=%d must be positive", n);
+    if (n1 <= 0 || n2 < 0 || n1 > INT32_MAX - n2) return fail(GDN_ERR_ARG, fn, "n1=%d, n2=%d out of range", n1, n2);
     if (rows == 0) return ok();
+    const int32_t n = n1 + n2;
     const int64_t xs_bytes = gdn_split_bf16_bytes(rows, k);
     if (xs_bytes < 0 || rows > INT64_MAX / 4 / n) return fail(GDN_ERR_ARG, fn, "rows too large");
     if (int rc = check_f4(xs, fn, "xs")) return rc;
     if (int rc = check_f4(wp, fn, "wp")) return rc;
-    if (int rc = check_f1(out, fn, "out")) return rc;
-    const size_t out_bytes = (size_t) rows * n * sizeof(float);
-    if (overlap(out, out_bytes, xs, (size_t) xs_bytes)) return fail(GDN_ERR_ARG, fn, "out overlaps xs");
-    if (overlap(out, out_bytes, wp, (size_t) gdn_pack_bf16_bytes(n, k))) return fail(GDN_ERR_ARG, fn, "out overlaps wp");
+    if (int rc = check_f1(out1, fn, n2 ? "out1" : "out")) return rc;
+    if (n2)
+        if (int rc = check_f1(out2, fn, "out2")) return rc;
+    const size_t b1 = (size_t) rows * n1 * sizeof(float), b2 = (size_t) rows * n2 * sizeof(float);
+    const size_t wp_bytes = (size_t) gdn_pack_bf16_bytes(n, k);
+    if (overlap(out1, b1, xs, (size_t) xs_bytes) || (n2 && overlap(out2, b2, xs, (size_t) xs_bytes)))
+        return fail(GDN_ERR_ARG, fn, "an output overlaps xs");
+    if (overlap(out1, b1, wp, wp_bytes) || (n2 && overlap(out2, b2, wp, wp_bytes)))
+        return fail(GDN_ERR_ARG, fn, "an output overlaps wp");
+    if (n2 && overlap(out1, b1, out2, b2)) return fail(GDN_ERR_ARG, fn, "out1 overlaps out2");
     gdn::GemmParams gp;
     gp.xs = xs;
     gp.wp = wp;
-    gp.out = out;
+    gp.out = out1;
+    gp.out2 = n2 ? out2 : nullptr;
     gp.rows = (long long) rows;
     gp.k = k;
     gp.n = n;
+    gp.n1 = n1;
     const gdn::GemmConfig cfg = gdn::choose_gemm_config(gp.rows, k, n);
     if (gdn::gemm_workgroups(gp, cfg) > INT32_MAX) return fail(GDN_ERR_ARG, fn, "rows x n too large");
     return launched(gdn::launch_project_bf16(gp, cfg, static_cast<hipStream_t>(stream)), fn);
+}
+
+}  // namespace
+
+int gdn_project_bf16(const uint16_t* xs, const uint16_t* wp, int64_t rows, int32_t k, int32_t n, float* out,
+                     void* stream) {
+    if (n <= 0) return fail(GDN_ERR_ARG, "gdn_project_bf16", "n=%d must be positive", n);
+    return project_common("gdn_project_bf16", xs, wp, rows, k, n, out, 0, nullptr, stream);
+}
+
+int gdn_project2_bf16(const uint16_t* xs, const uint16_t* wp, int64_t rows, int32_t k, int32_t n1, float* out1,
+                      int32_t n2, float* out2, void* stream) {
+    if (n2 <= 0) return fail(GDN_ERR_ARG, "gdn_project2_bf16", "n2=%d must be positive", n2);
+    return project_common("gdn_project2_bf16", xs, wp, rows, k, n1, out1, n2, out2, stream);
 }
 
 int gdn_gated_rmsnorm(const float* o, const float* z, const float* w, float eps, int64_t rows, int32_t s,

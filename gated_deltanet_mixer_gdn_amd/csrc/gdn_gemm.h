@@ -36,20 +36,24 @@ struct PackParams {
     int n, k;           // k a multiple of 8
 };
 
-// out[r][j] = sum_e w[j][e] * (hi + lo)[r][e]
+// res[r][j] = sum_e w[j][e] * (hi + lo)[r][e]; columns j < n1 go to out [rows][n1],
+// the others to out2 [rows][n - n1] (n1 = n: one output)
 struct GemmParams {
     const uint16_t* xs;  // split activations, tiled
     const uint16_t* wp;  // packed weights, tiled
-    float* out;          // [rows][n]
+    float* out;
+    float* out2;
     long long rows;
-    int k, n;
+    int k, n, n1;
 };
 
 // Tile shape of one launch: each of the 4 waves of a workgroup computes a
 // (32*wm) x (32*wn) block of out; kw waves (1, 2 or 4) share one block and split
-// its k range, the other 4/kw waves take neighbouring column blocks.
+// its k range, the other 4/kw waves take neighbouring column blocks.  lds = G > 0
+// (kw = 1 only): G groups of 4 such waves take alternate k chunks, and each group's
+// activation tiles go through LDS once instead of being read by every wave.
 struct GemmConfig {
-    int wm, wn, kw;
+    int wm, wn, kw, lds;
 };
 
 bool gemm_config_supported(const GemmConfig& c);

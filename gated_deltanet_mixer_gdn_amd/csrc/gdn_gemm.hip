@@ -97,6 +97,35 @@ __global__ __launch_bounds__(256) void pack_bf16_kernel(PackParams p) {
 // Waves that split k add their partial blocks through LDS in a fixed order
 // (wk = 0, 1, ...), so results do not depend on timing.  Row and column tiles past
 // the padded operands are clamped to the last one; their outputs are not stored.
+// Workgroups are dispatched to the 8 XCDs round robin; give each XCD a contiguous
+// run of tiles, in which the row blocks of one column tile are neighbours and share
+// their weight tiles in that XCD's L2.
+__device__ __forceinline__ int xcd_tile(int b, int tiles_total) {
+    const int per = tiles_total >> 3, extra = tiles_total & 7, xcd = b & 7;
+    return xcd * per + min(xcd, extra) + (b >> 3);
+}
+
+// Accumulator element e of lane (i, h) holds row 8(e/4) + 4h + e%4, column i of its
+// 32 x 32 block; rows past p.rows and columns past p.n are not stored.
+template <int WM, int WN>
+__device__ __forceinline__ void store_blocks(const GemmParams& p, const f16v (&acc)[WM][WN], long long m0, int n0,
+                                             int i, int h) {
+#pragma unroll
+    for (int r = 0; r < WM; ++r)
+#pragma unroll
+        for (int c = 0; c < WN; ++c) {
+            const int col = n0 + 32 * c + i;
+            if (col >= p.n) continue;
+            float* dst = col < p.n1 ? p.out + col : p.out2 + (col - p.n1);
+            const long long ld = col < p.n1 ? p.n1 : p.n - p.n1;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const long long row = m0 + 32 * r + 8 * (e >> 2) + 4 * h + (e & 3);
+                if (row < p.rows) dst[row * ld] = acc[r][c][e];
+            }
+        }
+}
+
 template <int WM, int WN>
 struct Frag {
     bf16x8 a[WM][4][2];  // [row tile][step][hi, lo]
@@ -115,12 +144,7 @@ __global__ __launch_bounds__(256) void project_bf16_kernel(GemmParams p, int til
     const int wn = wave % kWavesN;
     const int wk = wave / kWavesN;
 
-    // Workgroups are dispatched to the 8 XCDs round robin; give each XCD a
-    // contiguous run of tiles, in which the row blocks of one column tile are
-    // neighbours and share their weight tiles in that XCD's L2.
-    const int b = blockIdx.x;
-    const int per = tiles_total >> 3, extra = tiles_total & 7, xcd = b & 7;
-    const int t = xcd * per + min(xcd, extra) + (b >> 3);
+    const int t = xcd_tile(blockIdx.x, tiles_total);
     const int tm = t % tiles_m;
     const int tn = t / tiles_m;
     const long long m0 = (long long) tm * BM;
@@ -218,23 +242,163 @@ __global__ __launch_bounds__(256) void project_bf16_kernel(GemmParams p, int til
         }
     }
 
+    store_blocks<WM, WN>(p, acc, m0, n0, i, h);
+}
+
+// The same product with the activation tiles shared through LDS: a workgroup of
+// 4 * KG waves, 4 side by side in n and KG groups that take alternate k chunks.  Each
+// chunk's WM activation tiles (8 KiB each) are read from memory once per group, by
+// its 256 threads with contiguous 16-byte loads, and every wave of the group takes
+// its fragments from LDS (lane-order 16-byte reads, no bank conflicts).  Two LDS
+// buffers per group alternate; the next chunk's activation share and weight
+// fragments are loaded while the current chunk runs and the share is written to
+// the other buffer after it.  With KG = 2 the second group's partial blocks are
+// added to the first's through LDS at the end (group 0 first, a fixed order).
+template <int WM, int WN, int KG>
+__global__ __launch_bounds__(256 * KG) void project_lds_kernel(GemmParams p, int tiles_m, int tiles_total,
+                                                               int n_chunks) {
+    constexpr int BM = 32 * WM;
+    constexpr int BN = 128 * WN;
+    constexpr int kAbufU4 = 2 * WM * 512;                 // per group
+    constexpr int kRedU4 = KG > 1 ? 4 * WM * WN * 16 * 16 : 0;   // 4 waves x acc floats / 4
+    constexpr int kLdsU4 = KG * kAbufU4 > kRedU4 ? KG * kAbufU4 : kRedU4;
+    __shared__ u4v lds[kLdsU4];
+    const int gtid = threadIdx.x;
+    const int kg = gtid >> 8;            // k group
+    const int tid = gtid & 255;          // thread within the group
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int i = lane & 31;
+    const int h = lane >> 5;
+    u4v* abuf = lds + kg * kAbufU4;      // [2][WM][512]
+
+    const int t = xcd_tile(blockIdx.x, tiles_total);
+    const int tm = t % tiles_m;
+    const int tn = t / tiles_m;
+    const long long m0 = (long long) tm * BM;
+    const int n0 = tn * BN + wave * 32 * WN;
+    const long long last_rt = (p.rows + kTileRows - 1) / kTileRows - 1;
+    const int last_ct = (p.n + kTileRows - 1) / kTileRows - 1;
+
+    const u4v* asrc[WM];
+#pragma unroll
+    for (int r = 0; r < WM; ++r) {
+        const long long rt = min((long long) tm * WM + r, last_rt);
+        asrc[r] = (const u4v*) p.xs + rt * n_chunks * 512 + tid;
+    }
+    const bf16x8* bbase[WN];
+#pragma unroll
+    for (int c = 0; c < WN; ++c) {
+        const long long ct = min(n0 / 32 + c, last_ct);
+        bbase[c] = (const bf16x8*) p.wp + ct * n_chunks * 256 + lane;
+    }
+
+    struct BFrag {
+        bf16x8 b[WN][4];
+    };
+    u4v ash[WM][2];
+    auto load_a = [&](int ch) {
+#pragma unroll
+        for (int r = 0; r < WM; ++r) {
+            ash[r][0] = asrc[r][ch * 512];
+            ash[r][1] = asrc[r][ch * 512 + 256];
+        }
+    };
+    auto store_a = [&](int buf) {
+#pragma unroll
+        for (int r = 0; r < WM; ++r) {
+            abuf[(buf * WM + r) * 512 + tid] = ash[r][0];
+            abuf[(buf * WM + r) * 512 + tid + 256] = ash[r][1];
+        }
+    };
+    auto load_b = [&](int ch, BFrag& f) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int c = 0; c < WN; ++c) f.b[c][s] = bbase[c][ch * 256 + s * 64];
+    };
+
+    f16v acc[WM][WN];
 #pragma unroll
     for (int r = 0; r < WM; ++r)
 #pragma unroll
-        for (int c = 0; c < WN; ++c) {
-            const int col = n0 + 32 * c + i;
-            if (col >= p.n) continue;
+        for (int c = 0; c < WN; ++c) acc[r][c] = f16v{};
+    auto compute = [&](int buf, const BFrag& f) {
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const long long row = m0 + 32 * r + 8 * (e >> 2) + 4 * h + (e & 3);
-                if (row < p.rows) p.out[row * p.n + col] = acc[r][c][e];
+        for (int s = 0; s < 4; ++s) {
+            bf16x8 a[WM][2];
+#pragma unroll
+            for (int r = 0; r < WM; ++r) {
+                a[r][0] = __builtin_bit_cast(bf16x8, abuf[(buf * WM + r) * 512 + (2 * s) * 64 + lane]);
+                a[r][1] = __builtin_bit_cast(bf16x8, abuf[(buf * WM + r) * 512 + (2 * s + 1) * 64 + lane]);
             }
+#pragma unroll
+            for (int r = 0; r < WM; ++r)
+#pragma unroll
+                for (int c = 0; c < WN; ++c) {
+                    acc[r][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[r][0], f.b[c][s], acc[r][c], 0, 0, 0);
+                    acc[r][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[r][1], f.b[c][s], acc[r][c], 0, 0, 0);
+                }
         }
+    };
+
+    // Group kg takes chunks kg, kg + KG, ...; its j-th chunk lives in its buffer j % 2
+    // and f0 / f1 hold the weight fragments of its even / odd ones.  Every group runs
+    // the same number of trips (a group past its last chunk reloads that chunk and
+    // skips the arithmetic) so all waves meet at the same barriers; every load is
+    // issued unconditionally so the compiler's wait counts stay exact.
+    const int cnt = (n_chunks + KG - 1) / KG;                   // trips of the longest group
+    const int mine = (n_chunks - kg + KG - 1) / KG;              // chunks of this group (>= cnt - 1)
+    auto chunk = [&](int j) { return mine > 0 ? kg + KG * min(j, mine - 1) : 0; };
+    BFrag f0, f1;
+    load_a(chunk(0));
+    load_b(chunk(0), f0);
+    store_a(0);
+    __syncthreads();
+    int j = 0;
+    for (; j + 2 <= cnt; j += 2) {
+        load_a(chunk(j + 1));
+        load_b(chunk(j + 1), f1);
+        __builtin_amdgcn_sched_barrier(0);
+        if (j < mine) compute(0, f0);
+        store_a(1);
+        __syncthreads();
+        load_a(chunk(j + 2));
+        load_b(chunk(j + 2), f0);
+        __builtin_amdgcn_sched_barrier(0);
+        if (j + 1 < mine) compute(1, f1);
+        store_a(0);
+        __syncthreads();
+    }
+    if (j < cnt && j < mine) compute(0, f0);
+
+    if constexpr (KG > 1) {
+        // group 1 hands its partial blocks to group 0 (the A buffers are free now)
+        __syncthreads();
+        float* red = (float*) lds + wave * (WM * WN * 16 * 64) + lane;
+        if (kg == 1) {
+#pragma unroll
+            for (int r = 0; r < WM; ++r)
+#pragma unroll
+                for (int c = 0; c < WN; ++c)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) red[((r * WN + c) * 16 + e) * 64] = acc[r][c][e];
+        }
+        __syncthreads();
+        if (kg == 1) return;
+#pragma unroll
+        for (int r = 0; r < WM; ++r)
+#pragma unroll
+            for (int c = 0; c < WN; ++c)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) acc[r][c][e] += red[((r * WN + c) * 16 + e) * 64];
+    }
+    store_blocks<WM, WN>(p, acc, m0, n0, i, h);
 }
 
-// the instantiated tile shapes: {wm, wn, kw}
+// the instantiated tile shapes: {wm, wn, kw, lds}
 constexpr GemmConfig kConfigs[] = {
-    {1, 1, 4}, {1, 2, 4}, {1, 2, 2}, {1, 2, 1}, {2, 1, 4}, {2, 2, 4}, {2, 2, 2}, {2, 2, 1}, {2, 4, 2}, {2, 4, 1},
+    {1, 1, 4, 0}, {1, 2, 4, 0}, {1, 3, 4, 0}, {2, 1, 4, 0}, {2, 2, 4, 0}, {2, 3, 4, 0}, {2, 3, 2, 0}, {2, 3, 1, 2},
 };
 
 template <int WM, int WN, int KW>
@@ -246,11 +410,20 @@ hipError_t launch_tile(const GemmParams& p, hipStream_t stream) {
     return hipGetLastError();
 }
 
+template <int WM, int WN, int KG>
+hipError_t launch_lds_tile(const GemmParams& p, hipStream_t stream) {
+    constexpr int BM = 32 * WM, BN = 128 * WN;
+    const long long tm = (p.rows + BM - 1) / BM, tn = ((long long) p.n + BN - 1) / BN;
+    hipLaunchKernelGGL((project_lds_kernel<WM, WN, KG>), dim3((unsigned) (tm * tn)), dim3(256 * KG), 0, stream, p,
+                       (int) tm, (int) (tm * tn), (int) (pad_up(p.k, kTileK) / kTileK));
+    return hipGetLastError();
+}
+
 }  // namespace
 
 bool gemm_config_supported(const GemmConfig& c) {
     for (const GemmConfig& k : kConfigs)
-        if (k.wm == c.wm && k.wn == c.wn && k.kw == c.kw) return true;
+        if (k.wm == c.wm && k.wn == c.wn && k.kw == c.kw && k.lds == c.lds) return true;
     return false;
 }
 
@@ -259,33 +432,18 @@ long long gemm_workgroups(const GemmParams& p, const GemmConfig& c) {
     return (p.rows + bm - 1) / bm * (((long long) p.n + bn - 1) / bn);
 }
 
-// Fewest rows per tile that cover the batch, then the widest tile that still
-// gives every compute unit a workgroup; when none does, the tile with the most
-// workgroups.
+// Tile shapes measured best on MI355X for the pages' projection shapes (k = 2560 or
+// 6144, n = 2560 to 16384) at 1 to 512 rows: one row tile while the batch fits in
+// 64 rows, two above; wider column tiles as n grows, so the launch keeps about one
+// workgroup per compute unit; k split over the workgroup's waves unless the tiles
+// are already many (and, from 512 rows with n >= 8192, the LDS-shared form).
 GemmConfig choose_gemm_config(long long rows, int k, int n) {
     (void) k;
-    const int wm = rows <= 32 ? 1 : 2;
-    GemmParams p{};
-    p.rows = rows;
-    p.n = n;
-    GemmConfig best{0, 0, 0};
-    long long best_wg = -1;
-    for (const GemmConfig& c : kConfigs) {
-        if (c.wm != wm) continue;
-        const long long wg = gemm_workgroups(p, c);
-        const long long cols = 32LL * c.wn * (4 / c.kw);
-        const long long best_cols = 32LL * best.wn * (best.kw ? 4 / best.kw : 0);
-        if (wg >= 256) {
-            if (best_wg < 256 || cols > best_cols || (cols == best_cols && c.kw < best.kw)) {
-                best = c;
-                best_wg = wg;
-            }
-        } else if (best_wg < 256 && wg > best_wg) {
-            best = c;
-            best_wg = wg;
-        }
-    }
-    return best;
+    if (rows <= 32) return n >= 8192 ? GemmConfig{1, 2, 4, 0} : GemmConfig{1, 1, 4, 0};
+    if (rows <= 64) return n >= 8192 ? GemmConfig{1, 3, 4, 0} : n >= 4096 ? GemmConfig{1, 2, 4, 0} : GemmConfig{1, 1, 4, 0};
+    if (rows <= 128) return n >= 8192 ? GemmConfig{2, 3, 4, 0} : n >= 4096 ? GemmConfig{2, 2, 4, 0} : GemmConfig{2, 1, 4, 0};
+    if (rows <= 256) return n >= 8192 ? GemmConfig{2, 3, 2, 0} : n >= 4096 ? GemmConfig{2, 3, 4, 0} : GemmConfig{2, 2, 4, 0};
+    return n >= 8192 ? GemmConfig{2, 3, 1, 2} : n >= 4096 ? GemmConfig{2, 3, 2, 0} : GemmConfig{2, 3, 4, 0};
 }
 
 hipError_t launch_split_bf16(const SplitParams& p, hipStream_t stream) {
@@ -304,18 +462,19 @@ hipError_t launch_pack_bf16(const PackParams& p, hipStream_t stream) {
 
 hipError_t launch_project_bf16(const GemmParams& p, const GemmConfig& c, hipStream_t stream) {
 #define GDN_TILE(A, B, C) \
-    if (c.wm == A && c.wn == B && c.kw == C) return launch_tile<A, B, C>(p, stream);
+    if (!c.lds && c.wm == A && c.wn == B && c.kw == C) return launch_tile<A, B, C>(p, stream);
+#define GDN_LDS_TILE(A, B, G) \
+    if (c.lds == G && c.wm == A && c.wn == B && c.kw == 1) return launch_lds_tile<A, B, G>(p, stream);
     GDN_TILE(1, 1, 4)
     GDN_TILE(1, 2, 4)
-    GDN_TILE(1, 2, 2)
-    GDN_TILE(1, 2, 1)
+    GDN_TILE(1, 3, 4)
     GDN_TILE(2, 1, 4)
     GDN_TILE(2, 2, 4)
-    GDN_TILE(2, 2, 2)
-    GDN_TILE(2, 2, 1)
-    GDN_TILE(2, 4, 2)
-    GDN_TILE(2, 4, 1)
+    GDN_TILE(2, 3, 4)
+    GDN_TILE(2, 3, 2)
+    GDN_LDS_TILE(2, 3, 2)
 #undef GDN_TILE
+#undef GDN_LDS_TILE
     return hipErrorInvalidValue;
 }
 

@@ -23,7 +23,7 @@ EXPORTS = (
     "gdn_state_pool_slots", "gdn_state_pool_zero", "gdn_conv_silu_norm", "gdn_decode_step",
     "gdn_decode_step_norm", "gdn_decode_fused", "gdn_verify_window", "gdn_commit", "gdn_gated_rmsnorm",
     "gdn_ab_project", "gdn_split_bf16_bytes", "gdn_pack_bf16_bytes", "gdn_split_bf16", "gdn_pack_bf16",
-    "gdn_project_bf16",
+    "gdn_project_bf16", "gdn_project2_bf16",
 )
 
 
@@ -94,6 +94,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "gdn_pack_bf16_bytes": ([i32, i32], ctypes.c_int64),
         "gdn_split_bf16": ([vp, i64, i32, vp, vp], ctypes.c_int),
         "gdn_pack_bf16": ([vp, i32, i32, vp, vp], ctypes.c_int),
+        "gdn_project2_bf16": ([vp, vp, i64, i32, i32, vp, i32, vp, vp], ctypes.c_int),
         "gdn_project_bf16": ([vp, vp, i64, i32, i32, vp, vp], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
@@ -378,6 +379,23 @@ def gdn_project_bf16(xs: SplitX, wp: PackedW, out=None):
     _check(load_library().gdn_project_bf16(xs.data.data_ptr(), wp.data.data_ptr(), xs.rows, xs.k, wp.n,
                                            _f32(out, "out"), _stream(xs.data)))
     return out
+
+
+def gdn_project2_bf16(xs: SplitX, wp: PackedW, n1: int, out1=None, out2=None):
+    """Two projections of the same activations in one launch: wp packs the
+    concatenation [w1; w2] (n1 + n2 rows); returns (out1 [rows][n1], out2 [rows][n2])."""
+    import torch
+    n2 = wp.n - n1
+    if xs.k != wp.k or not 0 < n1 < wp.n:
+        raise ValueError(f"x has k={xs.k}, w has k={wp.k} and {wp.n} rows, n1={n1}")
+    dev = xs.data.device
+    out1 = torch.empty(xs.rows, n1, device=dev) if out1 is None else out1
+    out2 = torch.empty(xs.rows, n2, device=dev) if out2 is None else out2
+    if out1.numel() != xs.rows * n1 or out2.numel() != xs.rows * n2:
+        raise ValueError("out1 / out2 have the wrong size")
+    _check(load_library().gdn_project2_bf16(xs.data.data_ptr(), wp.data.data_ptr(), xs.rows, xs.k, n1,
+                                            _f32(out1, "out1"), n2, _f32(out2, "out2"), _stream(xs.data)))
+    return out1, out2
 
 
 def gdn_project(x, wp: PackedW, out=None):

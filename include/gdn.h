@@ -265,6 +265,15 @@ int gdn_pack_bf16(const uint16_t* w, int32_t n, int32_t k, uint16_t* wp, void* s
 int gdn_project_bf16(const uint16_t* xs, const uint16_t* wp, int64_t rows, int32_t k, int32_t n, float* out,
                      void* stream);
 
+/* Two projections of the same activations in one launch (qkv and z both read the
+ * layer input): wp is gdn_pack_bf16 of the (n1 + n2) x k matrix whose first n1 rows
+ * are the first weight matrix and whose last n2 rows are the second; columns j < n1
+ * of the product go to out1 [rows][n1], the others to out2 [rows][n2] (4-byte
+ * aligned, overlapping neither each other nor an input).  n1, n2 >= 1.  Each output
+ * equals gdn_project_bf16 of the concatenated weights, column for column. */
+int gdn_project2_bf16(const uint16_t* xs, const uint16_t* wp, int64_t rows, int32_t k, int32_t n1, float* out1,
+                      int32_t n2, float* out2, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

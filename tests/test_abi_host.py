@@ -226,7 +226,14 @@ def test_projection_argument_errors(L):
     assert L.gdn_project_bf16(16, 24, 4, 64, 32, 1 << 20, None) == GDN_ERR_ARG
     assert b"wp is not 16-byte aligned" in L.gdn_last_error()
     assert L.gdn_project_bf16(1 << 20, 1 << 24, 4, 64, 32, (1 << 20) + 64, None) == GDN_ERR_ARG
-    assert b"out overlaps xs" in L.gdn_last_error()
+    assert b"output overlaps xs" in L.gdn_last_error()
     assert L.gdn_project_bf16(1 << 24, 1 << 20, 4, 64, 32, (1 << 20) + 64, None) == GDN_ERR_ARG
-    assert b"out overlaps wp" in L.gdn_last_error()
+    assert b"output overlaps wp" in L.gdn_last_error()
     assert L.gdn_project_bf16(None, None, 0, 64, 32, None, None) == GDN_OK
+    assert L.gdn_project2_bf16(16, 16, 4, 64, 32, 1 << 20, 0, 1 << 22, None) == GDN_ERR_ARG
+    assert L.gdn_project2_bf16(16, 16, 4, 64, 0, 1 << 20, 32, 1 << 22, None) == GDN_ERR_ARG
+    assert L.gdn_project2_bf16(16, 16, 4, 64, 32, 1 << 20, 32, (1 << 20) + 256, None) == GDN_ERR_ARG
+    assert b"out1 overlaps out2" in L.gdn_last_error()
+    assert L.gdn_project2_bf16(16, 16, 4, 64, 32, 1 << 20, 32, 2, None) == GDN_ERR_ARG
+    assert b"out2 is not 4-byte aligned" in L.gdn_last_error()
+    assert L.gdn_project2_bf16(None, None, 0, 64, 32, None, 16, None, None) == GDN_OK

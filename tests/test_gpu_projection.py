@@ -69,9 +69,14 @@ def test_pack_is_a_permutation_with_zero_padding():
     assert not full[:, n:, :].any() and not full[:, :, k:].any()
 
 
-# (rows, k, n): a single row, ragged rows / columns / k, several tiles of each shape
+# (rows, k, n): a single row, ragged rows / columns / k, several tiles of each shape, and
+# every tile shape the launch picks by rows and n (one or two row tiles per workgroup,
+# 1-3 column tiles per wave, k split over 1, 2 or 4 waves, the LDS-shared form with
+# an odd chunk count and with a single chunk, which leaves its second wave group idle)
 SHAPES = [(1, 64, 32), (3, 72, 40), (33, 136, 100), (64, 2560, 256), (70, 520, 300), (200, 520, 1030),
-          (37, 6144, 96), (1, 2560, 10240), (16, 2560, 6144), (300, 128, 4100)]
+          (37, 6144, 96), (1, 2560, 10240), (16, 2560, 6144), (300, 128, 4100), (50, 200, 8200),
+          (40, 136, 5000), (100, 264, 8300), (150, 136, 4500), (250, 72, 8250), (300, 200, 9000),
+          (300, 136, 8200), (600, 64, 8192)]
 
 
 @pytest.mark.parametrize("rows,k,n", SHAPES)
@@ -100,6 +105,26 @@ def test_projection_full_size_sampled(name):
     torch.cuda.synchronize()
     pick = np.array([0, 1, 31, 32, 63, 64, 100, 127, 128, 191, 200, 223, 224, 254, 255])
     assert_close(name, out.cpu().numpy()[pick], oracle.project(x[pick], w), TOL)
+
+
+@pytest.mark.parametrize("rows,k,n1,n2", [(256, 2560, 10240, 6144), (37, 200, 100, 60), (300, 136, 8192, 40)])
+def test_two_outputs_equal_the_concatenated_projection(rows, k, n1, n2):
+    """gdn_project2_bf16 (qkv and z in one launch) writes, column for column, what
+    gdn_project_bf16 writes for the concatenated weights, and matches the oracle."""
+    import torch
+    import gated_deltanet_mixer_gdn_amd as G
+    log(f"two outputs rows={rows} k={k} n1={n1} n2={n2}")
+    x, w = W.make_proj(rows, k, n1 + n2, seed=104 + rows)
+    wp = G.gdn_pack_bf16(_w(w))
+    xs = G.gdn_split_bf16(dev(x))
+    o1, o2 = G.gdn_project2_bf16(xs, wp, n1)
+    whole = G.gdn_project_bf16(xs, wp)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, whole[:, :n1]) and torch.equal(o2, whole[:, n1:])
+    pick = np.unique(np.linspace(0, rows - 1, 9).astype(int))
+    ref = oracle.project(x[pick], w)
+    assert_close("out1", o1.cpu().numpy()[pick], ref[:, :n1], TOL)
+    assert_close("out2", o2.cpu().numpy()[pick], ref[:, n1:], TOL)
 
 
 def test_projection_is_deterministic():
@@ -147,8 +172,9 @@ def test_projections_around_the_mixer():
     # the HIP chain
     gm = GpuMixer(wl)
     xs = G.gdn_split_bf16(dev(xq))
-    G.gdn_project_bf16(xs, G.gdn_pack_bf16(_w(wqkv)), gm.qkv.view(B * T, -1))
-    G.gdn_project_bf16(xs, G.gdn_pack_bf16(_w(wgate)), gm.z.view(B * T, -1))
+    # qkv and z in one launch over the concatenated weights
+    wqkvz = G.gdn_pack_bf16(_w(np.concatenate([wqkv, wgate])))
+    G.gdn_project2_bf16(xs, wqkvz, geom.channels, gm.qkv.view(B * T, -1), gm.z.view(B * T, -1))
     G.gdn_ab_project(dev(ab.x), _w(ab.w_alpha), _w(ab.w_beta), gm.alpha, gm.beta_logit)
     gm.run(fused=True)
     out = G.gdn_project(gm.y.view(B * T, -1), G.gdn_pack_bf16(_w(wout)))
