@@ -33,6 +33,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0            # MI355X HBM3E, published peak
+BF16_PEAK_TFLOPS = 2500.0         # MI355X dense bf16 matrix peak, published
 # the sources the recurrence kernel is built from (its counter record is void once they change)
 KERNEL_SRCS = [os.path.join(ROOT, "gated_deltanet_mixer_gdn_amd", "csrc", f)
                for f in ("gdn_recurrence.hip", "gdn_device.h", "gdn_kernels.h")]
@@ -124,6 +125,49 @@ def copy_probe(mib: int, reps: int = 5):
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_probe_bytes_read": n * 4, "copy_probe_bytes_written": n * 4, "reps": reps}))
+
+
+def projections_context(G, W, rows: int, stream, reps: int = 50):
+    """Time the split of x, qkv + z in one launch, the split of y and the out projection
+    at the pages' sizes; algorithmic flops are 2 * rows * k * n per projection."""
+    import numpy as np
+    import torch
+    k_in, n_qkv = W.PROJECTIONS["qkv"]
+    _, n_z = W.PROJECTIONS["z"]
+    k_out, n_out = W.PROJECTIONS["out"]
+    x, w_qkvz = W.make_proj(rows, k_in, n_qkv + n_z, seed=12)
+    y, w_out = W.make_proj(rows, k_out, n_out, seed=13)
+    dev16 = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda()
+    wp_qkvz, wp_out = G.gdn_pack_bf16(dev16(w_qkvz)), G.gdn_pack_bf16(dev16(w_out))
+    xd, yd = torch.from_numpy(x).cuda(), torch.from_numpy(y).cuda()
+    xs, ys = G.gdn_split_bf16(xd), G.gdn_split_bf16(yd)
+    qkv, z = torch.empty(rows, n_qkv, device="cuda"), torch.empty(rows, n_z, device="cuda")
+    out = torch.empty(rows, n_out, device="cuda")
+    calls = {
+        "split_x": lambda: G.gdn_split_bf16(xd, xs),
+        "qkv_z": lambda: G.gdn_project2_bf16(xs, wp_qkvz, n_qkv, qkv, z),
+        "split_y": lambda: G.gdn_split_bf16(yd, ys),
+        "out": lambda: G.gdn_project_bf16(ys, wp_out, out),
+    }
+    us = {}
+    for name, fn in calls.items():
+        for _ in range(5):
+            fn()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record(stream)
+        for _ in range(reps):
+            fn()
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        us[name] = ev[0].elapsed_time(ev[1]) / reps * 1000.0
+    flops = {"qkv_z": 2.0 * rows * k_in * (n_qkv + n_z), "out": 2.0 * rows * k_out * n_out}
+    tflops = {kname: flops[kname] / us[kname] / 1e6 for kname in flops}
+    total_us = sum(us.values())
+    log("projections: " + ", ".join(f"{kname}={v:.1f}us" for kname, v in us.items()) +
+        f"; qkv+z {tflops['qkv_z']:.0f} TFLOP/s, out {tflops['out']:.0f} TFLOP/s")
+    return {"rows": rows, "us": us, "us_total": total_us, "algorithmic_flops": flops, "tflops": tflops,
+            "frac_of_bf16_peak": {kname: v / BF16_PEAK_TFLOPS for kname, v in tflops.items()},
+            "note": "fp32 activations as bf16 hi+lo: two bf16 matrix ops per multiply-add"}
 
 
 def main():
@@ -258,6 +302,11 @@ def main():
     ab_bytes = ab.x.nbytes + ab.w_alpha.nbytes + ab.w_beta.nbytes + 2 * ab_a.numel() * 4
     del ab_x, ab_a, ab_b
 
+    # context: the dense projections around the mixer for the same rows (bf16 weights,
+    # fp32 activations split once into bf16 hi + lo): qkv and z in one launch over the
+    # layer input, out over the mixer output
+    proj = projections_context(G, W, wl.B * wl.T, stream)
+
     # context: a plain device-to-device copy of the state's size on the same stream
     ref_src = pool.state.view(-1)
     ref_dst = torch.empty_like(ref_src)
@@ -328,6 +377,7 @@ def main():
         "d2d_copy_gbps_same_size": copy_gbps,
         "ab_projection": {"us": ab_us, "algorithmic_bytes": int(ab_bytes), "gbps": ab_bytes / ab_us / 1e3,
                           "rows": wl.B * wl.T, "n_embd": W.N_EMBD},
+        "projections": proj,
         "roofline": {"kernel": "decode_one_kernel<fused norm>" if wl.T == 1 else "decode_multi_kernel<fused norm>",
                      "bound": "hbm",
                      "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",

@@ -398,7 +398,8 @@ __global__ __launch_bounds__(256 * KG) void project_lds_kernel(GemmParams p, int
 
 // the instantiated tile shapes: {wm, wn, kw, lds}
 constexpr GemmConfig kConfigs[] = {
-    {1, 1, 4, 0}, {1, 2, 4, 0}, {1, 3, 4, 0}, {2, 1, 4, 0}, {2, 2, 4, 0}, {2, 3, 4, 0}, {2, 3, 2, 0}, {2, 3, 1, 2},
+    {1, 1, 4, 0}, {1, 2, 4, 0}, {1, 3, 4, 0}, {2, 1, 4, 0}, {2, 2, 4, 0}, {2, 2, 2, 0},
+    {2, 2, 1, 0}, {2, 3, 4, 0}, {2, 3, 2, 0}, {2, 3, 1, 2},
 };
 
 template <int WM, int WN, int KW>
@@ -432,18 +433,46 @@ long long gemm_workgroups(const GemmParams& p, const GemmConfig& c) {
     return (p.rows + bm - 1) / bm * (((long long) p.n + bn - 1) / bn);
 }
 
-// Tile shapes measured best on MI355X for the pages' projection shapes (k = 2560 or
-// 6144, n = 2560 to 16384) at 1 to 512 rows: one row tile while the batch fits in
-// 64 rows, two above; wider column tiles as n grows, so the launch keeps about one
-// workgroup per compute unit; k split over the workgroup's waves unless the tiles
-// are already many (and, from 512 rows with n >= 8192, the LDS-shared form).
+// Up to 64 rows the product is bound by the weight stream, and the tile shapes that
+// measured fastest on MI355X for n = 2560 to 16384 are taken by rule: one row tile,
+// the k range split over the 4 waves, wider column tiles as n grows.  Above 64 rows
+// it is bound by the matrix cores and the L2 -> CU operand stream; each candidate
+// shape is priced as (rounds of 256 workgroups) x (chunks per wave) x (32x32 blocks
+// per wave) x (measured microseconds per block-chunk of that shape), which keeps
+// the launch from spilling a few workgroups into a second round.
+namespace {
+struct Priced {
+    GemmConfig c;
+    double us_per_block_chunk;
+    long long min_rows;
+};
+constexpr Priced kPriced[] = {
+    {{2, 2, 1, 0}, 0.245, 65}, {{2, 3, 2, 0}, 0.31, 65}, {{2, 2, 2, 0}, 0.305, 65}, {{2, 2, 4, 0}, 0.33, 65},
+    {{2, 3, 4, 0}, 0.38, 65},  {{2, 1, 4, 0}, 0.42, 65}, {{2, 3, 1, 2}, 0.46, 257},
+};
+}  // namespace
+
 GemmConfig choose_gemm_config(long long rows, int k, int n) {
-    (void) k;
     if (rows <= 32) return n >= 8192 ? GemmConfig{1, 2, 4, 0} : GemmConfig{1, 1, 4, 0};
     if (rows <= 64) return n >= 8192 ? GemmConfig{1, 3, 4, 0} : n >= 4096 ? GemmConfig{1, 2, 4, 0} : GemmConfig{1, 1, 4, 0};
-    if (rows <= 128) return n >= 8192 ? GemmConfig{2, 3, 4, 0} : n >= 4096 ? GemmConfig{2, 2, 4, 0} : GemmConfig{2, 1, 4, 0};
-    if (rows <= 256) return n >= 8192 ? GemmConfig{2, 3, 2, 0} : n >= 4096 ? GemmConfig{2, 3, 4, 0} : GemmConfig{2, 2, 4, 0};
-    return n >= 8192 ? GemmConfig{2, 3, 1, 2} : n >= 4096 ? GemmConfig{2, 3, 2, 0} : GemmConfig{2, 3, 4, 0};
+    const long long chunks = pad_up(k, kTileK) / kTileK;
+    GemmParams p{};
+    p.rows = rows;
+    p.n = n;
+    GemmConfig best = kPriced[0].c;
+    double best_us = -1.0;
+    for (const Priced& q : kPriced) {
+        if (rows < q.min_rows) continue;
+        const long long split = q.c.lds ? q.c.lds : q.c.kw;
+        const long long rounds = (gemm_workgroups(p, q.c) + 255) / 256;
+        const double us = (double) rounds * (double) ((chunks + split - 1) / split) * q.c.wm * q.c.wn *
+                          q.us_per_block_chunk;
+        if (best_us < 0.0 || us < best_us) {
+            best = q.c;
+            best_us = us;
+        }
+    }
+    return best;
 }
 
 hipError_t launch_split_bf16(const SplitParams& p, hipStream_t stream) {
@@ -470,6 +499,8 @@ hipError_t launch_project_bf16(const GemmParams& p, const GemmConfig& c, hipStre
     GDN_TILE(1, 3, 4)
     GDN_TILE(2, 1, 4)
     GDN_TILE(2, 2, 4)
+    GDN_TILE(2, 2, 2)
+    GDN_TILE(2, 2, 1)
     GDN_TILE(2, 3, 4)
     GDN_TILE(2, 3, 2)
     GDN_LDS_TILE(2, 3, 2)

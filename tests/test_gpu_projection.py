@@ -70,9 +70,9 @@ def test_pack_is_a_permutation_with_zero_padding():
 
 
 # (rows, k, n): a single row, ragged rows / columns / k, several tiles of each shape, and
-# every tile shape the launch picks by rows and n (one or two row tiles per workgroup,
-# 1-3 column tiles per wave, k split over 1, 2 or 4 waves, the LDS-shared form with
-# an odd chunk count and with a single chunk, which leaves its second wave group idle)
+# the tile shapes the launch picks by rows, k and n (one or two row tiles per
+# workgroup, 1-3 column tiles per wave, k split over 1, 2 or 4 waves); the LDS-shared
+# form, picked only for long k at more than 256 rows, has its own sampled test below
 SHAPES = [(1, 64, 32), (3, 72, 40), (33, 136, 100), (64, 2560, 256), (70, 520, 300), (200, 520, 1030),
           (37, 6144, 96), (1, 2560, 10240), (16, 2560, 6144), (300, 128, 4100), (50, 200, 8200),
           (40, 136, 5000), (100, 264, 8300), (150, 136, 4500), (250, 72, 8250), (300, 200, 9000),
@@ -105,6 +105,21 @@ def test_projection_full_size_sampled(name):
     torch.cuda.synchronize()
     pick = np.array([0, 1, 31, 32, 63, 64, 100, 127, 128, 191, 200, 223, 224, 254, 255])
     assert_close(name, out.cpu().numpy()[pick], oracle.project(x[pick], w), TOL)
+
+
+@pytest.mark.parametrize("rows,k", [(512, 2560), (520, 2624)])
+def test_projection_lds_form_sampled(rows, k):
+    """More than 256 rows with a long k take the LDS-shared two-group tile (an even and an
+    odd chunk count, a ragged last row tile); rows sampled across all row tiles."""
+    import torch
+    import gated_deltanet_mixer_gdn_amd as G
+    n = 10240
+    log(f"projection (LDS form) rows={rows} k={k} n={n}")
+    x, w = W.make_proj(rows, k, n, seed=110 + k)
+    out = G.gdn_project(dev(x), G.gdn_pack_bf16(_w(w)))
+    torch.cuda.synchronize()
+    pick = np.unique(np.concatenate([np.linspace(0, rows - 1, 13).astype(int), [63, 64, 255, 256, rows - 1]]))
+    assert_close("out", out.cpu().numpy()[pick], oracle.project(x[pick], w), TOL)
 
 
 @pytest.mark.parametrize("rows,k,n1,n2", [(256, 2560, 10240, 6144), (37, 200, 100, 60), (300, 136, 8192, 40)])
