@@ -72,6 +72,10 @@ class Workload:
     z: np.ndarray              # [B][T][h_v*s]
     eps: float = 1e-6
     meta: dict = field(default_factory=dict)
+    # model variants: the SiLU output gate z * sigmoid(z), and the 1/sqrt(S) on the
+    # readout o instead of on q (both off = the pages' model)
+    gate_silu: bool = False
+    scale_after_readout: bool = False
 
     def tokens_of(self, b: int) -> int:
         return self.T if self.n_tok is None else int(self.n_tok[b])

@@ -49,11 +49,11 @@ def lib():
         L.gdn_oracle_sigmoid.restype = d
         L.gdn_oracle_softplus.argtypes = [d]
         L.gdn_oracle_softplus.restype = d
-        L.gdn_oracle_conv_silu_norm.argtypes = [i, i, i, i, i, _D, _D, d, _D, _D]
+        L.gdn_oracle_conv_silu_norm.argtypes = [i, i, i, i, i, _D, _D, d, _D, _D, i]
         L.gdn_oracle_beta_gate.argtypes = [i, i, _D, _D, _D, _D, _D, _D]
-        L.gdn_oracle_delta_rule.argtypes = [i, i, i, i, _D, _D, _D, _D, _D]
-        L.gdn_oracle_gated_rmsnorm.argtypes = [i64, i, _D, _D, _D, d, _D]
-        L.gdn_oracle_mixer.argtypes = [i, i, i, i, i] + [_D] * 8 + [d] + [_D] * 6
+        L.gdn_oracle_delta_rule.argtypes = [i, i, i, i, _D, _D, _D, _D, _D, d]
+        L.gdn_oracle_gated_rmsnorm.argtypes = [i64, i, _D, _D, _D, d, _D, i]
+        L.gdn_oracle_mixer.argtypes = [i, i, i, i, i] + [_D] * 8 + [d] + [_D] * 6 + [i, i]
         U16 = ctypes.POINTER(ctypes.c_uint16)
         L.gdn_oracle_bf16_value.argtypes = [ctypes.c_uint16]
         L.gdn_oracle_bf16_value.restype = d
@@ -89,14 +89,16 @@ def softplus(x: float) -> float:
     return lib().gdn_oracle_softplus(float(x))
 
 
-def conv_silu_norm(geom, qkv, conv_w, eps, conv_state):
-    """qkv [T][C], conv_w [C][d], conv_state [C][d-1] -> (h [T][C], new conv_state)."""
+def conv_silu_norm(geom, qkv, conv_w, eps, conv_state, scale_q: bool = True):
+    """qkv [T][C], conv_w [C][d], conv_state [C][d-1] -> (h [T][C], new conv_state).
+    scale_q=False leaves q unit-norm (the 1/sqrt(S) then goes on the readout)."""
     qkv, conv_w = _f64(qkv), _f64(conv_w)
     cs = _f64(conv_state).copy()
     T = qkv.shape[0]
     h = np.zeros_like(qkv)
     _check(lib().gdn_oracle_conv_silu_norm(geom.h_k, geom.h_v, geom.s, geom.d_conv, T, _p(qkv),
-                                           _p(conv_w), float(eps), _p(cs), _p(h)), "conv_silu_norm")
+                                           _p(conv_w), float(eps), _p(cs), _p(h), int(bool(scale_q))),
+           "conv_silu_norm")
     return h, cs
 
 
@@ -111,30 +113,34 @@ def beta_gate(alpha, beta_logit, dt, ssm_a):
     return beta, gate
 
 
-def delta_rule(geom, h, beta, gate, state):
-    """h [T][C], beta/gate [T][h_v], state [h_v][s][s] -> (o [T][h_v][s], new state)."""
+def delta_rule(geom, h, beta, gate, state, o_scale: float = 1.0):
+    """h [T][C], beta/gate [T][h_v], state [h_v][s][s] -> (o [T][h_v][s], new state);
+    o is multiplied by o_scale after the readout."""
     h, beta, gate = _f64(h), _f64(beta), _f64(gate)
     st = _f64(state).copy()
     T = h.shape[0]
     o = np.zeros((T, geom.h_v, geom.s))
     _check(lib().gdn_oracle_delta_rule(geom.h_k, geom.h_v, geom.s, T, _p(h), _p(beta), _p(gate),
-                                       _p(st), _p(o)), "delta_rule")
+                                       _p(st), _p(o), float(o_scale)), "delta_rule")
     return o, st
 
 
-def gated_rmsnorm(o, z, w, eps):
-    """o, z [rows][s], w [s] -> y [rows][s]."""
+def gated_rmsnorm(o, z, w, eps, gate_silu: bool = False):
+    """o, z [rows][s], w [s] -> y [rows][s]; gate_silu: z * sigmoid(z) instead of sigmoid(z)."""
     o, z, w = _f64(o), _f64(z), _f64(w)
     s = o.shape[-1]
     rows = o.size // s
     y = np.zeros_like(o)
-    _check(lib().gdn_oracle_gated_rmsnorm(rows, s, _p(o), _p(z), _p(w), float(eps), _p(y)),
+    _check(lib().gdn_oracle_gated_rmsnorm(rows, s, _p(o), _p(z), _p(w), float(eps), _p(y), int(bool(gate_silu))),
            "gated_rmsnorm")
     return y
 
 
-def mixer(geom, qkv, conv_w, alpha, beta_logit, dt, ssm_a, z, norm_w, eps, conv_state, state):
-    """Whole mixer for one sequence over T tokens; returns dict(h, o, y, state, conv_state)."""
+def mixer(geom, qkv, conv_w, alpha, beta_logit, dt, ssm_a, z, norm_w, eps, conv_state, state,
+          gate_silu: bool = False, scale_after_readout: bool = False):
+    """Whole mixer for one sequence over T tokens; returns dict(h, o, y, state, conv_state).
+    gate_silu / scale_after_readout select the two variants (SiLU output gate; 1/sqrt(S)
+    on the readout instead of on q)."""
     qkv, conv_w, alpha, beta_logit, dt, ssm_a, z, norm_w = map(
         _f64, (qkv, conv_w, alpha, beta_logit, dt, ssm_a, z, norm_w))
     cs = _f64(conv_state).copy()
@@ -146,7 +152,8 @@ def mixer(geom, qkv, conv_w, alpha, beta_logit, dt, ssm_a, z, norm_w, eps, conv_
     scratch = np.zeros(2 * geom.h_v)
     _check(lib().gdn_oracle_mixer(geom.h_k, geom.h_v, geom.s, geom.d_conv, T, _p(qkv), _p(conv_w),
                                   _p(alpha), _p(beta_logit), _p(dt), _p(ssm_a), _p(z), _p(norm_w),
-                                  float(eps), _p(cs), _p(st), _p(h), _p(o), _p(y), _p(scratch)),
+                                  float(eps), _p(cs), _p(st), _p(h), _p(o), _p(y), _p(scratch),
+                                  int(bool(gate_silu)), int(bool(scale_after_readout))),
            "mixer")
     return {"h": h, "o": o, "y": y, "state": st, "conv_state": cs}
 
@@ -198,14 +205,17 @@ def project(x, w_bits, threads: Optional[int] = None):
 
 
 def run_sequence(wl, b: int, t0: int = 0, t1: Optional[int] = None, state=None, conv_state=None):
-    """Advance sequence b of a workload over its tokens [t0, t1) (clipped to its token count)."""
+    """Advance sequence b of a workload over its tokens [t0, t1) (clipped to its token count),
+    in the workload's model variant (wl.gate_silu, wl.scale_after_readout)."""
     n = wl.tokens_of(b)
     t1 = n if t1 is None else min(t1, n)
     slot = int(wl.slots[b])
     st0 = wl.state[slot] if state is None else state
     cs0 = wl.conv_state[slot] if conv_state is None else conv_state
     return mixer(wl.geom, wl.qkv[b, t0:t1], wl.conv_w, wl.alpha[b, t0:t1], wl.beta_logit[b, t0:t1],
-                 wl.dt, wl.ssm_a, wl.z[b, t0:t1], wl.norm_w, wl.eps, cs0, st0)
+                 wl.dt, wl.ssm_a, wl.z[b, t0:t1], wl.norm_w, wl.eps, cs0, st0,
+                 gate_silu=getattr(wl, "gate_silu", False),
+                 scale_after_readout=getattr(wl, "scale_after_readout", False))
 
 
 def run_workload(wl, seqs: Optional[Iterable[int]] = None, threads: Optional[int] = None):

@@ -16,6 +16,13 @@
  *   gate = softplus(alpha + dt) * ssm_a -> recurrent step ->
  *   y = rms_norm(o, ssm_norm) * sigmoid(z)   (sigmoid, not SiLU)
  *
+ * Two variants the pages name are options of the functions below: an output gate
+ * z * sigmoid(z) (SiLU), which the docstring on the layer.hpp page gives for an
+ * earlier model of the family, and the 1/sqrt(S) applied to the readout o instead
+ * of to q (step 4 of gdn_layer: the legacy recurrence consumes a prescaled q, the
+ * pinned CUDA path scales after the readout dot).  The recurrence is linear in q,
+ * so both placements give the same o up to rounding.
+ *
  * The recurrent step is the gated delta rule on each value head's S x S state
  * (row = key index r, column = value index c):
  *   S <- exp(g) * S;  m = S^T k;  S <- S + k (beta (v - m))^T;  o = S^T q.
@@ -71,10 +78,12 @@ double gdn_oracle_softplus(double x) { return softplus(x); }
  *   conv_w     [C][d_conv]
  *   conv_state [C][d_conv-1]   in/out: the last d_conv-1 raw inputs, oldest first
  *   h          [T][C]          out: q/sqrt(s) (normalised) | k (normalised) | silu(v)
+ *   scale_q    1: q gets the extra 1/sqrt(s) here; 0: q is left unit-norm (the
+ *              readout is scaled instead, gdn_oracle_delta_rule's o_scale)
  */
 int gdn_oracle_conv_silu_norm(int h_k, int h_v, int s, int d_conv, int T,
                               const double* qkv, const double* conv_w, double eps,
-                              double* conv_state, double* h) {
+                              double* conv_state, double* h, int scale_q) {
     if (!geom_ok(h_k, h_v, s, d_conv) || T < 0 || !qkv || !conv_w || !conv_state || !h)
         return GDN_ORACLE_BAD_ARG;
     const int64_t C = (int64_t) (2 * h_k + h_v) * s;
@@ -106,8 +115,10 @@ int gdn_oracle_conv_silu_norm(int h_k, int h_v, int s, int d_conv, int T,
             }
         }
         /* the extra 1/sqrt(S) on q, applied after its norm */
-        const double qscale = 1.0 / sqrt((double) s);
-        for (int64_t e = 0; e < (int64_t) h_k * s; ++e) out[e] *= qscale;
+        if (scale_q) {
+            const double qscale = 1.0 / sqrt((double) s);
+            for (int64_t e = 0; e < (int64_t) h_k * s; ++e) out[e] *= qscale;
+        }
     }
     return GDN_ORACLE_OK;
 }
@@ -142,10 +153,12 @@ int gdn_oracle_beta_gate(int h_v, int T, const double* alpha, const double* beta
  *   h     [T][C]        q | k | v as produced by gdn_oracle_conv_silu_norm
  *   beta, gate [T][h_v]
  *   state [h_v][s][s]   in/out
- *   o     [T][h_v][s]   out
+ *   o     [T][h_v][s]   out, multiplied by o_scale after the readout (1 when q
+ *                       already carries the 1/sqrt(s); 1/sqrt(s) when it does not)
  */
 int gdn_oracle_delta_rule(int h_k, int h_v, int s, int T, const double* h,
-                          const double* beta, const double* gate, double* state, double* o) {
+                          const double* beta, const double* gate, double* state, double* o,
+                          double o_scale) {
     if (!geom_ok(h_k, h_v, s, 1) || T < 0 || !h || !beta || !gate || !state || !o)
         return GDN_ORACLE_BAD_ARG;
     const int64_t C = (int64_t) (2 * h_k + h_v) * s;
@@ -177,7 +190,7 @@ int gdn_oracle_delta_rule(int h_k, int h_v, int s, int T, const double* h,
             for (int c = 0; c < s; ++c) {
                 double acc = 0.0;
                 for (int r = 0; r < s; ++r) acc += St[(int64_t) r * s + c] * q[r];
-                out[c] = acc;
+                out[c] = acc * o_scale;
             }
         }
     }
@@ -185,11 +198,12 @@ int gdn_oracle_delta_rule(int h_k, int h_v, int s, int T, const double* h,
 }
 
 /*
- * Step 7 of gdn_layer: y = rms_norm(o, w) * sigmoid(z), per row of s values.
+ * Step 7 of gdn_layer: y = rms_norm(o, w) * sigmoid(z), per row of s values; with
+ * gate_silu the gate is z * sigmoid(z) (the earlier model's SiLU).
  *   o, z, y [rows][s];  w [s]
  */
 int gdn_oracle_gated_rmsnorm(int64_t rows, int s, const double* o, const double* z,
-                             const double* w, double eps, double* y) {
+                             const double* w, double eps, double* y, int gate_silu) {
     if (rows < 0 || s <= 0 || !o || !z || !w || !y) return GDN_ORACLE_BAD_ARG;
     for (int64_t r = 0; r < rows; ++r) {
         const double* x = o + r * s;
@@ -197,7 +211,11 @@ int gdn_oracle_gated_rmsnorm(int64_t rows, int s, const double* o, const double*
         for (int c = 0; c < s; ++c) ms += x[c] * x[c];
         ms /= (double) s;
         const double inv = 1.0 / sqrt(ms + eps);
-        for (int c = 0; c < s; ++c) y[r * s + c] = x[c] * inv * w[c] * sigmoid(z[r * s + c]);
+        for (int c = 0; c < s; ++c) {
+            const double zz = z[r * s + c];
+            const double g = gate_silu ? zz * sigmoid(zz) : sigmoid(zz);
+            y[r * s + c] = x[c] * inv * w[c] * g;
+        }
     }
     return GDN_ORACLE_OK;
 }
@@ -210,13 +228,14 @@ int gdn_oracle_gated_rmsnorm(int64_t rows, int s, const double* o, const double*
  *   conv_state [C][d_conv-1] and state [h_v][s][s] in/out
  *   h [T][C], o [T][h_v][s], y [T][h_v*s] out
  * scratch: 2*h_v doubles (beta and gate of one token).
+ * gate_silu: the SiLU output gate; scale_after_readout: 1/sqrt(s) on o, not on q.
  */
 int gdn_oracle_mixer(int h_k, int h_v, int s, int d_conv, int T,
                      const double* qkv, const double* conv_w, const double* alpha,
                      const double* beta_logit, const double* dt, const double* ssm_a,
                      const double* z, const double* norm_w, double eps,
                      double* conv_state, double* state, double* h, double* o, double* y,
-                     double* scratch) {
+                     double* scratch, int gate_silu, int scale_after_readout) {
     if (!geom_ok(h_k, h_v, s, d_conv) || T < 0 || !scratch) return GDN_ORACLE_BAD_ARG;
     const int64_t C = (int64_t) (2 * h_k + h_v) * s;
     const int64_t V = (int64_t) h_v * s;
@@ -224,14 +243,15 @@ int gdn_oracle_mixer(int h_k, int h_v, int s, int d_conv, int T,
     double* gate = scratch + h_v;
     for (int t = 0; t < T; ++t) {
         int rc = gdn_oracle_conv_silu_norm(h_k, h_v, s, d_conv, 1, qkv + t * C, conv_w, eps,
-                                           conv_state, h + t * C);
+                                           conv_state, h + t * C, !scale_after_readout);
         if (rc) return rc;
         rc = gdn_oracle_beta_gate(h_v, 1, alpha + (int64_t) t * h_v, beta_logit + (int64_t) t * h_v,
                                   dt, ssm_a, beta, gate);
         if (rc) return rc;
-        rc = gdn_oracle_delta_rule(h_k, h_v, s, 1, h + t * C, beta, gate, state, o + t * V);
+        rc = gdn_oracle_delta_rule(h_k, h_v, s, 1, h + t * C, beta, gate, state, o + t * V,
+                                   scale_after_readout ? 1.0 / sqrt((double) s) : 1.0);
         if (rc) return rc;
-        rc = gdn_oracle_gated_rmsnorm(h_v, s, o + t * V, z + t * V, norm_w, eps, y + t * V);
+        rc = gdn_oracle_gated_rmsnorm(h_v, s, o + t * V, z + t * V, norm_w, eps, y + t * V, gate_silu);
         if (rc) return rc;
     }
     return GDN_ORACLE_OK;

@@ -413,3 +413,34 @@ def test_project_matches_numpy_and_hand_example():
     xr, wr = W.make_proj(7, 64, 40, seed=33)
     dec = (wr.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
     np.testing.assert_allclose(oracle.project(xr, wr, threads=3), xr.astype(np.float64) @ dec.T, rtol=1e-12, atol=1e-12)
+
+
+def test_silu_gate_closed_forms():
+    """The earlier model's output gate is SiLU, z * sigmoid(z): zero at z = 0, (3/4) ln 3 at
+    z = ln 3 (sigmoid(ln 3) = 3/4), and z itself to 1e-17 at z = 40; the norm part is
+    unchanged: o = (3, 4) has mean square 12.5."""
+    o = np.array([[3.0, 4.0], [3.0, 4.0]])
+    w = np.array([1.0, 2.0])
+    z = np.array([[0.0, np.log(3.0)], [40.0, -40.0]])
+    y = oracle.gated_rmsnorm(o, z, w, 0.0, gate_silu=True)
+    inv = 1.0 / np.sqrt(12.5)
+    np.testing.assert_allclose(y[0], [0.0, 4.0 * inv * 2.0 * 0.75 * np.log(3.0)], rtol=1e-15, atol=0)
+    np.testing.assert_allclose(y[1], [3.0 * inv * 40.0, 0.0], rtol=1e-15, atol=1e-15)
+    ys = oracle.gated_rmsnorm(o, z, w, 0.0)
+    np.testing.assert_allclose(ys[0], [3.0 * inv * 0.5, 4.0 * inv * 2.0 * 0.75], rtol=1e-15)
+
+
+def test_readout_scale_placement_is_the_same_mixer():
+    """1/sqrt(S) on the readout instead of on q: q in h is unit-norm (sqrt(S) times the
+    default's), and o, y and the state agree with the default to rounding, because the
+    recurrence is linear in q and q does not enter the state."""
+    wl = W.make("v", 2, 5, seed=41, geom=W.Geom(h_k=2, h_v=4, s=16), state_std=0.02, conv_std=1.0)
+    a = oracle.run_sequence(wl, 1)
+    wl.scale_after_readout = True
+    b = oracle.run_sequence(wl, 1)
+    qn = wl.geom.h_k * wl.geom.s
+    np.testing.assert_allclose(b["h"][:, :qn], a["h"][:, :qn] * np.sqrt(wl.geom.s), rtol=1e-14)
+    np.testing.assert_array_equal(b["h"][:, qn:], a["h"][:, qn:])
+    for key in ("o", "y", "state", "conv_state"):
+        np.testing.assert_allclose(b[key], a[key], rtol=1e-12, atol=1e-14 * np.abs(a[key]).max())
+    assert np.abs(b["o"]).max() > 0.1
