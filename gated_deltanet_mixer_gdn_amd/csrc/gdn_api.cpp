@@ -63,6 +63,9 @@ int check_geom(const gdn_geom* g, const char* fn) {
                     g->h_k, g->h_v, g->s, g->d_conv);
     if (g->h_v % g->h_k != 0)
         return fail(GDN_ERR_ARG, fn, "h_v=%d is not a multiple of h_k=%d", g->h_v, g->h_k);
+    if ((g->gate_silu != 0 && g->gate_silu != 1) || (g->scale_after_readout != 0 && g->scale_after_readout != 1))
+        return fail(GDN_ERR_ARG, fn, "geometry flags gate_silu=%d, scale_after_readout=%d must be 0 or 1",
+                    g->gate_silu, g->scale_after_readout);
     if (g->s != gdn::kS || g->d_conv != gdn::kDConv)
         return fail(GDN_ERR_UNSUPPORTED, fn, "the kernels are built for s=%d, d_conv=%d (got s=%d, d_conv=%d)",
                     gdn::kS, gdn::kDConv, g->s, g->d_conv);
@@ -240,7 +243,7 @@ int conv_common(const char* fn, gdn_pool* p, const int32_t* slots, const int32_t
     c.n_tb = n_tb;
     c.persist = persist ? 1 : 0;
     c.eps = eps;
-    c.qscale = 1.0f / std::sqrt((float) p->g.s);
+    c.qscale = p->g.scale_after_readout ? 1.0f : 1.0f / std::sqrt((float) p->g.s);
     return launched(gdn::launch_conv_silu_norm(c, static_cast<hipStream_t>(stream)), fn);
 }
 
@@ -306,7 +309,9 @@ int decode_common(const char* fn, gdn_pool* p, const int32_t* slots, const int32
     s.h_v = p->g.h_v;
     s.group = p->g.h_v / p->g.h_k;
     s.persist = persist ? 1 : 0;
+    s.gate_silu = p->g.gate_silu;
     s.eps = eps;
+    s.oscale = p->g.scale_after_readout ? 1.0f / std::sqrt((float) p->g.s) : 1.0f;
     return launched(gdn::launch_decode_step(s, static_cast<hipStream_t>(stream)), fn);
 }
 
@@ -419,7 +424,9 @@ int gdn_decode_fused(gdn_pool* p, const int32_t* slots, int32_t B, const float* 
     f.h_v = p->g.h_v;
     f.group = group;
     f.eps = eps;
-    f.qscale = 1.0f / std::sqrt((float) p->g.s);
+    f.gate_silu = p->g.gate_silu;
+    f.qscale = p->g.scale_after_readout ? 1.0f : 1.0f / std::sqrt((float) p->g.s);
+    f.oscale = p->g.scale_after_readout ? 1.0f / std::sqrt((float) p->g.s) : 1.0f;
     return launched(gdn::launch_decode_fused(f, static_cast<hipStream_t>(stream)), fn);
 }
 
@@ -551,8 +558,9 @@ int gdn_project2_bf16(const uint16_t* xs, const uint16_t* wp, int64_t rows, int3
 }
 
 int gdn_gated_rmsnorm(const float* o, const float* z, const float* w, float eps, int64_t rows, int32_t s,
-                      float* y, void* stream) {
+                      int32_t gate_silu, float* y, void* stream) {
     const char* fn = "gdn_gated_rmsnorm";
+    if (gate_silu != 0 && gate_silu != 1) return fail(GDN_ERR_ARG, fn, "gate_silu=%d must be 0 or 1", gate_silu);
     if (rows < 0) return fail(GDN_ERR_ARG, fn, "rows=%lld is negative", (long long) rows);
     if (s != gdn::kS) return fail(GDN_ERR_UNSUPPORTED, fn, "s=%d: the kernel is built for s=%d", s, gdn::kS);
     if (!(eps >= 0.0f) || !std::isfinite(eps)) return fail(GDN_ERR_ARG, fn, "eps must be finite and >= 0");
@@ -573,6 +581,7 @@ int gdn_gated_rmsnorm(const float* o, const float* z, const float* w, float eps,
     np.y = y;
     np.rows = (long long) rows;
     np.eps = eps;
+    np.gate_silu = gate_silu;
     return launched(gdn::launch_gated_rmsnorm(np, static_cast<hipStream_t>(stream)), fn);
 }
 

@@ -45,6 +45,13 @@ __device__ __forceinline__ f4 sigmoid4(f4 x) {
     return f4{sigmoid_f(x.x), sigmoid_f(x.y), sigmoid_f(x.z), sigmoid_f(x.w)};
 }
 
+// output gate of the gated RMSNorm: sigmoid(z), or z * sigmoid(z) (SiLU, the earlier
+// model of the family); silu is uniform over the launch
+__device__ __forceinline__ f4 gate4(f4 z, int silu) {
+    const f4 g = sigmoid4(z);
+    return silu ? z * g : g;
+}
+
 // Explicit fused multiply-adds: both recurrence kernels spell out the same operation
 // sequence so that a T-token call reproduces T single-token calls bit for bit.
 __device__ __forceinline__ f4 fma4(f4 a, f4 b, f4 c) {

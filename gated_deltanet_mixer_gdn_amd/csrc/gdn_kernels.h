@@ -53,7 +53,9 @@ struct StepParams {
     long long n_slots;
     int B, T, h_k, h_v, group;  // group = h_v / h_k
     int persist;            // 0: leave the state untouched (speculative window)
+    int gate_silu;          // epilogue gate: 0 sigmoid(z), 1 z * sigmoid(z)
     float eps;              // RMSNorm epsilon (epilogue only)
+    float oscale;           // multiplies the readout o (1, or 1/sqrt(S) when q is unscaled)
 };
 
 // Largest GQA group (h_v / h_k) the single-launch decode supports: the conv prologue
@@ -77,7 +79,8 @@ struct FusedParams {
     uint32_t* flags;
     long long n_slots;
     int B, h_k, h_v, group;
-    float eps, qscale;
+    int gate_silu;
+    float eps, qscale, oscale;
 };
 
 struct NormParams {
@@ -87,6 +90,7 @@ struct NormParams {
     float* y;
     long long rows;
     float eps;
+    int gate_silu;
 };
 
 struct ZeroParams {

@@ -15,7 +15,7 @@ __global__ __launch_bounds__(256) void gated_rmsnorm_kernel(NormParams p) {
     const f4 w = *(const f4*) (p.w + 4 * l);
     const float ss = halfwave_sum(sumsq4(x));
     const float inv = rms_inv(ss, p.eps);
-    *(f4*) (p.y + off) = x * inv * w * sigmoid4(z);
+    *(f4*) (p.y + off) = x * inv * w * gate4(z, p.gate_silu);
 }
 
 // ------------------------------------------------------------------ launch

@@ -48,10 +48,13 @@ struct HeadReduce {
 // head and write o (if o_row) and the gated RMSNorm y (if kNorm); s[] becomes the new
 // state.  The operation sequence is the multi-token kernel's, so the two agree bit
 // for bit.
+// oscale multiplies o after the readout (1 unless the 1/sqrt(S) is applied there
+// rather than to q); gate_silu picks the epilogue's gate.
 template <bool kNorm>
 __device__ __forceinline__ void head_token_256(f4 (&s)[16], const f4* qk, f4 v, float beta, float eg,
                                                HeadReduce& red, float* o_row, const float* z_row,
-                                               const float* norm_w, float* y_row, float eps) {
+                                               const float* norm_w, float* y_row, float eps, float oscale,
+                                               int gate_silu) {
     const int tid = threadIdx.x;
     const int cg = tid & 31;
     const int rg = tid >> 5;
@@ -85,7 +88,8 @@ __device__ __forceinline__ void head_token_256(f4 (&s)[16], const f4* qk, f4 v, 
     const float KQ = (red.kq[0] + red.kq[1]) + (red.kq[2] + red.kq[3]);
     const f4 d = beta * fma4(-eg, PK, v);
     if (rg == 0) {
-        const f4 out = fma4(KQ, d, eg * PQ);
+        f4 out = fma4(KQ, d, eg * PQ);
+        if (oscale != 1.0f) out *= oscale;
         if (o_row) *(f4*) (o_row + cg * 4) = out;
         if (kNorm) {
             // sum of o^2: 8-lane (32-column) blocks first, then ((b0+b1)+(b2+b3))
@@ -93,7 +97,7 @@ __device__ __forceinline__ void head_token_256(f4 (&s)[16], const f4* qk, f4 v, 
             const float inv = rms_inv(ss, eps);
             const f4 zz = *(const f4*) (z_row + cg * 4);
             const f4 wn = *(const f4*) (norm_w + cg * 4);
-            *(f4*) (y_row + cg * 4) = out * inv * wn * sigmoid4(zz);
+            *(f4*) (y_row + cg * 4) = out * inv * wn * gate4(zz, gate_silu);
         }
     }
 #pragma unroll
@@ -150,7 +154,8 @@ __global__ __launch_bounds__(256) void decode_one_kernel(StepParams p) {
     __syncthreads();
 
     head_token_256<kNorm>(s, qk_lds, v, beta, eg, red, p.o ? p.o + e * kS : nullptr,
-                          kNorm ? p.z + e * kS : nullptr, p.norm_w, kNorm ? p.y + e * kS : nullptr, p.eps);
+                          kNorm ? p.z + e * kS : nullptr, p.norm_w, kNorm ? p.y + e * kS : nullptr, p.eps,
+                          p.oscale, p.gate_silu);
     if (p.persist) store_tile(s, tile);
 }
 
@@ -238,7 +243,7 @@ __global__ __launch_bounds__(256) void decode_fused_kernel(FusedParams p) {
         const float beta = sigmoid_f(p.beta_logit[e]);
         const float eg = expf(softplus_f(p.alpha[e] + p.dt[i]) * p.ssm_a[i]);
         head_token_256<true>(s, qk_lds, v_lds[n][cg], beta, eg, red[n & 1], nullptr, p.z + e * kS, p.norm_w,
-                             p.y + e * kS, p.eps);
+                             p.y + e * kS, p.eps, p.oscale, p.gate_silu);
         store_tile(s, tile);
     }
 }
@@ -347,7 +352,8 @@ __global__ __launch_bounds__(256) void decode_multi_kernel(StepParams p) {
         pq = add_xor32(add_xor16(add_xor8(pq)));
         kq = add_xor32(add_xor16(add_xor8(kq)));
         const f4 d = beta * fma4(-eg, pk, v);
-        const f4 out = fma4(kq, d, eg * pq);
+        f4 out = fma4(kq, d, eg * pq);
+        if (p.oscale != 1.0f) out *= p.oscale;
         if (p.o && rg == 0) *(f4*) (p.o + ((tok0 + t) * p.h_v + i) * kS + col) = out;
         if (kNorm) {
             const int par = (t / kNormChunk) & 1;
@@ -367,7 +373,7 @@ __global__ __launch_bounds__(256) void decode_multi_kernel(StepParams p) {
                     const float inv = rms_inv(tot, p.eps);
                     const f4 wn = *(const f4*) (p.norm_w + n_c4);
                     *(f4*) (p.y + ((tok0 + t0c + n_tt) * p.h_v + i) * kS + n_c4) =
-                        o_ring[par][n_tt][n_c4 / 4] * inv * wn * sigmoid4(zz);
+                        o_ring[par][n_tt][n_c4 / 4] * inv * wn * gate4(zz, p.gate_silu);
                 }
             }
         }

@@ -35,23 +35,27 @@ class GdnError(RuntimeError):
 
 class gdn_geom(ctypes.Structure):
     _fields_ = [("h_k", ctypes.c_int32), ("h_v", ctypes.c_int32), ("s", ctypes.c_int32),
-                ("d_conv", ctypes.c_int32)]
+                ("d_conv", ctypes.c_int32), ("gate_silu", ctypes.c_int32), ("scale_after_readout", ctypes.c_int32)]
 
 
 @dataclass(frozen=True)
 class Geom:
-    """GDN geometry; the defaults are the pages' model (16 qk heads, 48 value heads)."""
+    """GDN geometry; the defaults are the pages' model (16 qk heads, 48 value heads,
+    sigmoid output gate, 1/sqrt(S) on q).  gate_silu: the earlier model's SiLU gate;
+    scale_after_readout: the 1/sqrt(S) on the readout o instead of on q."""
     h_k: int = 16
     h_v: int = 48
     s: int = 128
     d_conv: int = 4
+    gate_silu: bool = False
+    scale_after_readout: bool = False
 
     @property
     def channels(self) -> int:
         return (2 * self.h_k + self.h_v) * self.s
 
     def c(self) -> gdn_geom:
-        return gdn_geom(self.h_k, self.h_v, self.s, self.d_conv)
+        return gdn_geom(self.h_k, self.h_v, self.s, self.d_conv, int(self.gate_silu), int(self.scale_after_readout))
 
 
 _lib = None
@@ -88,7 +92,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "gdn_verify_window": ([vp, vp, vp, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, f32, vp, vp, vp],
                               ctypes.c_int),
         "gdn_commit": ([vp, vp, vp, i32, i32, vp, vp, vp, vp, vp, vp, vp], ctypes.c_int),
-        "gdn_gated_rmsnorm": ([vp, vp, vp, f32, i64, i32, vp, vp], ctypes.c_int),
+        "gdn_gated_rmsnorm": ([vp, vp, vp, f32, i64, i32, i32, vp, vp], ctypes.c_int),
         "gdn_ab_project": ([vp, vp, vp, i64, i32, i32, vp, vp, vp], ctypes.c_int),
         "gdn_split_bf16_bytes": ([i64, i32], ctypes.c_int64),
         "gdn_pack_bf16_bytes": ([i32, i32], ctypes.c_int64),
@@ -276,15 +280,16 @@ def gdn_commit(pool: StatePool, qkv, h, alpha, beta_logit, dt, ssm_a, n_keep=Non
                                      *ptrs, _stream(qkv)))
 
 
-def gdn_gated_rmsnorm(o, z, w, eps: float, y):
-    """o, z, y: any contiguous float32 layout whose last axis is s = 128 rows; w [s]."""
+def gdn_gated_rmsnorm(o, z, w, eps: float, y, gate_silu: bool = False):
+    """o, z, y: any contiguous float32 layout whose last axis is s = 128 rows; w [s].
+    gate_silu: z * sigmoid(z) as the gate instead of sigmoid(z)."""
     s = w.shape[-1]
     rows = o.numel() // s
     ptrs = (_f32(o, "o"), _f32(z, "z"), _f32(w, "w", (s,)), _f32(y, "y"))
     if z.numel() != o.numel() or y.numel() != o.numel():
         raise ValueError("o, z and y must hold the same number of elements")
-    _check(load_library().gdn_gated_rmsnorm(ptrs[0], ptrs[1], ptrs[2], float(eps), rows, s, ptrs[3],
-                                            _stream(o)))
+    _check(load_library().gdn_gated_rmsnorm(ptrs[0], ptrs[1], ptrs[2], float(eps), rows, s, int(bool(gate_silu)),
+                                            ptrs[3], _stream(o)))
 
 
 def gdn_mixer(pool: StatePool, qkv, alpha, beta_logit, z, conv_w, dt, ssm_a, norm_w, eps: float,
@@ -296,7 +301,7 @@ def gdn_mixer(pool: StatePool, qkv, alpha, beta_logit, z, conv_w, dt, ssm_a, nor
         gdn_decode_step_norm(pool, h, alpha, beta_logit, dt, ssm_a, z, norm_w, eps, y, o, slots, n_tok)
     else:
         gdn_decode_step(pool, h, alpha, beta_logit, dt, ssm_a, o, slots, n_tok)
-        gdn_gated_rmsnorm(o, z, norm_w, eps, y)
+        gdn_gated_rmsnorm(o, z, norm_w, eps, y, gate_silu=pool.geom.gate_silu)
 
 
 def gdn_ab_project(x, w_alpha, w_beta, alpha, beta_logit):

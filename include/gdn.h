@@ -13,7 +13,8 @@
  *                       * ssm_a, then the gated delta rule on each value head's
  *                       S x S fp32 state; T >= 1 tokens per call, state held
  *                       on chip across the tokens of one call
- *   gdn_gated_rmsnorm   y = rms_norm(o) * w * sigmoid(z)   (sigmoid, not SiLU)
+ *   gdn_gated_rmsnorm   y = rms_norm(o) * w * sigmoid(z)   (sigmoid, not SiLU; the
+ *                       SiLU gate of an earlier model is a geometry option)
  *
  * States live in a pool of slots carved from caller-provided device memory (the
  * pattern of `gdn_buffers_bytes` / `gdn_buffers_init` / `gdn_buffers_zero_state`
@@ -52,7 +53,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 1
+#define GDN_ABI_VERSION 2
 
 enum {
     GDN_OK = 0,
@@ -66,12 +67,22 @@ enum {
 #define GDN_FLAG_BAD_NTOK 0x2u  /* a token count was outside [0, T]: it was clamped */
 
 /* GDN geometry: qk heads, value heads, head size S, conv width.  The value head i
- * reads qk head i / (h_v / h_k).  Channels C = (2*h_k + h_v) * s: q | k | v. */
+ * reads qk head i / (h_v / h_k).  Channels C = (2*h_k + h_v) * s: q | k | v.
+ * Two model options (0 or 1; zero-initialised = the pages' model):
+ *   gate_silu            the gated RMSNorm's gate is z * sigmoid(z) (SiLU) instead of
+ *                        sigmoid(z): the layer.hpp docstring gives SiLU for an earlier
+ *                        model of the family and sigmoid for this one;
+ *   scale_after_readout  the extra 1/sqrt(S) multiplies the readout o instead of q
+ *                        (step 4 of gdn_layer: the legacy recurrence consumes a
+ *                        prescaled q, the pinned CUDA path scales after the readout
+ *                        dot); h then carries the unit-norm q.  Same o up to rounding. */
 typedef struct gdn_geom {
     int32_t h_k;
     int32_t h_v;
     int32_t s;
     int32_t d_conv;
+    int32_t gate_silu;
+    int32_t scale_after_readout;
 } gdn_geom;
 
 /* Opaque host-side descriptor of a state pool.  It owns no device memory. */
@@ -125,6 +136,8 @@ int gdn_state_pool_zero(gdn_pool* p, const int32_t* slots, int32_t n, void* stre
  *   u = sum_{j<3} conv_w[c][j] * X[c][j] + conv_w[c][3] * qkv[c],  X rolled with the raw qkv,
  *   h = u * sigmoid(u)                        (all C channels, before the split)
  *   q heads (channels [0, h_k*s)):       h / sqrt(|h|^2 + eps) / sqrt(s)
+ *                                        (without the / sqrt(s) when the pool's
+ *                                        geometry has scale_after_readout)
  *   k heads (channels [h_k*s, 2*h_k*s)): h / sqrt(|h|^2 + eps)
  *   v (channels [2*h_k*s, C)):           unchanged
  * slots  int32 [B]          pool slot of each sequence (NULL: slot b for sequence b)
@@ -142,7 +155,8 @@ int gdn_conv_silu_norm(gdn_pool* p, const int32_t* slots, const int32_t* n_tok, 
  *   beta = sigmoid(beta_logit), g = softplus(alpha + dt[i]) * ssm_a[i]
  *   S <- exp(g) S;  m = S^T k;  S <- S + k (beta (v - m))^T;  o = S^T q
  * for every value head i with q, k of qk head i / (h_v/h_k), taken from h as
- * produced by gdn_conv_silu_norm (q already carries its 1/sqrt(s)).
+ * produced by gdn_conv_silu_norm (q already carries its 1/sqrt(s); with the
+ * geometry's scale_after_readout it does not, and o is multiplied by 1/sqrt(s)).
  * slots, n_tok  as above; tokens t >= n_tok[b] leave the state alone and write o = 0
  * h        [B][T][C];  alpha, beta_logit [B][T][h_v];  dt, ssm_a [h_v]
  * o        [B][T][h_v][s]   output
@@ -155,7 +169,8 @@ int gdn_decode_step(gdn_pool* p, const int32_t* slots, const int32_t* n_tok, int
  * the pages' engine fuses its step and output norm (`fused_gdn_step_norm`, step 7 of
  * gdn_layer).  Same arguments as gdn_decode_step plus
  * z       [B][T][h_v*s]   gate input;  norm_w [s];  eps (>= 0)
- * y       [B][T][h_v*s]   output: rms_norm(o) * norm_w * sigmoid(z)
+ * y       [B][T][h_v*s]   output: rms_norm(o) * norm_w * sigmoid(z)  (z * sigmoid(z)
+ *                         with the geometry's gate_silu)
  * o       [B][T][h_v][s]  optional: NULL skips writing o (saves its HBM traffic)
  * y and o may not overlap each other, h, z or the pool. */
 int gdn_decode_step_norm(gdn_pool* p, const int32_t* slots, const int32_t* n_tok, int32_t B,
@@ -203,11 +218,12 @@ int gdn_commit(gdn_pool* p, const int32_t* slots, const int32_t* n_keep, int32_t
                const float* dt, const float* ssm_a, void* stream);
 
 /* Step 7 of gdn_layer: per row of s values,
- *   y = o / sqrt(mean(o^2) + eps) * w * sigmoid(z)
+ *   y = o / sqrt(mean(o^2) + eps) * w * sigmoid(z)      (gate_silu = 0)
+ *   y = o / sqrt(mean(o^2) + eps) * w * z * sigmoid(z)  (gate_silu = 1)
  * o, z, y [rows][s] (rows = B*T*h_v); w [s], shared by all rows.  s must be 128.
  * y may alias o. */
 int gdn_gated_rmsnorm(const float* o, const float* z, const float* w, float eps, int64_t rows,
-                      int32_t s, float* y, void* stream);
+                      int32_t s, int32_t gate_silu, float* y, void* stream);
 
 /* ---------------------------------------------------------------- the step before the mixer
  * The alpha / beta projections of step 5 of gdn_layer ("The weights are BF16";

@@ -38,7 +38,8 @@ class GpuMixer:
         self.G = G
         self.wl = wl
         g = wl.geom
-        self.geom = G.Geom(g.h_k, g.h_v, g.s, g.d_conv)
+        self.geom = G.Geom(g.h_k, g.h_v, g.s, g.d_conv, gate_silu=getattr(wl, "gate_silu", False),
+                           scale_after_readout=getattr(wl, "scale_after_readout", False))
         if pool is None:
             pool = G.StatePool(wl.n_slots, self.geom)
             pool.state.copy_(dev(wl.state))

@@ -59,12 +59,12 @@ def test_library_is_built_for_gfx950_only(tmp_path):
 
 
 def test_abi_version(L):
-    assert L.gdn_abi_version() == 1
+    assert L.gdn_abi_version() == 2
 
 
 def _geom(h_k=16, h_v=48, s=128, d_conv=4):
     from gated_deltanet_mixer_gdn_amd.gdn import gdn_geom
-    return gdn_geom(h_k, h_v, s, d_conv)
+    return gdn_geom(h_k, h_v, s, d_conv, 0, 0)
 
 
 def test_pool_bytes(L):
@@ -116,23 +116,39 @@ def test_calls_on_null_pool_are_rejected(L):
 
 def test_rmsnorm_argument_errors(L):
     from gated_deltanet_mixer_gdn_amd.gdn import GDN_ERR_ARG, GDN_ERR_UNSUPPORTED, GDN_OK
-    assert L.gdn_gated_rmsnorm(16, 16, 16, 1e-6, 4, 64, 16, None) == GDN_ERR_UNSUPPORTED
-    assert L.gdn_gated_rmsnorm(16, 16, 16, 1e-6, -1, 128, 16, None) == GDN_ERR_ARG
-    assert L.gdn_gated_rmsnorm(16, 16, 16, float("nan"), 4, 128, 16, None) == GDN_ERR_ARG
-    assert L.gdn_gated_rmsnorm(16, 16, 16, -1.0, 4, 128, 16, None) == GDN_ERR_ARG
-    assert L.gdn_gated_rmsnorm(None, 16, 16, 1e-6, 4, 128, 16, None) == GDN_ERR_ARG
+    assert L.gdn_gated_rmsnorm(16, 16, 16, 1e-6, 4, 64, 0, 16, None) == GDN_ERR_UNSUPPORTED
+    assert L.gdn_gated_rmsnorm(16, 16, 16, 1e-6, -1, 128, 0, 16, None) == GDN_ERR_ARG
+    assert L.gdn_gated_rmsnorm(16, 16, 16, float("nan"), 4, 128, 0, 16, None) == GDN_ERR_ARG
+    assert L.gdn_gated_rmsnorm(16, 16, 16, -1.0, 4, 128, 0, 16, None) == GDN_ERR_ARG
+    assert L.gdn_gated_rmsnorm(None, 16, 16, 1e-6, 4, 128, 0, 16, None) == GDN_ERR_ARG
     assert b"o is null" in L.gdn_last_error()
-    assert L.gdn_gated_rmsnorm(16, 16, 20, 1e-6, 4, 128, 16, None) == GDN_ERR_ARG
+    assert L.gdn_gated_rmsnorm(16, 16, 20, 1e-6, 4, 128, 0, 16, None) == GDN_ERR_ARG
     assert b"w is not 16-byte aligned" in L.gdn_last_error()
     # z and y overlapping is refused; rows = 0 is a no-op that touches nothing
-    assert L.gdn_gated_rmsnorm(4096, 1 << 20, 16, 1e-6, 4, 128, 1 << 20, None) == GDN_ERR_ARG
-    assert L.gdn_gated_rmsnorm(None, None, None, 1e-6, 0, 128, None, None) == GDN_OK
+    assert L.gdn_gated_rmsnorm(4096, 1 << 20, 16, 1e-6, 4, 128, 0, 1 << 20, None) == GDN_ERR_ARG
+    assert L.gdn_gated_rmsnorm(None, None, None, 1e-6, 0, 128, 0, None, None) == GDN_OK
     assert L.gdn_last_error() == b""
+    assert L.gdn_gated_rmsnorm(16, 16, 16, 1e-6, 4, 128, 2, 16, None) == GDN_ERR_ARG
+    assert b"gate_silu" in L.gdn_last_error()
+
+
+def test_geometry_option_flags(L):
+    """The two model options are 0 or 1; anything else is refused before any work."""
+    import ctypes
+    from gated_deltanet_mixer_gdn_amd.gdn import GDN_ERR_ARG, gdn_geom
+    for flags in ((2, 0), (0, -1)):
+        g = gdn_geom(16, 48, 128, 4, *flags)
+        assert L.gdn_state_pool_bytes(ctypes.byref(g), 4) == 0
+        p = ctypes.c_void_p()
+        assert L.gdn_state_pool_create(ctypes.byref(g), 4, 256, 1 << 30, ctypes.byref(p)) == GDN_ERR_ARG
+        assert b"must be 0 or 1" in L.gdn_last_error()
+    g = gdn_geom(16, 48, 128, 4, 1, 1)
+    assert L.gdn_state_pool_bytes(ctypes.byref(g), 4) == L.gdn_state_pool_bytes(ctypes.byref(_geom()), 4) > 0
 
 
 def test_last_error_is_thread_local(L):
     import threading
-    L.gdn_gated_rmsnorm(16, 16, 16, 1e-6, 4, 64, 16, None)
+    L.gdn_gated_rmsnorm(16, 16, 16, 1e-6, 4, 64, 0, 16, None)
     seen = []
     t = threading.Thread(target=lambda: seen.append(L.gdn_last_error()))
     t.start()

@@ -508,3 +508,59 @@ def test_ab_projection_empty_is_a_no_op():
     x = torch.empty(0, 2560, device="cuda")
     w = torch.zeros(48, 2560, dtype=torch.int16, device="cuda")
     G.gdn_ab_project(x, w, w, torch.empty(0, 48, device="cuda"), torch.empty(0, 48, device="cuda"))
+
+
+# ------------------------------------------------------------------ model variants
+VARIANTS = pytest.mark.parametrize("gate_silu,after", [(True, False), (False, True), (True, True)],
+                                   ids=["silu_gate", "scale_after_readout", "both"])
+
+
+@VARIANTS
+@DECODE_MODES
+def test_model_variants_decode(gate_silu, after, fused):
+    """The SiLU output gate and the 1/sqrt(S) on the readout (geometry options) in every
+    decode form, against the oracle in the same variant (h then holds the unit-norm q)."""
+    wl = W.make("variant", 12, 1, seed=120, state_std=0.02, conv_std=1.0)
+    wl.gate_silu, wl.scale_after_readout = gate_silu, after
+    log(f"variant silu={gate_silu} after={after} fused={fused}")
+    res = oracle.run_workload(wl)
+    gm = GpuMixer(wl)
+    gm.run(fused=fused)
+    _compare_all(gm, wl, res, STEP_TOL, "variant", keys=("y", "h") if fused == "one" else ("o", "y", "h"))
+
+
+@VARIANTS
+@FUSED
+def test_model_variants_multi_token_ragged(gate_silu, after, fused):
+    """The variants in the multi-token kernel with ragged counts (small geometry)."""
+    wl = W.make("variant_ragged", 5, 11, seed=121, geom=W.Geom(h_k=2, h_v=6), state_std=0.02, conv_std=1.0,
+                ragged_max=11)
+    wl.gate_silu, wl.scale_after_readout = gate_silu, after
+    log(f"variant ragged silu={gate_silu} after={after} fused={fused}")
+    res = oracle.run_workload(wl)
+    gm = GpuMixer(wl)
+    gm.run(fused=fused)
+    _compare_all(gm, wl, res, STEP_TOL, "variant ragged")
+
+
+@VARIANTS
+def test_model_variants_keep_the_bitwise_identities(gate_silu, after):
+    """Within a variant, the single launch equals the two calls, the fused norm equals the
+    separate norm, and a T-token call equals the same tokens one call at a time."""
+    import torch
+    wl = W.make("variant_bits", 6, 1, seed=122, geom=W.Geom(h_k=2, h_v=6), state_std=0.02, conv_std=1.0)
+    wl.gate_silu, wl.scale_after_readout = gate_silu, after
+    outs = {}
+    for mode in (False, True, "one"):
+        gm = GpuMixer(wl)
+        gm.run(fused=mode)
+        outs[mode] = (gm.y.clone(), gm.pool.state.clone())
+    assert torch.equal(outs[False][0], outs[True][0]) and torch.equal(outs[True][0], outs["one"][0])
+    assert torch.equal(outs[False][1], outs["one"][1])
+    wl2 = W.make("variant_chunks", 3, 7, seed=123, geom=W.Geom(h_k=2, h_v=6), state_std=0.02, conv_std=1.0)
+    wl2.gate_silu, wl2.scale_after_readout = gate_silu, after
+    a, b = GpuMixer(wl2), GpuMixer(wl2)
+    a.run(fused=True)
+    for t0, t1 in ((0, 1), (1, 4), (4, 7)):
+        b.run(t0, t1, fused=True)
+    assert torch.equal(a.y, b.y) and torch.equal(a.pool.state, b.pool.state)
