@@ -3,24 +3,24 @@
 
 A step is one pass of the whole mixer (conv/SiLU/L2 -> gated delta rule -> gated
 RMSNorm) over one batch: by default the bandwidth-bound decode of 256 sequences x
-1 token (768 MiB of fp32 state), inputs already in HBM.  The timed step is two
-launches, gdn_conv_silu_norm and gdn_decode_step_norm (the recurrence with the
-gated RMSNorm fused into its epilogue, writing y only), the fastest form at large
-batch.  The single-launch decode (gdn_decode_fused) and the three-call form are
-timed beside it for context.  Prints ONE JSON line on stdout; diagnostics go to
-stderr.
+1 token (768 MiB of fp32 state), inputs already in HBM.  For one token per
+sequence the timed step is the single launch gdn_decode_fused (conv, recurrence
+and gated RMSNorm, writing y only), the fastest form; the two-launch form
+(gdn_conv_silu_norm + gdn_decode_step_norm) and the three-call form are timed
+beside it for context.  Workloads with several tokens per sequence time the
+two-launch form.  Prints ONE JSON line on stdout; diagnostics go to stderr.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--config b256]
                   [--cpu-seconds S | --no-cpu-baseline] [--copy-probe-mib M]
 
 The `roofline` object is for the dominant kernel of the timed step
-(decode_one_kernel<fused norm> for the default workload): its algorithmic bytes per
+(decode_fused_par_kernel<3> for the default workload): its algorithmic bytes per
 launch over its average launch time, measured with HIP events recorded on the
 stream the kernels run on, around the kernels of every 8th step of the timed
 region.  `traffic` (HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE
 counters, scaled by a copy-kernel calibration) is read from
-profiles/decode_one_norm_b256_traffic.txt and reported only while the kernel
-sources it was measured on are unchanged.
+profiles/decode_fused_b256_traffic.txt and reported only while the kernel sources
+it was measured on are unchanged.
 """
 import argparse
 import hashlib
@@ -37,7 +37,7 @@ BF16_PEAK_TFLOPS = 2500.0         # MI355X dense bf16 matrix peak, published
 # the sources the recurrence kernel is built from (its counter record is void once they change)
 KERNEL_SRCS = [os.path.join(ROOT, "gated_deltanet_mixer_gdn_amd", "csrc", f)
                for f in ("gdn_recurrence.hip", "gdn_device.h", "gdn_kernels.h")]
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_one_norm_b256_traffic.txt")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_fused_b256_traffic.txt")
 
 
 def log(*a):
@@ -279,11 +279,15 @@ def main():
 
     three_ms, three_k, _ = timed(step_three, 4, ("conv", "step", "norm"))
     single = wl.T == 1 and wl.n_tok is None
-    one_ms, one_k = (timed(step_one, 2, ("one",))[:2]) if single else (None, None)
-    # the timed hot path: conv/SiLU/L2 + recurrence with the norm fused (two launches),
-    # the fastest form at large batch
-    ms_per_step, k_ms, n_samples = timed(step_fused, 3, ("conv", "step_norm"))
-    two_ms, two_k, dominant = ms_per_step, k_ms, "step_norm"
+    two_ms, two_k, two_n = timed(step_fused, 3, ("conv", "step_norm"))
+    # the timed hot path: the single launch for one token per sequence (the fastest
+    # form), else conv/SiLU/L2 + the recurrence with the norm fused (two launches)
+    if single:
+        one_ms, one_k, one_n = timed(step_one, 2, ("one",))
+        ms_per_step, k_ms, n_samples, dominant = one_ms, one_k, one_n, "one"
+    else:
+        one_ms = one_k = None
+        ms_per_step, k_ms, n_samples, dominant = two_ms, two_k, two_n, "step_norm"
     # context: the alpha / beta projections that feed this step (n_embd = 2560, bf16 weights)
     ab = W.make_ab(wl.B, wl.T, seed=11)
     ab_x = dev(ab.x)
@@ -327,7 +331,7 @@ def main():
     nbytes, units = algorithmic_bytes(wl)
     value = units / (ms_per_step / 1000.0)
     achieved = nbytes[dominant] / (k_ms[dominant] / 1000.0) / 1e9
-    mixer_bytes = nbytes["conv"] + nbytes["step_norm"]
+    mixer_bytes = nbytes["one"] if single else nbytes["conv"] + nbytes["step_norm"]
     mixer_gbps = mixer_bytes / (ms_per_step / 1000.0) / 1e9
     two_gbps = nbytes["step_norm"] / (two_k["step_norm"] / 1000.0) / 1e9
     three_step_gbps = nbytes["step"] / (three_k["step"] / 1000.0) / 1e9
@@ -363,14 +367,14 @@ def main():
         "config": {"workload": wl.name, "B": wl.B, "T": wl.T, "n_slots": wl.n_slots,
                    "h_k": g.h_k, "h_v": g.h_v, "S": g.s, "d_conv": g.d_conv,
                    "state_bytes": int(wl.n_slots * g.h_v * g.s * g.s * 4), "parallelism": "none"},
-        "path": "gdn_conv_silu_norm + gdn_decode_step_norm (gated RMSNorm fused, y only)",
+        "path": ("gdn_decode_fused (conv, recurrence and gated RMSNorm in one launch, y only)" if single else
+                 "gdn_conv_silu_norm + gdn_decode_step_norm (gated RMSNorm fused, y only)"),
         "hbm_gbps_mixer": mixer_gbps,
         "hbm_frac_mixer": mixer_gbps / HBM_PEAK_GBPS,
         "kernel_us": {k: v * 1000.0 for k, v in k_ms.items()},
-        "single_launch_path": (None if not single else
-                               {"ms_per_step": one_ms, "kernel_us": one_k["one"] * 1000.0,
-                                "value": units / (one_ms / 1000.0), "kernel_gbps": one_gbps,
-                                "algorithmic_bytes_per_launch": nbytes["one"]}),
+        "two_call_path": {"ms_per_step": two_ms, "kernel_us": {k: v * 1000.0 for k, v in two_k.items()},
+                          "value": units / (two_ms / 1000.0), "recurrence_kernel_gbps": two_gbps,
+                          "algorithmic_bytes_per_launch": {"conv": nbytes["conv"], "step_norm": nbytes["step_norm"]}},
         "three_call_path": {"ms_per_step": three_ms, "kernel_us": {k: v * 1000.0 for k, v in three_k.items()},
                             "value": units / (three_ms / 1000.0),
                             "recurrence_kernel_gbps": three_step_gbps},
@@ -378,7 +382,8 @@ def main():
         "ab_projection": {"us": ab_us, "algorithmic_bytes": int(ab_bytes), "gbps": ab_bytes / ab_us / 1e3,
                           "rows": wl.B * wl.T, "n_embd": W.N_EMBD},
         "projections": proj,
-        "roofline": {"kernel": "decode_one_kernel<fused norm>" if wl.T == 1 else "decode_multi_kernel<fused norm>",
+        "roofline": {"kernel": (f"decode_fused_par_kernel<{g.h_v // g.h_k}>" if single and g.h_v // g.h_k <= 3 else
+                                "decode_fused_kernel" if single else "decode_multi_kernel<fused norm>"),
                      "bound": "hbm",
                      "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,

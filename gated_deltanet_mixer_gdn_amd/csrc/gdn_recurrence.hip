@@ -39,7 +39,8 @@ struct HeadReduce {
     float kq[4];
 };
 
-// One token of one head for a 256-thread workgroup whose thread tid holds columns
+// One token of one head for a group of 256 threads (tid = the thread's index in the
+// group; a larger workgroup runs one such group per head) whose thread tid holds columns
 // 4*cg..4*cg+3 (cg = tid % 32) of rows 16*rg..16*rg+15 (rg = tid / 32) of the old
 // state in s[] (16 float4 = 64 VGPRs).  qk: q as 32 float4, then k as 32 float4, in
 // LDS; v: this thread's 4 columns of v.  Reductions: a per-thread partial over 16
@@ -54,8 +55,7 @@ template <bool kNorm>
 __device__ __forceinline__ void head_token_256(f4 (&s)[16], const f4* qk, f4 v, float beta, float eg,
                                                HeadReduce& red, float* o_row, const float* z_row,
                                                const float* norm_w, float* y_row, float eps, float oscale,
-                                               int gate_silu) {
-    const int tid = threadIdx.x;
+                                               int gate_silu, int tid) {
     const int cg = tid & 31;
     const int rg = tid >> 5;
     const int wave = tid >> 6;
@@ -155,19 +155,116 @@ __global__ __launch_bounds__(256) void decode_one_kernel(StepParams p) {
 
     head_token_256<kNorm>(s, qk_lds, v, beta, eg, red, p.o ? p.o + e * kS : nullptr,
                           kNorm ? p.z + e * kS : nullptr, p.norm_w, kNorm ? p.y + e * kS : nullptr, p.eps,
-                          p.oscale, p.gate_silu);
+                          p.oscale, p.gate_silu, tid);
     if (p.persist) store_tile(s, tile);
 }
 
-// The whole mixer for one decode token in one launch.  One workgroup of 256 threads
-// per (sequence b, qk head j): it owns the conv channels of q_j, k_j and of the
-// group's value heads i = g*j .. g*j+g-1 (g = h_v / h_k), so it is the only reader
-// and writer of their conv history.  Prologue: 16-lane rows run the conv + SiLU + L2
-// norm exactly as conv_silu_norm_kernel does (row 0: q_j, row 1: k_j, row 2+n: v of
-// head g*j+n) into LDS; then the workgroup steps the g heads one after another with
-// head_token_256 and the fused gated RMSNorm.  Head 0's tile loads are issued before
-// the prologue; each later head's loads follow the previous head's stores.  Results
-// equal gdn_conv_silu_norm followed by gdn_decode_step_norm bit for bit.
+// The conv prologue of the single-launch decode for (sequence b, qk head j): 16-lane
+// rows run the conv + SiLU + L2 norm exactly as conv_silu_norm_kernel does (row 0:
+// q_j, row 1: k_j, row 2+n: v of head g*j+n) into LDS and advance the conv history.
+// Threads tid >= 16 * (2 + g) do nothing.  slot >= 0.
+__device__ __forceinline__ void fused_conv_prologue(const FusedParams& p, int b, int j, int slot, int tid,
+                                                    f4* qk_lds, f4 (*v_lds)[32]) {
+    const int g = p.group;
+    const long long C = (long long) (2 * p.h_k + p.h_v) * kS;
+    const int crow = tid >> 4;
+    if (crow >= 2 + g) return;
+    const int cl = tid & 15;
+    const int hd = crow == 0 ? j : crow == 1 ? p.h_k + j : 2 * p.h_k + g * j + (crow - 2);
+    const long long ca = (long long) hd * kS + 4 * cl;
+    const long long cb = ca + 64;
+    float* X = p.conv + (long long) slot * C * kHist;
+    const float* xq = p.qkv + (long long) b * C;
+    ConvGroup ga, gb;
+    ga.load_taps(p.w, ca);
+    gb.load_taps(p.w, cb);
+    ga.load_history(X + ca * kHist);
+    gb.load_history(X + cb * kHist);
+    const f4 ua = ga.step(*(const f4*) (xq + ca));
+    const f4 ub = gb.step(*(const f4*) (xq + cb));
+    f4 ha = ua * sigmoid4(ua);
+    f4 hb = ub * sigmoid4(ub);
+    if (crow < 2) {
+        const float ss = add_xor8(block8_sum(sumsq4(ha) + sumsq4(hb)));
+        const float sc = (crow == 0 ? p.qscale : 1.0f) / sqrtf(ss + p.eps);
+        ha *= sc;
+        hb *= sc;
+    }
+    ConvGroup::store_history(X + ca * kHist, ga.x3, ga.x2, ga.x1);
+    ConvGroup::store_history(X + cb * kHist, gb.x3, gb.x2, gb.x1);
+    if (p.h) {
+        *(f4*) (p.h + (long long) b * C + ca) = ha;
+        *(f4*) (p.h + (long long) b * C + cb) = hb;
+    }
+    f4* dst = crow < 2 ? qk_lds + 32 * crow : v_lds[crow - 2];
+    dst[cl] = ha;
+    dst[16 + cl] = hb;
+}
+
+// Outputs of the single-launch decode for a sequence with an unknown slot: y of the
+// group's heads and (if asked for) their h channels are zero; the pool is untouched.
+__device__ __forceinline__ void fused_zero_outputs(const FusedParams& p, int b, int j, int tid, int nthreads) {
+    const int g = p.group;
+    const long long C = (long long) (2 * p.h_k + p.h_v) * kS;
+    const f4 zero = {0.f, 0.f, 0.f, 0.f};
+    for (int u = tid; u < g * 32; u += nthreads)
+        *(f4*) (p.y + ((long long) b * p.h_v + g * j + u / 32) * kS + (u % 32) * 4) = zero;
+    if (p.h)
+        for (int u = tid; u < (2 + g) * 32; u += nthreads) {
+            const int crow = u / 32;
+            const int hd = crow == 0 ? j : crow == 1 ? p.h_k + j : 2 * p.h_k + g * j + (crow - 2);
+            *(f4*) (p.h + (long long) b * C + (long long) hd * kS + (u % 32) * 4) = zero;
+        }
+}
+
+// The whole mixer for one decode token in one launch.  One workgroup per (sequence b,
+// qk head j): it owns the conv channels of q_j, k_j and of the group's value heads
+// i = g*j .. g*j+g-1 (g = h_v / h_k), so it is the only reader and writer of their conv
+// history.  After the conv prologue the g heads run head_token_256 with the fused
+// gated RMSNorm.  Results equal gdn_conv_silu_norm followed by gdn_decode_step_norm
+// bit for bit.
+//
+// decode_fused_par_kernel<G> (g = G <= 3): 256 * G threads, one 256-thread group per
+// value head, all G heads at once; every group's tile loads are issued before the
+// prologue, so the workgroup streams its G tiles together.
+template <int G>
+__global__ __launch_bounds__(256 * G) void decode_fused_par_kernel(FusedParams p) {
+    __shared__ f4 qk_lds[64];
+    __shared__ f4 v_lds[G][32];
+    __shared__ HeadReduce red[G];
+
+    const int tid = threadIdx.x;
+    const int n = tid >> 8;       // value head g*j + n of this thread's group
+    const int lt = tid & 255;
+    const int cg = lt & 31;
+    const int rg = lt >> 5;
+    const unsigned nwg = gridDim.x;
+    unsigned wid = blockIdx.x;
+    if ((nwg & 7u) == 0) wid = (wid & 7u) * (nwg >> 3) + (wid >> 3);
+    const int b = (int) (wid / (unsigned) p.h_k);
+    const int j = (int) (wid - (unsigned) b * (unsigned) p.h_k);
+    const int slot = read_slot(p.slots, b, p.n_slots, p.flags, tid == 0 && j == 0);
+    if (slot < 0) {
+        fused_zero_outputs(p, b, j, tid, 256 * G);
+        return;
+    }
+    const int i = G * j + n;
+    float* tile = p.state + ((long long) slot * p.h_v + i) * (kS * kS) + (rg * 16) * kS + cg * 4;
+    f4 s[16];
+    load_tile(s, tile);
+    fused_conv_prologue(p, b, j, slot, tid, qk_lds, v_lds);
+    __syncthreads();
+    const long long e = (long long) b * p.h_v + i;
+    const float beta = sigmoid_f(p.beta_logit[e]);
+    const float eg = expf(softplus_f(p.alpha[e] + p.dt[i]) * p.ssm_a[i]);
+    head_token_256<true>(s, qk_lds, v_lds[n][cg], beta, eg, red[n], nullptr, p.z + e * kS, p.norm_w, p.y + e * kS,
+                         p.eps, p.oscale, p.gate_silu, lt);
+    store_tile(s, tile);
+}
+
+// decode_fused_kernel (any g up to kFusedMaxGroup): 256 threads stepping the g heads
+// one after another; head 0's tile loads are issued before the prologue, each later
+// head's follow the previous head's stores.
 __global__ __launch_bounds__(256) void decode_fused_kernel(FusedParams p) {
     __shared__ f4 qk_lds[64];
     __shared__ f4 v_lds[kFusedMaxGroup][32];
@@ -182,57 +279,15 @@ __global__ __launch_bounds__(256) void decode_fused_kernel(FusedParams p) {
     const int b = (int) (wid / (unsigned) p.h_k);
     const int j = (int) (wid - (unsigned) b * (unsigned) p.h_k);
     const int g = p.group;
-    const long long C = (long long) (2 * p.h_k + p.h_v) * kS;
     const int slot = read_slot(p.slots, b, p.n_slots, p.flags, tid == 0 && j == 0);
-    const int crow = tid >> 4;   // conv row: 0 = q_j, 1 = k_j, 2 + n = v of head g*j + n
-    const int cl = tid & 15;
-    const int hd = crow == 0 ? j : crow == 1 ? p.h_k + j : 2 * p.h_k + g * j + (crow - 2);
-    const long long ca = (long long) hd * kS + 4 * cl;
-    const long long cb = ca + 64;
-
-    if (slot < 0) {   // unknown slot: outputs zero, pool untouched
-        const f4 zero = {0.f, 0.f, 0.f, 0.f};
-        if (rg == 0)
-            for (int n = 0; n < g; ++n) *(f4*) (p.y + ((long long) b * p.h_v + g * j + n) * kS + cg * 4) = zero;
-        if (p.h && crow < 2 + g) {
-            *(f4*) (p.h + (long long) b * C + ca) = zero;
-            *(f4*) (p.h + (long long) b * C + cb) = zero;
-        }
+    if (slot < 0) {
+        fused_zero_outputs(p, b, j, tid, 256);
         return;
     }
-
     const float* tile_base = p.state + ((long long) slot * p.h_v + g * j) * (kS * kS) + (rg * 16) * kS + cg * 4;
     f4 s[16];
     load_tile(s, tile_base);
-
-    if (crow < 2 + g) {
-        float* X = p.conv + (long long) slot * C * kHist;
-        const float* xq = p.qkv + (long long) b * C;
-        ConvGroup ga, gb;
-        ga.load_taps(p.w, ca);
-        gb.load_taps(p.w, cb);
-        ga.load_history(X + ca * kHist);
-        gb.load_history(X + cb * kHist);
-        const f4 ua = ga.step(*(const f4*) (xq + ca));
-        const f4 ub = gb.step(*(const f4*) (xq + cb));
-        f4 ha = ua * sigmoid4(ua);
-        f4 hb = ub * sigmoid4(ub);
-        if (crow < 2) {
-            const float ss = add_xor8(block8_sum(sumsq4(ha) + sumsq4(hb)));
-            const float sc = (crow == 0 ? p.qscale : 1.0f) / sqrtf(ss + p.eps);
-            ha *= sc;
-            hb *= sc;
-        }
-        ConvGroup::store_history(X + ca * kHist, ga.x3, ga.x2, ga.x1);
-        ConvGroup::store_history(X + cb * kHist, gb.x3, gb.x2, gb.x1);
-        if (p.h) {
-            *(f4*) (p.h + (long long) b * C + ca) = ha;
-            *(f4*) (p.h + (long long) b * C + cb) = hb;
-        }
-        f4* dst = crow < 2 ? qk_lds + 32 * crow : v_lds[crow - 2];
-        dst[cl] = ha;
-        dst[16 + cl] = hb;
-    }
+    fused_conv_prologue(p, b, j, slot, tid, qk_lds, v_lds);
     __syncthreads();
 
     for (int n = 0; n < g; ++n) {
@@ -243,7 +298,7 @@ __global__ __launch_bounds__(256) void decode_fused_kernel(FusedParams p) {
         const float beta = sigmoid_f(p.beta_logit[e]);
         const float eg = expf(softplus_f(p.alpha[e] + p.dt[i]) * p.ssm_a[i]);
         head_token_256<true>(s, qk_lds, v_lds[n][cg], beta, eg, red[n & 1], nullptr, p.z + e * kS, p.norm_w,
-                             p.y + e * kS, p.eps, p.oscale, p.gate_silu);
+                             p.y + e * kS, p.eps, p.oscale, p.gate_silu, tid);
         store_tile(s, tile);
     }
 }
@@ -404,7 +459,12 @@ __global__ __launch_bounds__(256) void decode_multi_kernel(StepParams p) {
 // ------------------------------------------------------------------ launch
 hipError_t launch_decode_fused(const FusedParams& p, hipStream_t stream) {
     const dim3 grid((unsigned) ((long long) p.B * p.h_k));
-    hipLaunchKernelGGL(decode_fused_kernel, grid, dim3(256), 0, stream, p);
+    switch (p.group) {
+    case 1: hipLaunchKernelGGL(decode_fused_par_kernel<1>, grid, dim3(256), 0, stream, p); break;
+    case 2: hipLaunchKernelGGL(decode_fused_par_kernel<2>, grid, dim3(512), 0, stream, p); break;
+    case 3: hipLaunchKernelGGL(decode_fused_par_kernel<3>, grid, dim3(768), 0, stream, p); break;
+    default: hipLaunchKernelGGL(decode_fused_kernel, grid, dim3(256), 0, stream, p); break;
+    }
     return hipGetLastError();
 }
 
