@@ -127,6 +127,24 @@ def copy_probe(mib: int, reps: int = 5):
     print(json.dumps({"copy_probe_bytes_read": n * 4, "copy_probe_bytes_written": n * 4, "reps": reps}))
 
 
+def gpu_clocks():
+    """Current GPU clocks as amd-smi reports them (JSON), or None if the tool is absent or
+    fails; run as a child process, after the timed region."""
+    import subprocess
+    for cmd in (["amd-smi", "metric", "--gpu", "0", "--clock", "--json"],
+                ["rocm-smi", "--showclocks", "--json"]):
+        try:
+            r = subprocess.run(cmd, capture_output=True, text=True, timeout=20)
+        except (OSError, subprocess.SubprocessError):
+            continue
+        if r.returncode == 0 and r.stdout.strip():
+            try:
+                return {"tool": cmd[0], "report": json.loads(r.stdout)}
+            except ValueError:
+                continue
+    return None
+
+
 def projections_context(G, W, rows: int, stream, reps: int = 50):
     """Time the split of x, qkv + z in one launch, the split of y and the out projection
     at the pages' sizes; algorithmic flops are 2 * rows * k * n per projection."""
@@ -344,6 +362,7 @@ def main():
     log("three calls: " + ", ".join(f"{k}={v * 1000:.1f}us" for k, v in three_k.items()) +
         f"; {three_ms * 1000:.1f} us/step; recurrence kernel {three_step_gbps:.0f} GB/s; d2d copy {copy_gbps:.0f} GB/s")
     traffic = read_traffic() if args.config == "b256" else None
+    clocks = gpu_clocks()
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -389,6 +408,7 @@ def main():
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
                      "algorithmic_bytes_per_launch": nbytes[dominant],
                      "event_samples": n_samples},
+        "gpu_clocks_after_timing": clocks,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
