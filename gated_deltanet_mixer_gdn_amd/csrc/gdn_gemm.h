@@ -55,6 +55,9 @@ struct GemmParams {
 struct GemmConfig {
     int wm, wn, kw, lds;
 };
+// lds value of the ring-pipelined LDS form (4 waves side by side in n, activation
+// tiles through a 3-buffer LDS ring, weight fragments in a 3-deep register ring)
+constexpr int kRing = 9;
 
 bool gemm_config_supported(const GemmConfig& c);
 GemmConfig choose_gemm_config(long long rows, int k, int n);

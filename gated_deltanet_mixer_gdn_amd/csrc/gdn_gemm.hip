@@ -396,10 +396,135 @@ __global__ __launch_bounds__(256 * KG) void project_lds_kernel(GemmParams p, int
     store_blocks<WM, WN>(p, acc, m0, n0, i, h);
 }
 
-// the instantiated tile shapes: {wm, wn, kw, lds}
+// The LDS-shared tile with a deeper pipeline: the 4 waves sit side by side in n, the
+// chunk's WM activation tiles go through a ring of three LDS buffers (written once
+// per workgroup) and each wave keeps a ring of three register sets of weight
+// fragments, so two chunks are in flight while a third is multiplied.  Chunk c lives
+// in LDS buffer c % 3 and register set c % 3; the activation share of chunk c + 1 is
+// written to LDS after chunk c has been multiplied, one barrier per chunk.  Loads past
+// the last chunk reload the last one (never used), so every load is unconditional.
+template <int WM, int WN>
+__global__ __launch_bounds__(256) void project_ring_kernel(GemmParams p, int tiles_m, int tiles_total, int n_chunks) {
+    constexpr int BM = 32 * WM;
+    constexpr int BN = 128 * WN;
+    __shared__ u4v abuf[3][WM][512];
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int i = lane & 31;
+    const int h = lane >> 5;
+
+    const int t = xcd_tile(blockIdx.x, tiles_total);
+    const int tm = t % tiles_m;
+    const int tn = t / tiles_m;
+    const long long m0 = (long long) tm * BM;
+    const int n0 = tn * BN + wave * 32 * WN;
+    const long long last_rt = (p.rows + kTileRows - 1) / kTileRows - 1;
+    const int last_ct = (p.n + kTileRows - 1) / kTileRows - 1;
+
+    const u4v* asrc[WM];
+#pragma unroll
+    for (int r = 0; r < WM; ++r) {
+        const long long rt = min((long long) tm * WM + r, last_rt);
+        asrc[r] = (const u4v*) p.xs + rt * n_chunks * 512 + tid;
+    }
+    const bf16x8* bbase[WN];
+#pragma unroll
+    for (int c = 0; c < WN; ++c) {
+        const long long ct = min(n0 / 32 + c, last_ct);
+        bbase[c] = (const bf16x8*) p.wp + ct * n_chunks * 256 + lane;
+    }
+
+    struct AShare {
+        u4v v[WM][2];
+    };
+    struct BFrag {
+        bf16x8 b[WN][4];
+    };
+    const int last = n_chunks - 1;
+    auto load = [&](int ch, AShare& a, BFrag& f) {
+        ch = min(ch, last);
+#pragma unroll
+        for (int r = 0; r < WM; ++r) {
+            a.v[r][0] = asrc[r][ch * 512];
+            a.v[r][1] = asrc[r][ch * 512 + 256];
+        }
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int c = 0; c < WN; ++c) f.b[c][s] = bbase[c][ch * 256 + s * 64];
+    };
+    auto store_a = [&](int buf, const AShare& a) {
+#pragma unroll
+        for (int r = 0; r < WM; ++r) {
+            abuf[buf][r][tid] = a.v[r][0];
+            abuf[buf][r][tid + 256] = a.v[r][1];
+        }
+    };
+
+    f16v acc[WM][WN];
+#pragma unroll
+    for (int r = 0; r < WM; ++r)
+#pragma unroll
+        for (int c = 0; c < WN; ++c) acc[r][c] = f16v{};
+    auto compute = [&](int buf, const BFrag& f) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            bf16x8 a[WM][2];
+#pragma unroll
+            for (int r = 0; r < WM; ++r) {
+                a[r][0] = __builtin_bit_cast(bf16x8, abuf[buf][r][(2 * s) * 64 + lane]);
+                a[r][1] = __builtin_bit_cast(bf16x8, abuf[buf][r][(2 * s + 1) * 64 + lane]);
+            }
+#pragma unroll
+            for (int r = 0; r < WM; ++r)
+#pragma unroll
+                for (int c = 0; c < WN; ++c) {
+                    acc[r][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[r][0], f.b[c][s], acc[r][c], 0, 0, 0);
+                    acc[r][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[r][1], f.b[c][s], acc[r][c], 0, 0, 0);
+                }
+        }
+    };
+
+    // On entry to a trip (c = 0 mod 3): chunk c is in LDS buffer 0 with its weights in
+    // f0; chunk c + 1 is loaded (in flight) into a1 / f1.
+    AShare a0, a1, a2;
+    BFrag f0, f1, f2;
+    load(0, a0, f0);
+    load(1, a1, f1);
+    store_a(0, a0);
+    __syncthreads();
+    int c = 0;
+    for (; c + 3 <= n_chunks; c += 3) {
+        load(c + 2, a2, f2);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(0, f0);
+        store_a(1, a1);
+        __syncthreads();
+        load(c + 3, a0, f0);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(1, f1);
+        store_a(2, a2);
+        __syncthreads();
+        load(c + 4, a1, f1);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(2, f2);
+        store_a(0, a0);
+        __syncthreads();
+    }
+    if (c < n_chunks) compute(0, f0);
+    if (c + 1 < n_chunks) {
+        store_a(1, a1);
+        __syncthreads();
+        compute(1, f1);
+    }
+    store_blocks<WM, WN>(p, acc, m0, n0, i, h);
+}
+
+// the instantiated tile shapes: {wm, wn, kw, lds} (lds = kRing: project_ring_kernel)
 constexpr GemmConfig kConfigs[] = {
-    {1, 1, 4, 0}, {1, 2, 4, 0}, {1, 3, 4, 0}, {2, 1, 4, 0}, {2, 2, 4, 0}, {2, 2, 2, 0},
-    {2, 2, 1, 0}, {2, 3, 4, 0}, {2, 3, 2, 0}, {2, 3, 1, 2},
+    {1, 1, 4, 0}, {1, 2, 4, 0}, {2, 1, 4, 0}, {2, 2, 4, 0}, {2, 2, 2, 0},
+    {2, 2, 1, 0}, {2, 3, 4, 0}, {2, 3, 2, 0}, {2, 3, 1, 2}, {1, 1, 1, kRing},
 };
 
 template <int WM, int WN, int KW>
@@ -408,6 +533,15 @@ hipError_t launch_tile(const GemmParams& p, hipStream_t stream) {
     const long long tm = (p.rows + BM - 1) / BM, tn = ((long long) p.n + BN - 1) / BN;
     hipLaunchKernelGGL((project_bf16_kernel<WM, WN, KW>), dim3((unsigned) (tm * tn)), dim3(256), 0, stream, p,
                        (int) tm, (int) (tm * tn), (int) (pad_up(p.k, kTileK) / kTileK));
+    return hipGetLastError();
+}
+
+template <int WM, int WN>
+hipError_t launch_ring_tile(const GemmParams& p, hipStream_t stream) {
+    constexpr int BM = 32 * WM, BN = 128 * WN;
+    const long long tm = (p.rows + BM - 1) / BM, tn = ((long long) p.n + BN - 1) / BN;
+    hipLaunchKernelGGL((project_ring_kernel<WM, WN>), dim3((unsigned) (tm * tn)), dim3(256), 0, stream, p, (int) tm,
+                       (int) (tm * tn), (int) (pad_up(p.k, kTileK) / kTileK));
     return hipGetLastError();
 }
 
@@ -435,7 +569,8 @@ long long gemm_workgroups(const GemmParams& p, const GemmConfig& c) {
 
 // Up to 64 rows the product is bound by the weight stream, and the tile shapes that
 // measured fastest on MI355X for n = 2560 to 16384 are taken by rule: one row tile,
-// the k range split over the 4 waves, wider column tiles as n grows.  Above 64 rows
+// the k range split over the 4 waves, wider column tiles as n grows (from 33 rows
+// and n >= 8192, the ring-pipelined LDS form).  Above 64 rows
 // it is bound by the matrix cores and the L2 -> CU operand stream; each candidate
 // shape is priced as (rounds of 256 workgroups) x (chunks per wave) x (32x32 blocks
 // per wave) x (measured microseconds per block-chunk of that shape), which keeps
@@ -449,12 +584,13 @@ struct Priced {
 constexpr Priced kPriced[] = {
     {{2, 2, 1, 0}, 0.245, 65}, {{2, 3, 2, 0}, 0.31, 65}, {{2, 2, 2, 0}, 0.305, 65}, {{2, 2, 4, 0}, 0.33, 65},
     {{2, 3, 4, 0}, 0.38, 65},  {{2, 1, 4, 0}, 0.42, 65}, {{2, 3, 1, 2}, 0.46, 257},
+    {{1, 1, 1, kRing}, 0.34, 65},
 };
 }  // namespace
 
 GemmConfig choose_gemm_config(long long rows, int k, int n) {
     if (rows <= 32) return n >= 8192 ? GemmConfig{1, 2, 4, 0} : GemmConfig{1, 1, 4, 0};
-    if (rows <= 64) return n >= 8192 ? GemmConfig{1, 3, 4, 0} : n >= 4096 ? GemmConfig{1, 2, 4, 0} : GemmConfig{1, 1, 4, 0};
+    if (rows <= 64) return n >= 8192 ? GemmConfig{1, 1, 1, kRing} : n >= 4096 ? GemmConfig{1, 2, 4, 0} : GemmConfig{1, 1, 4, 0};
     const long long chunks = pad_up(k, kTileK) / kTileK;
     GemmParams p{};
     p.rows = rows;
@@ -463,7 +599,7 @@ GemmConfig choose_gemm_config(long long rows, int k, int n) {
     double best_us = -1.0;
     for (const Priced& q : kPriced) {
         if (rows < q.min_rows) continue;
-        const long long split = q.c.lds ? q.c.lds : q.c.kw;
+        const long long split = q.c.lds == kRing ? 1 : q.c.lds ? q.c.lds : q.c.kw;
         const long long rounds = (gemm_workgroups(p, q.c) + 255) / 256;
         const double us = (double) rounds * (double) ((chunks + split - 1) / split) * q.c.wm * q.c.wn *
                           q.us_per_block_chunk;
@@ -494,9 +630,9 @@ hipError_t launch_project_bf16(const GemmParams& p, const GemmConfig& c, hipStre
     if (!c.lds && c.wm == A && c.wn == B && c.kw == C) return launch_tile<A, B, C>(p, stream);
 #define GDN_LDS_TILE(A, B, G) \
     if (c.lds == G && c.wm == A && c.wn == B && c.kw == 1) return launch_lds_tile<A, B, G>(p, stream);
+    if (c.lds == kRing && c.wm == 1 && c.wn == 1) return launch_ring_tile<1, 1>(p, stream);
     GDN_TILE(1, 1, 4)
     GDN_TILE(1, 2, 4)
-    GDN_TILE(1, 3, 4)
     GDN_TILE(2, 1, 4)
     GDN_TILE(2, 2, 4)
     GDN_TILE(2, 2, 2)

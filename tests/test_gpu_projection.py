@@ -71,12 +71,13 @@ def test_pack_is_a_permutation_with_zero_padding():
 
 # (rows, k, n): a single row, ragged rows / columns / k, several tiles of each shape, and
 # the tile shapes the launch picks by rows, k and n (one or two row tiles per
-# workgroup, 1-3 column tiles per wave, k split over 1, 2 or 4 waves); the LDS-shared
-# form, picked only for long k at more than 256 rows, has its own sampled test below
+# workgroup, 1-3 column tiles per wave, k split over 1, 2 or 4 waves, and the
+# ring-pipelined LDS form with 1, 2, 3 and 4 chunks); the two-group LDS form, picked
+# only for long k at more than 256 rows, has its own sampled test below
 SHAPES = [(1, 64, 32), (3, 72, 40), (33, 136, 100), (64, 2560, 256), (70, 520, 300), (200, 520, 1030),
           (37, 6144, 96), (1, 2560, 10240), (16, 2560, 6144), (300, 128, 4100), (50, 200, 8200),
           (40, 136, 5000), (100, 264, 8300), (150, 136, 4500), (250, 72, 8250), (300, 200, 9000),
-          (300, 136, 8200), (600, 64, 8192)]
+          (300, 136, 8200), (600, 64, 8192), (40, 64, 9000), (60, 120, 8300), (45, 136, 8200)]
 
 
 @pytest.mark.parametrize("rows,k,n", SHAPES)
