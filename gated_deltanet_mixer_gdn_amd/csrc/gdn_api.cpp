@@ -33,6 +33,9 @@ namespace {
 
 thread_local std::string g_last_error;
 
+// Largest k of the projections: chunk offsets inside the kernels are 32-bit.
+constexpr int32_t kMaxProjK = 1 << 24;
+
 constexpr size_t kAlign = 256;
 constexpr size_t kFlagBytes = 256;
 
@@ -462,19 +465,20 @@ int gdn_ab_project(const float* x, const uint16_t* w_alpha, const uint16_t* w_be
 }
 
 int64_t gdn_split_bf16_bytes(int64_t rows, int32_t k) {
-    if (rows < 0 || k <= 0 || k % 8 != 0 || rows > (INT64_MAX / 8) / gdn::pad_up(k, gdn::kTileK)) return -1;
+    if (rows < 0 || k <= 0 || k % 8 != 0 || k > kMaxProjK || rows > (INT64_MAX / 8) / gdn::pad_up(k, gdn::kTileK)) return -1;
     return gdn::pad_up(rows, gdn::kTileRows) * gdn::pad_up(k, gdn::kTileK) * 4;
 }
 
 int64_t gdn_pack_bf16_bytes(int32_t n, int32_t k) {
-    if (n <= 0 || k <= 0 || k % 8 != 0) return -1;
+    if (n <= 0 || k <= 0 || k % 8 != 0 || k > kMaxProjK) return -1;
     return gdn::pad_up(n, gdn::kTileRows) * gdn::pad_up(k, gdn::kTileK) * 2;
 }
 
 int gdn_split_bf16(const float* x, int64_t rows, int32_t k, uint16_t* xs, void* stream) {
     const char* fn = "gdn_split_bf16";
     if (rows < 0) return fail(GDN_ERR_ARG, fn, "rows=%lld is negative", (long long) rows);
-    if (k <= 0 || k % 8 != 0) return fail(GDN_ERR_ARG, fn, "k=%d must be a positive multiple of 8", k);
+    if (k <= 0 || k % 8 != 0 || k > kMaxProjK)
+        return fail(GDN_ERR_ARG, fn, "k=%d must be a positive multiple of 8, at most %d", k, kMaxProjK);
     if (rows == 0) return ok();
     const int64_t xs_bytes = gdn_split_bf16_bytes(rows, k);
     if (xs_bytes < 0) return fail(GDN_ERR_ARG, fn, "rows too large");
@@ -493,7 +497,8 @@ int gdn_split_bf16(const float* x, int64_t rows, int32_t k, uint16_t* xs, void* 
 int gdn_pack_bf16(const uint16_t* w, int32_t n, int32_t k, uint16_t* wp, void* stream) {
     const char* fn = "gdn_pack_bf16";
     if (n <= 0) return fail(GDN_ERR_ARG, fn, "n=%d must be positive", n);
-    if (k <= 0 || k % 8 != 0) return fail(GDN_ERR_ARG, fn, "k=%d must be a positive multiple of 8", k);
+    if (k <= 0 || k % 8 != 0 || k > kMaxProjK)
+        return fail(GDN_ERR_ARG, fn, "k=%d must be a positive multiple of 8, at most %d", k, kMaxProjK);
     if (int rc = check_f4(w, fn, "w")) return rc;
     if (int rc = check_f4(wp, fn, "wp")) return rc;
     if (overlap(wp, (size_t) gdn_pack_bf16_bytes(n, k), w, (size_t) n * k * 2))
@@ -511,7 +516,8 @@ namespace {
 int project_common(const char* fn, const uint16_t* xs, const uint16_t* wp, int64_t rows, int32_t k, int32_t n1,
                    float* out1, int32_t n2, float* out2, void* stream) {
     if (rows < 0) return fail(GDN_ERR_ARG, fn, "rows=%lld is negative", (long long) rows);
-    if (k <= 0 || k % 8 != 0) return fail(GDN_ERR_ARG, fn, "k=%d must be a positive multiple of 8", k);
+    if (k <= 0 || k % 8 != 0 || k > kMaxProjK)
+        return fail(GDN_ERR_ARG, fn, "k=%d must be a positive multiple of 8, at most %d", k, kMaxProjK);
     if (n1 <= 0 || n2 < 0 || n1 > INT32_MAX - n2) return fail(GDN_ERR_ARG, fn, "n1=%d, n2=%d out of range", n1, n2);
     if (rows == 0) return ok();
     const int32_t n = n1 + n2;

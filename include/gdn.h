@@ -256,7 +256,7 @@ int gdn_ab_project(const float* x, const uint16_t* w_alpha, const uint16_t* w_be
  * form a 16-byte fragment.  Packed weights: tile (R, C) of R-major order holds the
  * fragments (s, l) at index s*64 + l (4 KiB per tile).  Split activations: tile
  * (R, C) holds the hi fragment (s, l) at index (2s)*64 + l and the lo fragment at
- * (2s + 1)*64 + l (8 KiB per tile).  k must be a positive multiple of 8. */
+ * (2s + 1)*64 + l (8 KiB per tile).  k must be a positive multiple of 8, at most 2^24. */
 
 /* Bytes of the split activations for [rows][k]: ceil(rows/32)*32 * ceil(k/64)*64 * 4,
  * or -1 for a negative rows or a k that is not a positive multiple of 8. */

@@ -224,6 +224,9 @@ def test_projection_argument_errors(L):
     assert L.gdn_split_bf16_bytes(-1, 64) == -1 and L.gdn_split_bf16_bytes(4, 12) == -1
     assert L.gdn_pack_bf16_bytes(100, 136) == 128 * 192 * 2
     assert L.gdn_pack_bf16_bytes(0, 64) == -1 and L.gdn_pack_bf16_bytes(4, 0) == -1
+    assert L.gdn_split_bf16_bytes(1, (1 << 24) + 8) == -1 and L.gdn_pack_bf16_bytes(1, (1 << 24) + 8) == -1
+    assert L.gdn_project_bf16(16, 16, 4, (1 << 24) + 8, 32, 1 << 20, None) == GDN_ERR_ARG
+    assert b"at most" in L.gdn_last_error()
     assert L.gdn_split_bf16(16, -1, 64, 16, None) == GDN_ERR_ARG
     assert L.gdn_split_bf16(16, 4, 60, 16, None) == GDN_ERR_ARG
     assert b"multiple of 8" in L.gdn_last_error()
