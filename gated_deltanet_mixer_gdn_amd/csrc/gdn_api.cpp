@@ -441,7 +441,7 @@ int gdn_ab_project(const float* x, const uint16_t* w_alpha, const uint16_t* w_be
     if (n_embd % 4 != 0) return fail(GDN_ERR_UNSUPPORTED, fn, "n_embd=%d is not a multiple of 4", n_embd);
     if (rows == 0) return ok();
     const long long jobs = (rows + gdn::kAbRows - 1) / gdn::kAbRows * ((2LL * h_v + gdn::kAbCols - 1) / gdn::kAbCols);
-    if ((jobs + 3) / 4 > INT32_MAX) return fail(GDN_ERR_ARG, fn, "rows too large");
+    if (jobs > INT32_MAX) return fail(GDN_ERR_ARG, fn, "rows too large");
     if (int rc = check_f4(x, fn, "x")) return rc;
     if (!w_alpha || !aligned(w_alpha, 8)) return fail(GDN_ERR_ARG, fn, "w_alpha is null or not 8-byte aligned");
     if (!w_beta || !aligned(w_beta, 8)) return fail(GDN_ERR_ARG, fn, "w_beta is null or not 8-byte aligned");

@@ -7,9 +7,11 @@
 
 namespace gdn {
 
-// one wave per (kAbRows rows, kAbCols output columns)
+// one workgroup per (kAbRows rows, kAbCols output columns)
 constexpr int kAbRows = 4;
 constexpr int kAbCols = 8;
+// 256-element blocks of n_embd a wave loads at once (a wave takes every 4th block)
+constexpr int kAbBlocks = 3;
 
 struct AbParams {
     const float* x;          // [rows][n_embd]
