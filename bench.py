@@ -34,6 +34,10 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0            # MI355X HBM3E, published peak
 BF16_PEAK_TFLOPS = 2500.0         # MI355X dense bf16 matrix peak, published
+# fp32 VALU without packed instructions (this build keeps them off):
+# 256 CUs x 4 SIMDs x 16 lanes x 2 flop (FMA) x 2.4 GHz
+VALU_PEAK_TFLOPS = 78.6
+FLOP_PER_SEQ_HEAD_STEP = 7 * 128 * 128   # per state element: S^T k FMA, S^T q FMA, decay multiply, update FMA
 # the sources the recurrence kernel is built from (its counter record is void once they change)
 KERNEL_SRCS = [os.path.join(ROOT, "gated_deltanet_mixer_gdn_amd", "csrc", f)
                for f in ("gdn_recurrence.hip", "gdn_device.h", "gdn_kernels.h")]
@@ -349,6 +353,11 @@ def main():
     nbytes, units = algorithmic_bytes(wl)
     value = units / (ms_per_step / 1000.0)
     achieved = nbytes[dominant] / (k_ms[dominant] / 1000.0) / 1e9
+    # a workload whose flops per algorithmic byte exceed the VALU / HBM ridge (the
+    # multi-token prefill) is priced against the fp32 VALU peak instead
+    flops = units * FLOP_PER_SEQ_HEAD_STEP
+    alu_bound = flops / nbytes[dominant] > VALU_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)
+    achieved_tflops = flops / (k_ms[dominant] / 1000.0) / 1e12
     mixer_bytes = nbytes["one"] if single else nbytes["conv"] + nbytes["step_norm"]
     mixer_gbps = mixer_bytes / (ms_per_step / 1000.0) / 1e9
     two_gbps = nbytes["step_norm"] / (two_k["step_norm"] / 1000.0) / 1e9
@@ -403,10 +412,15 @@ def main():
         "projections": proj,
         "roofline": {"kernel": (f"decode_fused_par_kernel<{g.h_v // g.h_k}>" if single and g.h_v // g.h_k <= 3 else
                                 "decode_fused_kernel" if single else "decode_multi_kernel<fused norm>"),
-                     "bound": "hbm",
-                     "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
+                     "bound": "alu" if alu_bound else "hbm",
+                     "achieved": achieved_tflops if alu_bound else achieved,
+                     "peak": VALU_PEAK_TFLOPS if alu_bound else HBM_PEAK_GBPS,
+                     "unit": "TFLOP/s" if alu_bound else "GB/s",
+                     "frac": achieved_tflops / VALU_PEAK_TFLOPS if alu_bound else achieved / HBM_PEAK_GBPS,
+                     "traffic": traffic,
                      "algorithmic_bytes_per_launch": nbytes[dominant],
+                     "algorithmic_flops_per_launch": flops,
+                     "hbm_gbps": achieved,
                      "event_samples": n_samples},
         "gpu_clocks_after_timing": clocks,
         "cpu_baseline": cpu,
