@@ -324,8 +324,17 @@ def test_empty_batch_is_a_no_op():
     G.gdn_decode_step(pool, e, torch.empty(0, 1, 48, device="cuda"), torch.empty(0, 1, 48, device="cuda"),
                       torch.zeros(48, device="cuda"), torch.zeros(48, device="cuda"),
                       torch.empty(0, 1, 48, 128, device="cuda"))
+    e1 = torch.empty(0, 10240, device="cuda")
+    G.gdn_decode_fused(pool, e1, torch.zeros(10240, 4, device="cuda"), torch.empty(0, 48, device="cuda"),
+                       torch.empty(0, 48, device="cuda"), torch.zeros(48, device="cuda"), torch.zeros(48, device="cuda"),
+                       torch.empty(0, 6144, device="cuda"), torch.ones(128, device="cuda"), 1e-6,
+                       torch.empty(0, 6144, device="cuda"))
+    G.gdn_decode_step_norm(pool, e, torch.empty(0, 1, 48, device="cuda"), torch.empty(0, 1, 48, device="cuda"),
+                           torch.zeros(48, device="cuda"), torch.zeros(48, device="cuda"),
+                           torch.empty(0, 1, 6144, device="cuda"), torch.ones(128, device="cuda"), 1e-6,
+                           torch.empty(0, 1, 6144, device="cuda"))
     torch.cuda.synchronize()
-    assert int(torch.count_nonzero(pool.state)) == 0
+    assert int(torch.count_nonzero(pool.state)) == 0 and int(torch.count_nonzero(pool.conv)) == 0
 
 
 def test_abi_rejects_bad_arguments_on_device():
@@ -382,7 +391,8 @@ def test_token_counts_across_conv_blocks(fused):
     _compare_all(gm, wl, res, 3 * STEP_TOL, "blocks")
 
 
-@pytest.mark.parametrize("geom", [W.Geom(), W.Geom(h_k=2, h_v=6), W.Geom(h_k=2, h_v=4), W.Geom(h_k=1, h_v=14)],
+@pytest.mark.parametrize("geom", [W.Geom(), W.Geom(h_k=2, h_v=6), W.Geom(h_k=2, h_v=4), W.Geom(h_k=2, h_v=2),
+                                  W.Geom(h_k=1, h_v=4), W.Geom(h_k=1, h_v=14)],
                          ids=lambda g: f"hk{g.h_k}hv{g.h_v}")
 def test_single_launch_decode_equals_two_calls_bitwise(geom):
     """gdn_decode_fused == gdn_conv_silu_norm + gdn_decode_step_norm, bit for bit, and
