@@ -511,14 +511,25 @@ int gdn_pack_bf16(const uint16_t* w, int32_t n, int32_t k, uint16_t* wp, void* s
     return launched(gdn::launch_pack_bf16(pp, static_cast<hipStream_t>(stream)), fn);
 }
 
+int64_t gdn_project_workspace_bytes(int64_t rows, int32_t k, int32_t n) {
+    if (rows < 0 || n <= 0 || gdn_split_bf16_bytes(rows, k) < 0 || rows > INT64_MAX / 4 / n) return -1;
+    if (rows == 0) return 0;
+    gdn::GemmParams gp{};
+    gp.rows = (long long) rows;
+    gp.k = k;
+    gp.n = n;
+    return gdn::gemm_workspace_bytes(gp, gdn::choose_gemm_config(gp.rows, k, n));
+}
+
 namespace {
 
 int project_common(const char* fn, const uint16_t* xs, const uint16_t* wp, int64_t rows, int32_t k, int32_t n1,
-                   float* out1, int32_t n2, float* out2, void* stream) {
+                   float* out1, int32_t n2, float* out2, void* workspace, int64_t workspace_bytes, void* stream) {
     if (rows < 0) return fail(GDN_ERR_ARG, fn, "rows=%lld is negative", (long long) rows);
     if (k <= 0 || k % 8 != 0 || k > kMaxProjK)
         return fail(GDN_ERR_ARG, fn, "k=%d must be a positive multiple of 8, at most %d", k, kMaxProjK);
     if (n1 <= 0 || n2 < 0 || n1 > INT32_MAX - n2) return fail(GDN_ERR_ARG, fn, "n1=%d, n2=%d out of range", n1, n2);
+    if (workspace_bytes < 0) return fail(GDN_ERR_ARG, fn, "workspace_bytes=%lld is negative", (long long) workspace_bytes);
     if (rows == 0) return ok();
     const int32_t n = n1 + n2;
     const int64_t xs_bytes = gdn_split_bf16_bytes(rows, k);
@@ -546,21 +557,37 @@ int project_common(const char* fn, const uint16_t* xs, const uint16_t* wp, int64
     gp.n1 = n1;
     const gdn::GemmConfig cfg = gdn::choose_gemm_config(gp.rows, k, n);
     if (gdn::gemm_workgroups(gp, cfg) > INT32_MAX) return fail(GDN_ERR_ARG, fn, "rows x n too large");
+    const long long need = gdn::gemm_workspace_bytes(gp, cfg);
+    if (need > 0) {
+        if (workspace_bytes < need)
+            return fail(GDN_ERR_ARG, fn, "workspace of %lld bytes, the launch needs %lld (gdn_project_workspace_bytes)",
+                        (long long) workspace_bytes, need);
+        if (int rc = check_f4(workspace, fn, "workspace")) return rc;
+        const void* args[4] = {xs, wp, out1, out2};
+        const size_t sizes[4] = {(size_t) xs_bytes, wp_bytes, b1, b2};
+        for (int a = 0; a < 4; ++a)
+            if (sizes[a] && overlap(workspace, (size_t) need, args[a], sizes[a]))
+                return fail(GDN_ERR_ARG, fn, "workspace overlaps %s",
+                            a == 0 ? "xs" : a == 1 ? "wp" : a == 3 ? "out2" : n2 ? "out1" : "out");
+        gp.ws = static_cast<float*>(workspace);
+    }
+    gp.parts = cfg.parts;
     return launched(gdn::launch_project_bf16(gp, cfg, static_cast<hipStream_t>(stream)), fn);
 }
 
 }  // namespace
 
 int gdn_project_bf16(const uint16_t* xs, const uint16_t* wp, int64_t rows, int32_t k, int32_t n, float* out,
-                     void* stream) {
+                     void* workspace, int64_t workspace_bytes, void* stream) {
     if (n <= 0) return fail(GDN_ERR_ARG, "gdn_project_bf16", "n=%d must be positive", n);
-    return project_common("gdn_project_bf16", xs, wp, rows, k, n, out, 0, nullptr, stream);
+    return project_common("gdn_project_bf16", xs, wp, rows, k, n, out, 0, nullptr, workspace, workspace_bytes, stream);
 }
 
 int gdn_project2_bf16(const uint16_t* xs, const uint16_t* wp, int64_t rows, int32_t k, int32_t n1, float* out1,
-                      int32_t n2, float* out2, void* stream) {
+                      int32_t n2, float* out2, void* workspace, int64_t workspace_bytes, void* stream) {
     if (n2 <= 0) return fail(GDN_ERR_ARG, "gdn_project2_bf16", "n2=%d must be positive", n2);
-    return project_common("gdn_project2_bf16", xs, wp, rows, k, n1, out1, n2, out2, stream);
+    return project_common("gdn_project2_bf16", xs, wp, rows, k, n1, out1, n2, out2, workspace, workspace_bytes,
+                          stream);
 }
 
 int gdn_gated_rmsnorm(const float* o, const float* z, const float* w, float eps, int64_t rows, int32_t s,

@@ -38,6 +38,10 @@ struct PackParams {
 
 // res[r][j] = sum_e w[j][e] * (hi + lo)[r][e]; columns j < n1 go to out [rows][n1],
 // the others to out2 [rows][n - n1] (n1 = n: one output)
+//
+// parts > 1 (tile shapes with kw = 4 only): the k chunks are split into `parts`
+// contiguous ranges, one workgroup per (tile, range), each writing its partial block
+// to ws; a second kernel adds a tile's blocks in range order and stores the tile.
 struct GemmParams {
     const uint16_t* xs;  // split activations, tiled
     const uint16_t* wp;  // packed weights, tiled
@@ -45,6 +49,8 @@ struct GemmParams {
     float* out2;
     long long rows;
     int k, n, n1;
+    int parts = 1;
+    float* ws = nullptr;   // [tiles][parts][32 WM x 32 WN block] partial sums
 };
 
 // Tile shape of one launch: each of the 4 waves of a workgroup computes a
@@ -52,8 +58,11 @@ struct GemmParams {
 // its k range, the other 4/kw waves take neighbouring column blocks.  lds = G > 0
 // (kw = 1 only): G groups of 4 such waves take alternate k chunks, and each group's
 // activation tiles go through LDS once instead of being read by every wave.
+// parts > 1 (kw = 4, lds = 0 only): the k range is also split over `parts`
+// workgroups per tile (GemmParams::parts).
 struct GemmConfig {
     int wm, wn, kw, lds;
+    int parts = 1;
 };
 // lds value of the ring-pipelined LDS form (4 waves side by side in n, activation
 // tiles through a 3-buffer LDS ring, weight fragments in a 3-deep register ring)
@@ -62,6 +71,8 @@ constexpr int kRing = 9;
 bool gemm_config_supported(const GemmConfig& c);
 GemmConfig choose_gemm_config(long long rows, int k, int n);
 long long gemm_workgroups(const GemmParams& p, const GemmConfig& c);
+// bytes of GemmParams::ws a launch of shape c needs (0 when c.parts == 1)
+long long gemm_workspace_bytes(const GemmParams& p, const GemmConfig& c);
 
 hipError_t launch_split_bf16(const SplitParams& p, hipStream_t stream);
 hipError_t launch_pack_bf16(const PackParams& p, hipStream_t stream);

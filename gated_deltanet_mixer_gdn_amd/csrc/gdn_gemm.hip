@@ -144,13 +144,19 @@ __global__ __launch_bounds__(256) void project_bf16_kernel(GemmParams p, int til
     const int wn = wave % kWavesN;
     const int wk = wave / kWavesN;
 
-    const int t = xcd_tile(blockIdx.x, tiles_total);
+    // with parts > 1 the grid holds parts x tiles_total workgroups, range-major, so
+    // the workgroups on one XCD share a k range and its activation tiles
+    const int tq = xcd_tile(blockIdx.x, tiles_total * p.parts);
+    const int q = tq / tiles_total;
+    const int t = tq - q * tiles_total;
     const int tm = t % tiles_m;
     const int tn = t / tiles_m;
     const long long m0 = (long long) tm * BM;
     const int n0 = tn * BN + wn * 32 * WN;
     const long long last_rt = (p.rows + kTileRows - 1) / kTileRows - 1;
     const int last_ct = (p.n + kTileRows - 1) / kTileRows - 1;
+    const int c_first = (int) ((long long) q * n_chunks / p.parts);
+    const int c_count = (int) ((long long) (q + 1) * n_chunks / p.parts) - c_first;
 
     const bf16x8* abase[WM];
 #pragma unroll
@@ -198,17 +204,18 @@ __global__ __launch_bounds__(256) void project_bf16_kernel(GemmParams p, int til
     // Two chunks per trip: f0 holds chunk it on entry, f1 is loaded while f0 runs and
     // f0 reloaded while f1 runs.  The scheduling barriers keep the compiler from
     // sinking the loads of the next chunk down to their first use.
-    const int cnt = wk < n_chunks ? (n_chunks - wk + KW - 1) / KW : 0;
+    const int cnt = wk < c_count ? (c_count - wk + KW - 1) / KW : 0;
+    const int c0 = c_first + wk;
     if (cnt > 0) {
         Frag<WM, WN> f0, f1;
-        load(wk, f0);
+        load(c0, f0);
         int it = 0;
         for (; it + 2 <= cnt; it += 2) {
-            load(wk + KW * (it + 1), f1);
+            load(c0 + KW * (it + 1), f1);
             __builtin_amdgcn_sched_barrier(0);
             compute(f0);
             __builtin_amdgcn_sched_barrier(0);
-            load(wk + KW * min(it + 2, cnt - 1), f0);
+            load(c0 + KW * min(it + 2, cnt - 1), f0);
             __builtin_amdgcn_sched_barrier(0);
             compute(f1);
             __builtin_amdgcn_sched_barrier(0);
@@ -242,7 +249,47 @@ __global__ __launch_bounds__(256) void project_bf16_kernel(GemmParams p, int til
         }
     }
 
+    if constexpr (KW == 4) {
+        if (p.parts > 1) {
+            // one wave per workgroup is left: its block is this k range's partial sum
+            float* dst = p.ws + ((long long) t * p.parts + q) * (WM * WN * 16 * 64) + lane;
+#pragma unroll
+            for (int r = 0; r < WM; ++r)
+#pragma unroll
+                for (int c = 0; c < WN; ++c)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) dst[((r * WN + c) * 16 + e) * 64] = acc[r][c][e];
+            return;
+        }
+    }
+
     store_blocks<WM, WN>(p, acc, m0, n0, i, h);
+}
+
+// Second pass of a k-split launch: one wave per tile adds the tile's partial blocks
+// in range order 0, 1, ..., parts - 1 (a fixed order) and stores the tile.
+template <int WM, int WN>
+__global__ __launch_bounds__(256) void add_parts_kernel(GemmParams p, int tiles_m, int tiles_total) {
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= tiles_total) return;
+    const int lane = threadIdx.x & 63;
+    constexpr int kBlk = WM * WN * 16 * 64;
+    const float* src = p.ws + (long long) t * p.parts * kBlk + lane;
+    f16v acc[WM][WN];
+#pragma unroll
+    for (int r = 0; r < WM; ++r)
+#pragma unroll
+        for (int c = 0; c < WN; ++c)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[r][c][e] = src[((r * WN + c) * 16 + e) * 64];
+    for (int j = 1; j < p.parts; ++j)
+#pragma unroll
+        for (int r = 0; r < WM; ++r)
+#pragma unroll
+            for (int c = 0; c < WN; ++c)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) acc[r][c][e] += src[j * kBlk + ((r * WN + c) * 16 + e) * 64];
+    store_blocks<WM, WN>(p, acc, (long long) (t % tiles_m) * 32 * WM, t / tiles_m * 32 * WN, lane & 31, lane >> 5);
 }
 
 // The same product with the activation tiles shared through LDS: a workgroup of
@@ -531,8 +578,16 @@ template <int WM, int WN, int KW>
 hipError_t launch_tile(const GemmParams& p, hipStream_t stream) {
     constexpr int BM = 32 * WM, BN = 32 * WN * (4 / KW);
     const long long tm = (p.rows + BM - 1) / BM, tn = ((long long) p.n + BN - 1) / BN;
-    hipLaunchKernelGGL((project_bf16_kernel<WM, WN, KW>), dim3((unsigned) (tm * tn)), dim3(256), 0, stream, p,
+    hipLaunchKernelGGL((project_bf16_kernel<WM, WN, KW>), dim3((unsigned) (tm * tn * p.parts)), dim3(256), 0, stream, p,
                        (int) tm, (int) (tm * tn), (int) (pad_up(p.k, kTileK) / kTileK));
+    if constexpr (KW == 4) {
+        if (p.parts > 1) {
+            const hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+            hipLaunchKernelGGL((add_parts_kernel<WM, WN>), dim3((unsigned) ((tm * tn + 3) / 4)), dim3(256), 0, stream,
+                               p, (int) tm, (int) (tm * tn));
+        }
+    }
     return hipGetLastError();
 }
 
@@ -557,24 +612,36 @@ hipError_t launch_lds_tile(const GemmParams& p, hipStream_t stream) {
 }  // namespace
 
 bool gemm_config_supported(const GemmConfig& c) {
+    if (c.parts < 1 || (c.parts > 1 && (c.kw != 4 || c.lds != 0))) return false;
     for (const GemmConfig& k : kConfigs)
         if (k.wm == c.wm && k.wn == c.wn && k.kw == c.kw && k.lds == c.lds) return true;
     return false;
 }
 
 long long gemm_workgroups(const GemmParams& p, const GemmConfig& c) {
-    const long long bm = 32LL * c.wm, bn = 32LL * c.wn * (4 / c.kw);
-    return (p.rows + bm - 1) / bm * (((long long) p.n + bn - 1) / bn);
+    const long long bm = 32LL * c.wm, bn = c.lds ? 128LL * c.wn : 32LL * c.wn * (4 / c.kw);
+    return (p.rows + bm - 1) / bm * (((long long) p.n + bn - 1) / bn) * c.parts;
+}
+
+long long gemm_workspace_bytes(const GemmParams& p, const GemmConfig& c) {
+    if (c.parts <= 1) return 0;
+    return gemm_workgroups(p, c) * (c.wm * c.wn * 16 * 64 * (long long) sizeof(float));
 }
 
 // Up to 64 rows the product is bound by the weight stream, and the tile shapes that
 // measured fastest on MI355X for n = 2560 to 16384 are taken by rule: one row tile,
-// the k range split over the 4 waves, wider column tiles as n grows (from 33 rows
-// and n >= 8192, the ring-pipelined LDS form).  Above 64 rows
-// it is bound by the matrix cores and the L2 -> CU operand stream; each candidate
-// shape is priced as (rounds of 256 workgroups) x (chunks per wave) x (32x32 blocks
-// per wave) x (measured microseconds per block-chunk of that shape), which keeps
-// the launch from spilling a few workgroups into a second round.
+// the k range split over the 4 waves, wider column tiles as n grows (the
+// ring-pipelined LDS form for the widest).  A long k range (64 chunks or more) over
+// few tiles leaves most of the chip idle and each wave with a long serial chain, so
+// there the k range is also split over 2 to 4 workgroups per tile (a second kernel
+// adds the partial blocks) until about 192 workgroups run.
+//
+// Above 64 rows each candidate shape is priced as (rounds of 256 workgroups) x
+// (chunks per wave) x (32x32 blocks per wave) x (measured microseconds per
+// block-chunk of that shape), plus 8 us for the second kernel of a split launch
+// (fitted to graph-replayed timings on MI355X, k = 2560 and 6144, n = 1024 to
+// 16384), which keeps the launch from spilling a few workgroups into a second round
+// and splits k only where the shorter chains pay for that kernel.
 namespace {
 struct Priced {
     GemmConfig c;
@@ -583,29 +650,46 @@ struct Priced {
 };
 constexpr Priced kPriced[] = {
     {{2, 2, 1, 0}, 0.245, 65}, {{2, 3, 2, 0}, 0.31, 65}, {{2, 2, 2, 0}, 0.305, 65}, {{2, 2, 4, 0}, 0.33, 65},
-    {{2, 3, 4, 0}, 0.38, 65},  {{2, 1, 4, 0}, 0.42, 65}, {{2, 3, 1, 2}, 0.46, 257},
-    {{1, 1, 1, kRing}, 0.34, 65},
+    {{2, 3, 4, 0}, 0.38, 65},  {{2, 1, 4, 0}, 0.47, 65}, {{2, 3, 1, 2}, 0.46, 257}, {{1, 1, 1, kRing}, 0.34, 65},
+    {{1, 2, 4, 0}, 0.42, 65},  {{1, 1, 4, 0}, 0.65, 65},
 };
+constexpr double kSplitUs = 8.0;
+constexpr int kMaxParts = 4;
+constexpr long long kSplitMinChunks = 64;
 }  // namespace
 
 GemmConfig choose_gemm_config(long long rows, int k, int n) {
-    if (rows <= 32) return n >= 8192 ? GemmConfig{1, 2, 4, 0} : GemmConfig{1, 1, 4, 0};
-    if (rows <= 64) return n >= 8192 ? GemmConfig{1, 1, 1, kRing} : n >= 4096 ? GemmConfig{1, 2, 4, 0} : GemmConfig{1, 1, 4, 0};
     const long long chunks = pad_up(k, kTileK) / kTileK;
     GemmParams p{};
     p.rows = rows;
     p.n = n;
+    if (rows <= 64) {
+        GemmConfig c = rows <= 32 ? (n >= 12288 ? GemmConfig{1, 1, 1, kRing}
+                                    : n >= 8192 ? GemmConfig{1, 2, 4, 0} : GemmConfig{1, 1, 4, 0})
+                                  : (n >= 8192 ? GemmConfig{1, 1, 1, kRing}
+                                    : n >= 4096 ? GemmConfig{1, 2, 4, 0} : GemmConfig{1, 1, 4, 0});
+        if (chunks >= kSplitMinChunks && c.kw == 4 && c.lds == 0) {
+            const long long w0 = gemm_workgroups(p, c);
+            if (w0 <= 128) c.parts = (int) std::min<long long>(kMaxParts, (192 + w0 - 1) / w0);
+        }
+        return c;
+    }
     GemmConfig best = kPriced[0].c;
     double best_us = -1.0;
     for (const Priced& q : kPriced) {
         if (rows < q.min_rows) continue;
         const long long split = q.c.lds == kRing ? 1 : q.c.lds ? q.c.lds : q.c.kw;
-        const long long rounds = (gemm_workgroups(p, q.c) + 255) / 256;
-        const double us = (double) rounds * (double) ((chunks + split - 1) / split) * q.c.wm * q.c.wn *
-                          q.us_per_block_chunk;
-        if (best_us < 0.0 || us < best_us) {
-            best = q.c;
-            best_us = us;
+        const bool can_split = chunks >= kSplitMinChunks && q.c.wm == 1 && q.c.kw == 4 && q.c.lds == 0;
+        for (int parts = 1; parts <= (can_split ? kMaxParts : 1); ++parts) {
+            GemmConfig c = q.c;
+            c.parts = parts;
+            const long long rounds = (gemm_workgroups(p, c) + 255) / 256;
+            const double us = (double) rounds * (double) ((chunks + split * parts - 1) / (split * parts)) * c.wm *
+                                  c.wn * q.us_per_block_chunk + (parts > 1 ? kSplitUs : 0.0);
+            if (best_us < 0.0 || us < best_us) {
+                best = c;
+                best_us = us;
+            }
         }
     }
     return best;
@@ -626,6 +710,8 @@ hipError_t launch_pack_bf16(const PackParams& p, hipStream_t stream) {
 }
 
 hipError_t launch_project_bf16(const GemmParams& p, const GemmConfig& c, hipStream_t stream) {
+    if (p.parts != c.parts || (c.parts > 1 && (p.ws == nullptr || c.kw != 4 || c.lds != 0)))
+        return hipErrorInvalidValue;
 #define GDN_TILE(A, B, C) \
     if (!c.lds && c.wm == A && c.wn == B && c.kw == C) return launch_tile<A, B, C>(p, stream);
 #define GDN_LDS_TILE(A, B, G) \

@@ -23,7 +23,7 @@ EXPORTS = (
     "gdn_state_pool_slots", "gdn_state_pool_zero", "gdn_conv_silu_norm", "gdn_decode_step",
     "gdn_decode_step_norm", "gdn_decode_fused", "gdn_verify_window", "gdn_commit", "gdn_gated_rmsnorm",
     "gdn_ab_project", "gdn_split_bf16_bytes", "gdn_pack_bf16_bytes", "gdn_split_bf16", "gdn_pack_bf16",
-    "gdn_project_bf16", "gdn_project2_bf16",
+    "gdn_project_bf16", "gdn_project2_bf16", "gdn_project_workspace_bytes",
 )
 
 
@@ -98,8 +98,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "gdn_pack_bf16_bytes": ([i32, i32], ctypes.c_int64),
         "gdn_split_bf16": ([vp, i64, i32, vp, vp], ctypes.c_int),
         "gdn_pack_bf16": ([vp, i32, i32, vp, vp], ctypes.c_int),
-        "gdn_project2_bf16": ([vp, vp, i64, i32, i32, vp, i32, vp, vp], ctypes.c_int),
-        "gdn_project_bf16": ([vp, vp, i64, i32, i32, vp, vp], ctypes.c_int),
+        "gdn_project2_bf16": ([vp, vp, i64, i32, i32, vp, i32, vp, vp, i64, vp], ctypes.c_int),
+        "gdn_project_bf16": ([vp, vp, i64, i32, i32, vp, vp, i64, vp], ctypes.c_int),
+        "gdn_project_workspace_bytes": ([i64, i32, i32], ctypes.c_int64),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -372,8 +373,31 @@ def gdn_pack_bf16(w) -> PackedW:
     return PackedW(wp, n, k)
 
 
-def gdn_project_bf16(xs: SplitX, wp: PackedW, out=None):
-    """out [rows][n] fp32 = x @ w^T from the split activations and the packed weights."""
+def gdn_project_workspace_bytes(rows: int, k: int, n: int) -> int:
+    """Device workspace the product rows x k x n needs (0 for most shapes)."""
+    nbytes = load_library().gdn_project_workspace_bytes(rows, k, n)
+    if nbytes < 0:
+        raise ValueError(f"bad projection shape rows={rows} k={k} n={n}")
+    return nbytes
+
+
+def _workspace(rows, k, n, device, workspace):
+    """(pointer, bytes, keep-alive) of the projection workspace: the caller's tensor, or
+    a fresh one from torch's allocator when the shape needs one."""
+    import torch
+    if workspace is not None:
+        return workspace.data_ptr(), workspace.numel() * workspace.element_size(), workspace
+    nbytes = gdn_project_workspace_bytes(rows, k, n)
+    if nbytes == 0:
+        return None, 0, None
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    return ws.data_ptr(), nbytes, ws
+
+
+def gdn_project_bf16(xs: SplitX, wp: PackedW, out=None, workspace=None):
+    """out [rows][n] fp32 = x @ w^T from the split activations and the packed weights.
+    workspace: optional device tensor of gdn_project_workspace_bytes(rows, k, n) bytes
+    (allocated here when the shape needs one and none is given)."""
     import torch
     if xs.k != wp.k:
         raise ValueError(f"x has k={xs.k}, w has k={wp.k}")
@@ -381,12 +405,13 @@ def gdn_project_bf16(xs: SplitX, wp: PackedW, out=None):
         out = torch.empty(xs.rows, wp.n, dtype=torch.float32, device=xs.data.device)
     if out.numel() != xs.rows * wp.n:
         raise ValueError(f"out must hold {xs.rows * wp.n} elements")
+    ws, ws_bytes, _keep = _workspace(xs.rows, xs.k, wp.n, xs.data.device, workspace)
     _check(load_library().gdn_project_bf16(xs.data.data_ptr(), wp.data.data_ptr(), xs.rows, xs.k, wp.n,
-                                           _f32(out, "out"), _stream(xs.data)))
+                                           _f32(out, "out"), ws, ws_bytes, _stream(xs.data)))
     return out
 
 
-def gdn_project2_bf16(xs: SplitX, wp: PackedW, n1: int, out1=None, out2=None):
+def gdn_project2_bf16(xs: SplitX, wp: PackedW, n1: int, out1=None, out2=None, workspace=None):
     """Two projections of the same activations in one launch: wp packs the
     concatenation [w1; w2] (n1 + n2 rows); returns (out1 [rows][n1], out2 [rows][n2])."""
     import torch
@@ -398,8 +423,10 @@ def gdn_project2_bf16(xs: SplitX, wp: PackedW, n1: int, out1=None, out2=None):
     out2 = torch.empty(xs.rows, n2, device=dev) if out2 is None else out2
     if out1.numel() != xs.rows * n1 or out2.numel() != xs.rows * n2:
         raise ValueError("out1 / out2 have the wrong size")
+    ws, ws_bytes, _keep = _workspace(xs.rows, xs.k, wp.n, dev, workspace)
     _check(load_library().gdn_project2_bf16(xs.data.data_ptr(), wp.data.data_ptr(), xs.rows, xs.k, n1,
-                                            _f32(out1, "out1"), n2, _f32(out2, "out2"), _stream(xs.data)))
+                                            _f32(out1, "out1"), n2, _f32(out2, "out2"), ws, ws_bytes,
+                                            _stream(xs.data)))
     return out1, out2
 
 

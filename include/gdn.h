@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 2
+#define GDN_ABI_VERSION 3
 
 enum {
     GDN_OK = 0,
@@ -274,21 +274,34 @@ int gdn_split_bf16(const float* x, int64_t rows, int32_t k, uint16_t* xs, void* 
  * bytes, 16-byte aligned, not overlapping w).  n >= 1. */
 int gdn_pack_bf16(const uint16_t* w, int32_t n, int32_t k, uint16_t* wp, void* stream);
 
+/* Device workspace, in bytes, that gdn_project_bf16 / gdn_project2_bf16 need for a
+ * product of rows x k x n (n = n1 + n2 for the two-output form), or -1 for a negative
+ * rows or a bad k or n.  It is 0 unless the launch picked for the shape splits a long
+ * k range over several workgroups per output tile (at most 64 KiB per 32-row x
+ * 128-column share of the output); then the partial sums go through the workspace
+ * and a second kernel adds them in a fixed order. */
+int64_t gdn_project_workspace_bytes(int64_t rows, int32_t k, int32_t n);
+
 /* xs from gdn_split_bf16 for [rows][k]; wp from gdn_pack_bf16 for [n][k]; out
- * [rows][n] fp32, 4-byte aligned, overlapping neither input.  rows = 0 is a no-op.
- * For one (rows, k, n) the result is the same on every call (a fixed summation
- * order). */
+ * [rows][n] fp32, 4-byte aligned, overlapping neither input.  workspace: device
+ * memory of workspace_bytes >= gdn_project_workspace_bytes(rows, k, n) bytes,
+ * 16-byte aligned, overlapping no other argument (NULL with 0 when that is 0);
+ * its contents are scratch before and after the call, and calls that share one
+ * must be ordered (one stream).  A smaller workspace is an argument error.
+ * rows = 0 is a no-op.  For one (rows, k, n) the result is the same on every call
+ * (a fixed summation order). */
 int gdn_project_bf16(const uint16_t* xs, const uint16_t* wp, int64_t rows, int32_t k, int32_t n, float* out,
-                     void* stream);
+                     void* workspace, int64_t workspace_bytes, void* stream);
 
 /* Two projections of the same activations in one launch (qkv and z both read the
  * layer input): wp is gdn_pack_bf16 of the (n1 + n2) x k matrix whose first n1 rows
  * are the first weight matrix and whose last n2 rows are the second; columns j < n1
  * of the product go to out1 [rows][n1], the others to out2 [rows][n2] (4-byte
- * aligned, overlapping neither each other nor an input).  n1, n2 >= 1.  Each output
- * equals gdn_project_bf16 of the concatenated weights, column for column. */
+ * aligned, overlapping neither each other nor an input).  n1, n2 >= 1.  The workspace
+ * is that of gdn_project_bf16 for n = n1 + n2.  Each output equals gdn_project_bf16
+ * of the concatenated weights, column for column. */
 int gdn_project2_bf16(const uint16_t* xs, const uint16_t* wp, int64_t rows, int32_t k, int32_t n1, float* out1,
-                      int32_t n2, float* out2, void* stream);
+                      int32_t n2, float* out2, void* workspace, int64_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -47,6 +47,18 @@ def test_library_exports_every_declared_symbol(L):
     assert exported == set(declared_functions())
 
 
+def test_package_reexports_every_binding():
+    """Every public function and class of the binding module is reachable from the
+    package, where the tests and callers look for it."""
+    import inspect
+    import gated_deltanet_mixer_gdn_amd as G
+    from gated_deltanet_mixer_gdn_amd import gdn
+    public = [name for name, obj in vars(gdn).items()
+              if not name.startswith("_") and (inspect.isfunction(obj) or inspect.isclass(obj))
+              and obj.__module__ == gdn.__name__]
+    assert public and [name for name in public if not hasattr(G, name)] == []
+
+
 def test_library_is_built_for_gfx950_only(tmp_path):
     from gated_deltanet_mixer_gdn_amd import gdn
     fb = tmp_path / "fatbin.bin"
@@ -59,7 +71,7 @@ def test_library_is_built_for_gfx950_only(tmp_path):
 
 
 def test_abi_version(L):
-    assert L.gdn_abi_version() == 2
+    assert L.gdn_abi_version() == 3
 
 
 def _geom(h_k=16, h_v=48, s=128, d_conv=4):
@@ -225,7 +237,7 @@ def test_projection_argument_errors(L):
     assert L.gdn_pack_bf16_bytes(100, 136) == 128 * 192 * 2
     assert L.gdn_pack_bf16_bytes(0, 64) == -1 and L.gdn_pack_bf16_bytes(4, 0) == -1
     assert L.gdn_split_bf16_bytes(1, (1 << 24) + 8) == -1 and L.gdn_pack_bf16_bytes(1, (1 << 24) + 8) == -1
-    assert L.gdn_project_bf16(16, 16, 4, (1 << 24) + 8, 32, 1 << 20, None) == GDN_ERR_ARG
+    assert L.gdn_project_bf16(16, 16, 4, (1 << 24) + 8, 32, 1 << 20, None, 0, None) == GDN_ERR_ARG
     assert b"at most" in L.gdn_last_error()
     assert L.gdn_split_bf16(16, -1, 64, 16, None) == GDN_ERR_ARG
     assert L.gdn_split_bf16(16, 4, 60, 16, None) == GDN_ERR_ARG
@@ -239,20 +251,55 @@ def test_projection_argument_errors(L):
     assert L.gdn_pack_bf16(24, 4, 64, 1 << 20, None) == GDN_ERR_ARG
     assert L.gdn_pack_bf16(1 << 20, 32, 64, (1 << 20) + 64, None) == GDN_ERR_ARG
     assert b"wp overlaps w" in L.gdn_last_error()
-    assert L.gdn_project_bf16(16, 16, -1, 64, 32, 16, None) == GDN_ERR_ARG
-    assert L.gdn_project_bf16(16, 16, 4, 12, 32, 1 << 20, None) == GDN_ERR_ARG
-    assert L.gdn_project_bf16(16, 16, 4, 64, 0, 1 << 20, None) == GDN_ERR_ARG
-    assert L.gdn_project_bf16(16, 24, 4, 64, 32, 1 << 20, None) == GDN_ERR_ARG
+    assert L.gdn_project_bf16(16, 16, -1, 64, 32, 16, None, 0, None) == GDN_ERR_ARG
+    assert L.gdn_project_bf16(16, 16, 4, 12, 32, 1 << 20, None, 0, None) == GDN_ERR_ARG
+    assert L.gdn_project_bf16(16, 16, 4, 64, 0, 1 << 20, None, 0, None) == GDN_ERR_ARG
+    assert L.gdn_project_bf16(16, 24, 4, 64, 32, 1 << 20, None, 0, None) == GDN_ERR_ARG
     assert b"wp is not 16-byte aligned" in L.gdn_last_error()
-    assert L.gdn_project_bf16(1 << 20, 1 << 24, 4, 64, 32, (1 << 20) + 64, None) == GDN_ERR_ARG
+    assert L.gdn_project_bf16(1 << 20, 1 << 24, 4, 64, 32, (1 << 20) + 64, None, 0, None) == GDN_ERR_ARG
     assert b"output overlaps xs" in L.gdn_last_error()
-    assert L.gdn_project_bf16(1 << 24, 1 << 20, 4, 64, 32, (1 << 20) + 64, None) == GDN_ERR_ARG
+    assert L.gdn_project_bf16(1 << 24, 1 << 20, 4, 64, 32, (1 << 20) + 64, None, 0, None) == GDN_ERR_ARG
     assert b"output overlaps wp" in L.gdn_last_error()
-    assert L.gdn_project_bf16(None, None, 0, 64, 32, None, None) == GDN_OK
-    assert L.gdn_project2_bf16(16, 16, 4, 64, 32, 1 << 20, 0, 1 << 22, None) == GDN_ERR_ARG
-    assert L.gdn_project2_bf16(16, 16, 4, 64, 0, 1 << 20, 32, 1 << 22, None) == GDN_ERR_ARG
-    assert L.gdn_project2_bf16(16, 16, 4, 64, 32, 1 << 20, 32, (1 << 20) + 256, None) == GDN_ERR_ARG
+    assert L.gdn_project_bf16(None, None, 0, 64, 32, None, None, 0, None) == GDN_OK
+    assert L.gdn_project2_bf16(16, 16, 4, 64, 32, 1 << 20, 0, 1 << 22, None, 0, None) == GDN_ERR_ARG
+    assert L.gdn_project2_bf16(16, 16, 4, 64, 0, 1 << 20, 32, 1 << 22, None, 0, None) == GDN_ERR_ARG
+    assert L.gdn_project2_bf16(16, 16, 4, 64, 32, 1 << 20, 32, (1 << 20) + 256, None, 0, None) == GDN_ERR_ARG
     assert b"out1 overlaps out2" in L.gdn_last_error()
-    assert L.gdn_project2_bf16(16, 16, 4, 64, 32, 1 << 20, 32, 2, None) == GDN_ERR_ARG
+    assert L.gdn_project2_bf16(16, 16, 4, 64, 32, 1 << 20, 32, 2, None, 0, None) == GDN_ERR_ARG
     assert b"out2 is not 4-byte aligned" in L.gdn_last_error()
-    assert L.gdn_project2_bf16(None, None, 0, 64, 32, None, 16, None, None) == GDN_OK
+    assert L.gdn_project2_bf16(None, None, 0, 64, 32, None, 16, None, None, 0, None) == GDN_OK
+
+
+def test_projection_workspace(L):
+    """The workspace is 0 bytes unless a long k range meets few output tiles; a launch
+    that needs one refuses a missing, short, misaligned or overlapping workspace before
+    anything runs (every call below fails its checks)."""
+    from gated_deltanet_mixer_gdn_amd.gdn import GDN_ERR_ARG, GDN_OK
+    W = L.gdn_project_workspace_bytes
+    assert W(256, 2560, 16384) == 0 and W(1, 2560, 2560) == 0 and W(0, 6144, 2560) == 0
+    # 1 row, out projection: 80 tiles of 32 x 32, k split 3 ways, one 4 KiB block each
+    assert W(1, 6144, 2560) == 80 * 3 * 4096 == W(32, 6144, 2560)
+    # 100 rows, 1000 columns: 4 x 16 tiles of 32 x 64 split 4 ways, 8 KiB blocks
+    assert W(100, 6144, 1000) == 4 * 16 * 4 * 8192
+    assert W(256, 6144, 2560) == 0 and W(96, 6144, 2560) == 0
+    assert W(-1, 64, 32) == -1 and W(4, 12, 32) == -1 and W(4, 64, 0) == -1 and W(4, (1 << 24) + 8, 32) == -1
+    xs, wp, out, ws = 1 << 30, 2 << 30, 3 << 30, 4 << 30
+    need = W(1, 6144, 2560)
+    assert L.gdn_project_bf16(xs, wp, 1, 6144, 2560, out, None, 0, None) == GDN_ERR_ARG
+    assert b"the launch needs %d" % need in L.gdn_last_error()
+    assert L.gdn_project_bf16(xs, wp, 1, 6144, 2560, out, ws, need - 16, None) == GDN_ERR_ARG
+    assert L.gdn_project_bf16(xs, wp, 1, 6144, 2560, out, None, need, None) == GDN_ERR_ARG
+    assert b"workspace is null" in L.gdn_last_error()
+    assert L.gdn_project_bf16(xs, wp, 1, 6144, 2560, out, ws + 8, need, None) == GDN_ERR_ARG
+    assert b"workspace is not 16-byte aligned" in L.gdn_last_error()
+    assert L.gdn_project_bf16(xs, wp, 1, 6144, 2560, out, xs + 4096, need, None) == GDN_ERR_ARG
+    assert b"workspace overlaps xs" in L.gdn_last_error()
+    assert L.gdn_project_bf16(xs, wp, 1, 6144, 2560, out, wp - 4096, need, None) == GDN_ERR_ARG
+    assert b"workspace overlaps wp" in L.gdn_last_error()
+    assert L.gdn_project_bf16(xs, wp, 1, 6144, 2560, out, out - 16, need, None) == GDN_ERR_ARG
+    assert b"workspace overlaps out" in L.gdn_last_error()
+    assert L.gdn_project2_bf16(xs, wp, 1, 6144, 2000, out, 560, out + 8192, out + 8192 + 16, need, None) == GDN_ERR_ARG
+    assert b"workspace overlaps out2" in L.gdn_last_error()
+    assert L.gdn_project_bf16(xs, wp, 1, 6144, 2560, out, ws, -1, None) == GDN_ERR_ARG
+    assert b"negative" in L.gdn_last_error()
+    assert L.gdn_project_bf16(None, None, 0, 6144, 2560, None, None, 0, None) == GDN_OK

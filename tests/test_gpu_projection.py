@@ -72,12 +72,14 @@ def test_pack_is_a_permutation_with_zero_padding():
 # (rows, k, n): a single row, ragged rows / columns / k, several tiles of each shape, and
 # the tile shapes the launch picks by rows, k and n (one or two row tiles per
 # workgroup, 1-3 column tiles per wave, k split over 1, 2 or 4 waves, and the
-# ring-pipelined LDS form with 1, 2, 3 and 4 chunks); the two-group LDS form, picked
-# only for long k at more than 256 rows, has its own sampled test below
+# ring-pipelined LDS form with 1, 2, 3 and 4 chunks, from 1 row up); the two-group LDS
+# form, picked only for long k at more than 256 rows, and the k range split over
+# workgroups, picked only for long k, have their own tests below
 SHAPES = [(1, 64, 32), (3, 72, 40), (33, 136, 100), (64, 2560, 256), (70, 520, 300), (200, 520, 1030),
           (37, 6144, 96), (1, 2560, 10240), (16, 2560, 6144), (300, 128, 4100), (50, 200, 8200),
           (40, 136, 5000), (100, 264, 8300), (150, 136, 4500), (250, 72, 8250), (300, 200, 9000),
-          (300, 136, 8200), (600, 64, 8192), (40, 64, 9000), (60, 120, 8300), (45, 136, 8200)]
+          (300, 136, 8200), (600, 64, 8192), (40, 64, 9000), (60, 120, 8300), (45, 136, 8200),
+          (1, 200, 12300), (8, 2560, 16384)]
 
 
 @pytest.mark.parametrize("rows,k,n", SHAPES)
@@ -123,7 +125,8 @@ def test_projection_lds_form_sampled(rows, k):
     assert_close("out", out.cpu().numpy()[pick], oracle.project(x[pick], w), TOL)
 
 
-@pytest.mark.parametrize("rows,k,n1,n2", [(256, 2560, 10240, 6144), (37, 200, 100, 60), (300, 136, 8192, 40)])
+@pytest.mark.parametrize("rows,k,n1,n2", [(256, 2560, 10240, 6144), (37, 200, 100, 60), (300, 136, 8192, 40),
+                                          (20, 4104, 3000, 1000)])
 def test_two_outputs_equal_the_concatenated_projection(rows, k, n1, n2):
     """gdn_project2_bf16 (qkv and z in one launch) writes, column for column, what
     gdn_project_bf16 writes for the concatenated weights, and matches the oracle."""
@@ -143,10 +146,52 @@ def test_two_outputs_equal_the_concatenated_projection(rows, k, n1, n2):
     assert_close("out2", o2.cpu().numpy()[pick], ref[:, n1:], TOL)
 
 
-def test_projection_is_deterministic():
+# (rows, k, n) whose launch splits the k range over 4, 3 or 2 workgroups per tile and
+# adds the partial blocks in a second kernel: up to 64 rows with the tile the rules
+# pick (one and two row tiles, ragged k, rows and columns), and above 64 rows with
+# the 32 x 64 tiles the priced choice splits 4 and 3 ways (ragged rows and columns)
+SPLIT_SHAPES = [(1, 6144, 2560), (5, 4104, 1000), (20, 4104, 4000), (50, 4096, 1500), (64, 6144, 4096),
+                (70, 6144, 1000), (100, 6144, 1000), (200, 6144, 700)]
+
+
+@pytest.mark.parametrize("rows,k,n", SPLIT_SHAPES)
+def test_projection_split_k_matches_oracle(rows, k, n):
     import torch
     import gated_deltanet_mixer_gdn_amd as G
-    x, w = W.make_proj(256, 6144, 2560, seed=98)
+    assert G.gdn_project_workspace_bytes(rows, k, n) > 0, "the shape no longer splits its k range"
+    log(f"projection (k split) rows={rows} k={k} n={n}")
+    x, w = W.make_proj(rows, k, n, seed=120 + rows + n)
+    out = torch.full((rows, n), 7.0, device="cuda")
+    G.gdn_project(dev(x), G.gdn_pack_bf16(_w(w)), out)
+    torch.cuda.synchronize()
+    assert_close("out", out.cpu().numpy(), oracle.project(x, w), TOL)
+
+
+def test_projection_workspace_is_scratch():
+    """A caller's workspace full of NaN gives, bit for bit, what a fresh one gives, and
+    one workspace serves two calls in a row, the second with fewer rows."""
+    import torch
+    import gated_deltanet_mixer_gdn_amd as G
+    k, n = W.PROJECTIONS["out"]
+    x, w = W.make_proj(32, k, n, seed=125)
+    wp = G.gdn_pack_bf16(_w(w))
+    ws = torch.full((G.gdn_project_workspace_bytes(32, k, n) // 4,), float("nan"), device="cuda")
+    log(f"workspace of {ws.numel() * 4} bytes")
+    ref32 = G.gdn_project(dev(x), wp)
+    ref1 = G.gdn_project(dev(x[:1]), wp)
+    a = G.gdn_project_bf16(G.gdn_split_bf16(dev(x)), wp, workspace=ws)
+    b = G.gdn_project_bf16(G.gdn_split_bf16(dev(x[:1])), wp, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(a, ref32) and torch.equal(b, ref1)
+    assert_close("out", a.cpu().numpy(), oracle.project(x, w), TOL)
+
+
+@pytest.mark.parametrize("rows", [256, 1])
+def test_projection_is_deterministic(rows):
+    """Same inputs, same bits: the k-split launch (1 row) adds its parts in a fixed order."""
+    import torch
+    import gated_deltanet_mixer_gdn_amd as G
+    x, w = W.make_proj(rows, 6144, 2560, seed=98)
     xs = G.gdn_split_bf16(dev(x))
     wp = G.gdn_pack_bf16(_w(w))
     a = G.gdn_project_bf16(xs, wp)
