@@ -133,7 +133,9 @@ def copy_probe(mib: int, reps: int = 5):
 
 def gpu_clocks():
     """Current GPU clocks as amd-smi reports them (JSON), or None if the tool is absent or
-    fails; run as a child process, after the timed region."""
+    fails; run as a child process, after the timed region, and only on request
+    (--clocks): under a profiler that preloads itself into every process, the tool's
+    interpreter launcher would replace a process that has already opened the GPU."""
     import subprocess
     for cmd in (["amd-smi", "metric", "--gpu", "0", "--clock", "--json"],
                 ["rocm-smi", "--showclocks", "--json"]):
@@ -200,6 +202,7 @@ def main():
     ap.add_argument("--config", default="b256", choices=["tiny", "b64", "b256", "prefill", "ragged"])
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--clocks", action="store_true", help="report amd-smi clocks after the timed region")
     ap.add_argument("--copy-probe-mib", type=int, default=0)
     ap.add_argument("--event-every", type=int, default=8,
                     help="record per-kernel HIP events on every N-th timed step")
@@ -371,7 +374,7 @@ def main():
     log("three calls: " + ", ".join(f"{k}={v * 1000:.1f}us" for k, v in three_k.items()) +
         f"; {three_ms * 1000:.1f} us/step; recurrence kernel {three_step_gbps:.0f} GB/s; d2d copy {copy_gbps:.0f} GB/s")
     traffic = read_traffic() if args.config == "b256" else None
-    clocks = gpu_clocks()
+    clocks = gpu_clocks() if args.clocks else None
 
     cpu = None
     if not args.no_cpu_baseline:

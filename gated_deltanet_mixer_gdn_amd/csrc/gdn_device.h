@@ -98,6 +98,20 @@ __device__ __forceinline__ f4 add_xor32(f4 v) {
     return f4{add_xor32(v.x), add_xor32(v.y), add_xor32(v.z), add_xor32(v.w)};
 }
 
+// Reduce-scatter of the 4 components of v over the lanes lane, lane ^ 16, lane ^ 32 and
+// lane ^ 48: each lane ends with the total of one component, added in the order
+// add_xor32(add_xor16(.)) adds it, at a third of the instructions (one swap moves a
+// component each way).  Which component a lane gets depends only on its lane bits 4
+// and 5; scatter_sum4(f4{0, 1, 2, 3}) / 4 names it.  All 64 lanes must be active.
+__device__ __forceinline__ float scatter_sum4(f4 v) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v.x), __float_as_uint(v.z), false, false);
+    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v.y), __float_as_uint(v.w), false, false);
+    const float u = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const float w = __uint_as_float(b[0]) + __uint_as_float(b[1]);
+    const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(u), __float_as_uint(w), false, false);
+    return __uint_as_float(c[0]) + __uint_as_float(c[1]);
+}
+
 // Sum over each 8-lane block, then over the 32 lanes of a half-wave (lanes 0-31 or
 // 32-63); every lane gets the sum.  The fused norms of the recurrence kernels use
 // the same order: 8-lane (32-column) blocks b0..b3, then (b0+b1)+(b2+b3).

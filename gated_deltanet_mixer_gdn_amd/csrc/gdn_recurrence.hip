@@ -309,18 +309,20 @@ __global__ __launch_bounds__(256) void decode_fused_kernel(FusedParams p) {
 // rows: lane l has columns 32w + 4*(l % 8) .. +3 of rows 16*(l / 8) .. +15.  The
 // column sums then reduce inside the wave (xor-shuffles over the 8 row groups), the
 // q/k rows are staged in a wave-private LDS slot, and each token's inputs are
-// loaded one token ahead, so the token loop itself has no barrier.
-// kNorm: each wave parks its o columns and its sum of o^2 in an 8-token LDS ring;
-// every 8 tokens the workgroup synchronises once and normalises that chunk
-// cooperatively (thread -> token tid/32, columns 4*(tid%32)..+3), with the chunk's
-// z loaded one chunk ahead.
+// loaded one token ahead, so the token loop itself has no barrier.  The k sums
+// (needed by every lane for the update) are summed in every lane; the q sums only
+// feed the readout and are reduce-scattered, so each lane reads out one column
+// (lanes 8..15 of each row repeat lanes 0..7).
+// kNorm: each wave parks its o columns in an 8-token LDS ring; every 8 tokens the
+// workgroup synchronises once and normalises that chunk cooperatively (thread ->
+// token tid/32, columns 4*(tid%32)..+3, the sum of o^2 over a half-wave in the
+// single-token kernel's order), with the chunk's z loaded one chunk ahead.
 constexpr int kNormChunk = 8;
 
 template <bool kNorm>
 __global__ __launch_bounds__(256) void decode_multi_kernel(StepParams p) {
     __shared__ f4 qk_lds[4][64];                    // per wave: q as 32 float4, then k as 32 float4
     __shared__ f4 o_ring[2][kNormChunk][32];        // [chunk parity][token][float4 column group]
-    __shared__ float ss_ring[2][kNormChunk][4];     // [chunk parity][token][wave]
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -338,6 +340,9 @@ __global__ __launch_bounds__(256) void decode_multi_kernel(StepParams p) {
     // chunk normalisation: this thread's token within a chunk and columns
     const int n_tt = tid >> 5;
     const int n_c4 = (tid & 31) * 4;
+    // the column of its 4 whose q sum a lane ends with after scatter_sum4
+    const int oc = (int) (scatter_sum4(f4{0.f, 1.f, 2.f, 3.f}) * 0.25f);
+    const bool reads_out = (lane & 8) == 0;
 
     float* tile = nullptr;
     f4 s[16];
@@ -404,31 +409,28 @@ __global__ __launch_bounds__(256) void decode_multi_kernel(StepParams p) {
         // sum over the 8 row groups of the wave (lane bits 3..5):
         // ((g0+g1)+(g2+g3))+((g4+g5)+(g6+g7)), as in the single-token kernel
         pk = add_xor32(add_xor16(add_xor8(pk)));
-        pq = add_xor32(add_xor16(add_xor8(pq)));
         kq = add_xor32(add_xor16(add_xor8(kq)));
+        const float pqc = scatter_sum4(add_xor8(pq));
         const f4 d = beta * fma4(-eg, pk, v);
-        f4 out = fma4(kq, d, eg * pq);
-        if (p.oscale != 1.0f) out *= p.oscale;
-        if (p.o && rg == 0) *(f4*) (p.o + ((tok0 + t) * p.h_v + i) * kS + col) = out;
+        const float dc = oc == 0 ? d.x : oc == 1 ? d.y : oc == 2 ? d.z : d.w;
+        // the readout of column col + oc (a scale of 1 multiplies exactly)
+        const float out = __builtin_fmaf(kq, dc, eg * pqc) * p.oscale;
+        if (p.o && reads_out) p.o[((tok0 + t) * p.h_v + i) * kS + col + oc] = out;
         if (kNorm) {
             const int par = (t / kNormChunk) & 1;
             const int slot8 = t % kNormChunk;
-            // sum of o^2 over this wave's 32 columns (lane bits 0..2)
-            const float ss = block8_sum(sumsq4(out));
-            if (rg == 0) o_ring[par][slot8][wave * 8 + cg] = out;
-            if (lane == 0) ss_ring[par][slot8][wave] = ss;
+            if (reads_out) ((float*) o_ring[par][slot8])[wave * 32 + cg * 4 + oc] = out;
             if (slot8 == kNormChunk - 1 || t == nt - 1) {   // uniform over the workgroup
                 __syncthreads();
                 const int t0c = t - slot8;
                 const f4 zz = z_n;
                 if (t0c + kNormChunk < nt) fetch_z(t0c + kNormChunk);
-                if (n_tt <= slot8) {
-                    const float tot = (ss_ring[par][n_tt][0] + ss_ring[par][n_tt][1]) +
-                                      (ss_ring[par][n_tt][2] + ss_ring[par][n_tt][3]);
-                    const float inv = rms_inv(tot, p.eps);
+                if (n_tt <= slot8) {   // whole half-waves, as halfwave_sum needs
+                    const f4 o4 = o_ring[par][n_tt][n_c4 / 4];
+                    const float inv = rms_inv(halfwave_sum(sumsq4(o4)), p.eps);
                     const f4 wn = *(const f4*) (p.norm_w + n_c4);
                     *(f4*) (p.y + ((tok0 + t0c + n_tt) * p.h_v + i) * kS + n_c4) =
-                        o_ring[par][n_tt][n_c4 / 4] * inv * wn * gate4(zz, p.gate_silu);
+                        o4 * inv * wn * gate4(zz, p.gate_silu);
                 }
             }
         }
