@@ -112,6 +112,18 @@ __device__ __forceinline__ float scatter_sum4(f4 v) {
     return __uint_as_float(c[0]) + __uint_as_float(c[1]);
 }
 
+// The inverse placement of scatter_sum4: lane holds one value of the 4-lane group
+// (lane, lane ^ 16, lane ^ 32, lane ^ 48) in the slot scatter_sum4 gives it; every lane
+// gets the group's 4 values in component order.  Each level swaps a value with itself,
+// which puts the even row's (or low half's) value first whichever way the swap
+// instruction pairs its operands.  All 64 lanes must be active.
+__device__ __forceinline__ f4 gather4(float v) {
+    const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    const auto a = __builtin_amdgcn_permlane16_swap(h[0], h[0], false, false);
+    const auto b = __builtin_amdgcn_permlane16_swap(h[1], h[1], false, false);
+    return f4{__uint_as_float(a[0]), __uint_as_float(b[0]), __uint_as_float(a[1]), __uint_as_float(b[1])};
+}
+
 // Sum over each 8-lane block, then over the 32 lanes of a half-wave (lanes 0-31 or
 // 32-63); every lane gets the sum.  The fused norms of the recurrence kernels use
 // the same order: 8-lane (32-column) blocks b0..b3, then (b0+b1)+(b2+b3).

@@ -309,10 +309,10 @@ __global__ __launch_bounds__(256) void decode_fused_kernel(FusedParams p) {
 // rows: lane l has columns 32w + 4*(l % 8) .. +3 of rows 16*(l / 8) .. +15.  The
 // column sums then reduce inside the wave (xor-shuffles over the 8 row groups), the
 // q/k rows are staged in a wave-private LDS slot, and each token's inputs are
-// loaded one token ahead, so the token loop itself has no barrier.  The k sums
-// (needed by every lane for the update) are summed in every lane; the q sums only
-// feed the readout and are reduce-scattered, so each lane reads out one column
-// (lanes 8..15 of each row repeat lanes 0..7).
+// loaded one token ahead, so the token loop itself has no barrier.  The k and q
+// column sums are reduce-scattered, so each lane ends with the sums of one of its 4
+// columns (lanes 8..15 of each row repeat lanes 0..7): it forms delta of that column
+// and reads it out, and the deltas are gathered back for the update.
 // kNorm: each wave parks its o columns in an 8-token LDS ring; every 8 tokens the
 // workgroup synchronises once and normalises that chunk cooperatively (thread ->
 // token tid/32, columns 4*(tid%32)..+3, the sum of o^2 over a half-wave in the
@@ -408,11 +408,13 @@ __global__ __launch_bounds__(256) void decode_multi_kernel(StepParams p) {
         }
         // sum over the 8 row groups of the wave (lane bits 3..5):
         // ((g0+g1)+(g2+g3))+((g4+g5)+(g6+g7)), as in the single-token kernel
-        pk = add_xor32(add_xor16(add_xor8(pk)));
         kq = add_xor32(add_xor16(add_xor8(kq)));
+        const float pkc = scatter_sum4(add_xor8(pk));
         const float pqc = scatter_sum4(add_xor8(pq));
-        const f4 d = beta * fma4(-eg, pk, v);
-        const float dc = oc == 0 ? d.x : oc == 1 ? d.y : oc == 2 ? d.z : d.w;
+        // delta of column col + oc, then of all 4 columns for the update
+        const float vc = oc == 0 ? v.x : oc == 1 ? v.y : oc == 2 ? v.z : v.w;
+        const float dc = beta * __builtin_fmaf(-eg, pkc, vc);
+        const f4 d = gather4(dc);
         // the readout of column col + oc (a scale of 1 multiplies exactly)
         const float out = __builtin_fmaf(kq, dc, eg * pqc) * p.oscale;
         if (p.o && reads_out) p.o[((tok0 + t) * p.h_v + i) * kS + col + oc] = out;
