@@ -26,6 +26,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -34,7 +35,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0            # MI355X HBM3E, published peak
 BF16_PEAK_TFLOPS = 2500.0         # MI355X dense bf16 matrix peak, published
-# fp32 VALU without packed instructions (this build keeps them off):
+# fp32 VALU without packed instructions (the library is compiled with them off):
 # 256 CUs x 4 SIMDs x 16 lanes x 2 flop (FMA) x 2.4 GHz
 VALU_PEAK_TFLOPS = 78.6
 FLOP_PER_SEQ_HEAD_STEP = 7 * 128 * 128   # per state element: S^T k FMA, S^T q FMA, decay multiply, update FMA
@@ -131,24 +132,40 @@ def copy_probe(mib: int, reps: int = 5):
     print(json.dumps({"copy_probe_bytes_read": n * 4, "copy_probe_bytes_written": n * 4, "reps": reps}))
 
 
-def gpu_clocks():
-    """Current GPU clocks as amd-smi reports them (JSON), or None if the tool is absent or
-    fails; run as a child process, after the timed region, and only on request
-    (--clocks): under a profiler that preloads itself into every process, the tool's
-    interpreter launcher would replace a process that has already opened the GPU."""
-    import subprocess
-    for cmd in (["amd-smi", "metric", "--gpu", "0", "--clock", "--json"],
-                ["rocm-smi", "--showclocks", "--json"]):
-        try:
-            r = subprocess.run(cmd, capture_output=True, text=True, timeout=20)
-        except (OSError, subprocess.SubprocessError):
-            continue
-        if r.returncode == 0 and r.stdout.strip():
-            try:
-                return {"tool": cmd[0], "report": json.loads(r.stdout)}
-            except ValueError:
-                continue
+def _card_dir():
+    """sysfs directory of the amdgpu card that device 0 of this process is, matched by
+    its PCI address, or None."""
+    import glob
+    import torch
+    pr = torch.cuda.get_device_properties(0)
+    try:
+        want = "%04x:%02x:%02x." % (pr.pci_domain_id, pr.pci_bus_id, pr.pci_device_id)
+    except AttributeError:
+        return None
+    for card in sorted(glob.glob("/sys/class/drm/card[0-9]*/device")):
+        if os.path.basename(os.path.realpath(card)).startswith(want):
+            return card
     return None
+
+
+def gpu_clocks(card):
+    """The card's current shader and memory clock levels in MHz, read from the amdgpu
+    driver's pp_dpm_sclk / pp_dpm_mclk files (the level marked '*'); None where they
+    cannot be read.  A file read, so it is safe in any process (no child program)."""
+    if card is None:
+        return None
+    out = {}
+    for key, name in (("sclk_mhz", "pp_dpm_sclk"), ("mclk_mhz", "pp_dpm_mclk")):
+        try:
+            with open(os.path.join(card, name)) as f:
+                lines = f.read().splitlines()
+        except OSError:
+            continue
+        cur = [ln for ln in lines if ln.rstrip().endswith("*")]
+        m = re.search(r"(\d+)\s*mhz", cur[0], re.I) if cur else None
+        if m:
+            out[key] = int(m.group(1))
+    return out or None
 
 
 def projections_context(G, W, rows: int, stream, reps: int = 50):
@@ -202,7 +219,6 @@ def main():
     ap.add_argument("--config", default="b256", choices=["tiny", "b64", "b256", "prefill", "ragged"])
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--clocks", action="store_true", help="report amd-smi clocks after the timed region")
     ap.add_argument("--copy-probe-mib", type=int, default=0)
     ap.add_argument("--event-every", type=int, default=8,
                     help="record per-kernel HIP events on every N-th timed step")
@@ -210,9 +226,9 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py: this build runs on one GPU only; the decode mixer shards by sequence "
-              "slots or head groups with no exchange inside the path, and multi-GPU runs are "
-              "not part of it. Use --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU: the decode mixer shards by sequence slots or head "
+              "groups with no exchange inside the path, so a run on N GPUs is N independent "
+              "copies of this one. Use --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
@@ -282,6 +298,9 @@ def main():
         if ev:
             ev[3].record(stream)
 
+    card = _card_dir()
+    clocks = {}
+
     def timed(fn, n_ev, names):
         for _ in range(args.warmup):
             fn()
@@ -296,6 +315,8 @@ def main():
         t0 = time.perf_counter()
         for k in range(args.steps):
             fn(evs.get(k))
+        # the steps are queued and the GPU is still running them: sample its clocks
+        clocks[fn.__name__] = gpu_clocks(card)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
         k_ms = {name: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs.values()]))
@@ -374,7 +395,6 @@ def main():
     log("three calls: " + ", ".join(f"{k}={v * 1000:.1f}us" for k, v in three_k.items()) +
         f"; {three_ms * 1000:.1f} us/step; recurrence kernel {three_step_gbps:.0f} GB/s; d2d copy {copy_gbps:.0f} GB/s")
     traffic = read_traffic() if args.config == "b256" else None
-    clocks = gpu_clocks() if args.clocks else None
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -425,7 +445,7 @@ def main():
                      "algorithmic_flops_per_launch": flops,
                      "hbm_gbps": achieved,
                      "event_samples": n_samples},
-        "gpu_clocks_after_timing": clocks,
+        "gpu_clocks_during_timing": clocks.get("step_one" if single else "step_fused"),
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
