@@ -211,6 +211,86 @@ def projections_context(G, W, rows: int, stream, reps: int = 50):
             "note": "fp32 activations as bf16 hi+lo: two bf16 matrix ops per multiply-add"}
 
 
+def layer_decode(G, batches, reps: int = 50):
+    """One decode token of a whole GDN layer, x [B][n_embd] -> out [B][n_embd]: split of x,
+    qkv + z in one launch, the alpha / beta projections, the single-launch mixer, split
+    of y and the out projection, captured in a HIP graph and replayed (so the host's
+    launch cost is not in it), at each batch size; plus each call timed eagerly with
+    events.  Seeded random weights (bf16) and inputs; one JSON line per batch size."""
+    import torch
+    n_embd, n_qkv, n_z = 2560, 10240, 6144
+    geom = G.Geom()
+    hv, s_ = geom.h_v, geom.s
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(21)
+    rnd = lambda *shape, std=1.0: torch.randn(*shape, generator=gen, device="cuda") * std
+    bf16 = lambda t: t.to(torch.bfloat16).view(torch.int16).contiguous()
+    wp_qkvz = G.gdn_pack_bf16(bf16(rnd(n_qkv + n_z, n_embd, std=n_embd ** -0.5)))
+    w_alpha, w_beta = bf16(rnd(hv, n_embd, std=n_embd ** -0.5)), bf16(rnd(hv, n_embd, std=n_embd ** -0.5))
+    wp_out = G.gdn_pack_bf16(bf16(rnd(n_embd, n_z, std=n_z ** -0.5)))
+    conv_w, dt, norm_w = rnd(n_qkv, geom.d_conv, std=0.5), rnd(hv, std=0.5), 1.0 + rnd(s_, std=0.1)
+    ssm_a = -torch.exp(torch.rand(hv, generator=gen, device="cuda") * 2.0 - 1.0)
+    weight_bytes = (n_qkv + n_z) * n_embd * 2 + 2 * hv * n_embd * 2 + n_embd * n_z * 2
+    for B in batches:
+        pool = G.StatePool(B, geom)
+        pool.state.copy_(rnd(*pool.state.shape, std=0.02))
+        pool.conv.copy_(rnd(*pool.conv.shape))
+        x = rnd(B, n_embd)
+        xs = G.gdn_split_bf16(x)
+        qkv, z = torch.empty(B, n_qkv, device="cuda"), torch.empty(B, n_z, device="cuda")
+        alpha, beta_logit = torch.empty(B, hv, device="cuda"), torch.empty(B, hv, device="cuda")
+        y, out = torch.empty(B, n_z, device="cuda"), torch.empty(B, n_embd, device="cuda")
+        ys = G.gdn_split_bf16(y.zero_())
+        ws = torch.empty(max(G.gdn_project_workspace_bytes(B, n_z, n_embd), 16), dtype=torch.uint8,
+                         device="cuda")
+        calls = {
+            "split_x": lambda: G.gdn_split_bf16(x, xs),
+            "qkv_z": lambda: G.gdn_project2_bf16(xs, wp_qkvz, n_qkv, qkv, z, workspace=ws),
+            "alpha_beta": lambda: G.gdn_ab_project(x, w_alpha, w_beta, alpha, beta_logit),
+            "mixer": lambda: G.gdn_decode_fused(pool, qkv, conv_w, alpha, beta_logit, dt, ssm_a, z, norm_w,
+                                                1e-6, y),
+            "split_y": lambda: G.gdn_split_bf16(y, ys),
+            "out": lambda: G.gdn_project_bf16(ys, wp_out, out, workspace=ws),
+        }
+        eager = {}
+        for name, fn in calls.items():
+            for _ in range(3):
+                fn()
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            ev[0].record()
+            for _ in range(reps):
+                fn()
+            ev[1].record()
+            torch.cuda.synchronize()
+            eager[name] = ev[0].elapsed_time(ev[1]) / reps * 1000.0
+        step = lambda: [fn() for fn in calls.values()]
+        step()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        graph.replay()
+        torch.cuda.synchronize()
+        best = None
+        for _ in range(5):
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            ev[0].record()
+            for _ in range(reps):
+                graph.replay()
+            ev[1].record()
+            torch.cuda.synchronize()
+            us = ev[0].elapsed_time(ev[1]) / reps * 1000.0
+            best = us if best is None else min(best, us)
+        state_bytes = 2 * B * hv * s_ * s_ * 4
+        print(json.dumps({"layer_decode": {
+            "B": B, "graph_us_per_token": best, "eager_us": eager,
+            "weight_bytes": weight_bytes, "state_bytes_read_written": state_bytes,
+            "gbps_weights_and_state": (weight_bytes + state_bytes) / best / 1e3,
+            "note": "seeded random bf16 weights and fp32 inputs; n_embd 2560, h_k 16, h_v 48, S 128"}}),
+            flush=True)
+        del pool
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -220,6 +300,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0)
+    ap.add_argument("--layer", default="",
+                    help="comma-separated batch sizes: time one decode token of a whole layer "
+                         "(projections + mixer) from a HIP graph, instead of the step")
     ap.add_argument("--event-every", type=int, default=8,
                     help="record per-kernel HIP events on every N-th timed step")
     args = ap.parse_args()
@@ -245,6 +328,9 @@ def main():
     torch.cuda.set_device(0)
     if args.copy_probe_mib:
         copy_probe(args.copy_probe_mib)
+        return
+    if args.layer:
+        layer_decode(G, [int(v) for v in args.layer.split(",")])
         return
 
     wl = W.CONFIGS[args.config]()

@@ -523,38 +523,50 @@ int64_t gdn_project_workspace_bytes(int64_t rows, int32_t k, int32_t n) {
 
 namespace {
 
-int project_common(const char* fn, const uint16_t* xs, const uint16_t* wp, int64_t rows, int32_t k, int32_t n1,
-                   float* out1, int32_t n2, float* out2, void* workspace, int64_t workspace_bytes, void* stream) {
+// outs[o] takes cols[o] columns; names[o] is how errors call it
+int project_common(const char* fn, const uint16_t* xs, const uint16_t* wp, int64_t rows, int32_t k, int n_out,
+                   const int32_t* cols, float* const* outs, const char* const* names, void* workspace,
+                   int64_t workspace_bytes, void* stream) {
     if (rows < 0) return fail(GDN_ERR_ARG, fn, "rows=%lld is negative", (long long) rows);
     if (k <= 0 || k % 8 != 0 || k > kMaxProjK)
         return fail(GDN_ERR_ARG, fn, "k=%d must be a positive multiple of 8, at most %d", k, kMaxProjK);
-    if (n1 <= 0 || n2 < 0 || n1 > INT32_MAX - n2) return fail(GDN_ERR_ARG, fn, "n1=%d, n2=%d out of range", n1, n2);
+    int32_t n = 0;
+    for (int o = 0; o < n_out; ++o) {
+        if (cols[o] <= 0) return fail(GDN_ERR_ARG, fn, "%s has %d columns; each output needs at least one",
+                                      names[o], cols[o]);
+        if (cols[o] > INT32_MAX - n) return fail(GDN_ERR_ARG, fn, "the outputs' columns add up past 2^31");
+        n += cols[o];
+    }
     if (workspace_bytes < 0) return fail(GDN_ERR_ARG, fn, "workspace_bytes=%lld is negative", (long long) workspace_bytes);
     if (rows == 0) return ok();
-    const int32_t n = n1 + n2;
     const int64_t xs_bytes = gdn_split_bf16_bytes(rows, k);
     if (xs_bytes < 0 || rows > INT64_MAX / 4 / n) return fail(GDN_ERR_ARG, fn, "rows too large");
     if (int rc = check_f4(xs, fn, "xs")) return rc;
     if (int rc = check_f4(wp, fn, "wp")) return rc;
-    if (int rc = check_f1(out1, fn, n2 ? "out1" : "out")) return rc;
-    if (n2)
-        if (int rc = check_f1(out2, fn, "out2")) return rc;
-    const size_t b1 = (size_t) rows * n1 * sizeof(float), b2 = (size_t) rows * n2 * sizeof(float);
+    size_t bytes[gdn::kMaxOuts];
+    for (int o = 0; o < n_out; ++o) {
+        if (int rc = check_f1(outs[o], fn, names[o])) return rc;
+        bytes[o] = (size_t) rows * cols[o] * sizeof(float);
+    }
     const size_t wp_bytes = (size_t) gdn_pack_bf16_bytes(n, k);
-    if (overlap(out1, b1, xs, (size_t) xs_bytes) || (n2 && overlap(out2, b2, xs, (size_t) xs_bytes)))
-        return fail(GDN_ERR_ARG, fn, "an output overlaps xs");
-    if (overlap(out1, b1, wp, wp_bytes) || (n2 && overlap(out2, b2, wp, wp_bytes)))
-        return fail(GDN_ERR_ARG, fn, "an output overlaps wp");
-    if (n2 && overlap(out1, b1, out2, b2)) return fail(GDN_ERR_ARG, fn, "out1 overlaps out2");
-    gdn::GemmParams gp;
+    for (int o = 0; o < n_out; ++o) {
+        if (overlap(outs[o], bytes[o], xs, (size_t) xs_bytes)) return fail(GDN_ERR_ARG, fn, "an output overlaps xs");
+        if (overlap(outs[o], bytes[o], wp, wp_bytes)) return fail(GDN_ERR_ARG, fn, "an output overlaps wp");
+        for (int q = 0; q < o; ++q)
+            if (overlap(outs[q], bytes[q], outs[o], bytes[o]))
+                return fail(GDN_ERR_ARG, fn, "%s overlaps %s", names[q], names[o]);
+    }
+    gdn::GemmParams gp{};
     gp.xs = xs;
     gp.wp = wp;
-    gp.out = out1;
-    gp.out2 = n2 ? out2 : nullptr;
+    gp.c0[0] = 0;
+    for (int o = 0; o < gdn::kMaxOuts; ++o) {
+        gp.out[o] = o < n_out ? outs[o] : nullptr;
+        gp.c0[o + 1] = o < n_out ? gp.c0[o] + cols[o] : n;
+    }
     gp.rows = (long long) rows;
     gp.k = k;
     gp.n = n;
-    gp.n1 = n1;
     const gdn::GemmConfig cfg = gdn::choose_gemm_config(gp.rows, k, n);
     if (gdn::gemm_workgroups(gp, cfg) > INT32_MAX) return fail(GDN_ERR_ARG, fn, "rows x n too large");
     const long long need = gdn::gemm_workspace_bytes(gp, cfg);
@@ -563,12 +575,12 @@ int project_common(const char* fn, const uint16_t* xs, const uint16_t* wp, int64
             return fail(GDN_ERR_ARG, fn, "workspace of %lld bytes, the launch needs %lld (gdn_project_workspace_bytes)",
                         (long long) workspace_bytes, need);
         if (int rc = check_f4(workspace, fn, "workspace")) return rc;
-        const void* args[4] = {xs, wp, out1, out2};
-        const size_t sizes[4] = {(size_t) xs_bytes, wp_bytes, b1, b2};
-        for (int a = 0; a < 4; ++a)
-            if (sizes[a] && overlap(workspace, (size_t) need, args[a], sizes[a]))
-                return fail(GDN_ERR_ARG, fn, "workspace overlaps %s",
-                            a == 0 ? "xs" : a == 1 ? "wp" : a == 3 ? "out2" : n2 ? "out1" : "out");
+        if (overlap(workspace, (size_t) need, xs, (size_t) xs_bytes))
+            return fail(GDN_ERR_ARG, fn, "workspace overlaps xs");
+        if (overlap(workspace, (size_t) need, wp, wp_bytes)) return fail(GDN_ERR_ARG, fn, "workspace overlaps wp");
+        for (int o = 0; o < n_out; ++o)
+            if (overlap(workspace, (size_t) need, outs[o], bytes[o]))
+                return fail(GDN_ERR_ARG, fn, "workspace overlaps %s", names[o]);
         gp.ws = static_cast<float*>(workspace);
     }
     gp.parts = cfg.parts;
@@ -579,15 +591,30 @@ int project_common(const char* fn, const uint16_t* xs, const uint16_t* wp, int64
 
 int gdn_project_bf16(const uint16_t* xs, const uint16_t* wp, int64_t rows, int32_t k, int32_t n, float* out,
                      void* workspace, int64_t workspace_bytes, void* stream) {
+    static const char* const names[1] = {"out"};
     if (n <= 0) return fail(GDN_ERR_ARG, "gdn_project_bf16", "n=%d must be positive", n);
-    return project_common("gdn_project_bf16", xs, wp, rows, k, n, out, 0, nullptr, workspace, workspace_bytes, stream);
+    return project_common("gdn_project_bf16", xs, wp, rows, k, 1, &n, &out, names, workspace, workspace_bytes,
+                          stream);
 }
 
 int gdn_project2_bf16(const uint16_t* xs, const uint16_t* wp, int64_t rows, int32_t k, int32_t n1, float* out1,
                       int32_t n2, float* out2, void* workspace, int64_t workspace_bytes, void* stream) {
-    if (n2 <= 0) return fail(GDN_ERR_ARG, "gdn_project2_bf16", "n2=%d must be positive", n2);
-    return project_common("gdn_project2_bf16", xs, wp, rows, k, n1, out1, n2, out2, workspace, workspace_bytes,
+    static const char* const names[2] = {"out1", "out2"};
+    const int32_t cols[2] = {n1, n2};
+    float* const outs[2] = {out1, out2};
+    return project_common("gdn_project2_bf16", xs, wp, rows, k, 2, cols, outs, names, workspace, workspace_bytes,
                           stream);
+}
+
+int gdn_project_multi_bf16(const uint16_t* xs, const uint16_t* wp, int64_t rows, int32_t k, int32_t n_out,
+                           const int32_t* cols, float* const* outs, void* workspace, int64_t workspace_bytes,
+                           void* stream) {
+    static const char* const names[gdn::kMaxOuts] = {"outs[0]", "outs[1]", "outs[2]", "outs[3]"};
+    const char* fn = "gdn_project_multi_bf16";
+    if (n_out < 1 || n_out > gdn::kMaxOuts)
+        return fail(GDN_ERR_ARG, fn, "n_out=%d must be 1 to %d", n_out, gdn::kMaxOuts);
+    if (!cols || !outs) return fail(GDN_ERR_ARG, fn, "%s is null", cols ? "outs" : "cols");
+    return project_common(fn, xs, wp, rows, k, n_out, cols, outs, names, workspace, workspace_bytes, stream);
 }
 
 int gdn_gated_rmsnorm(const float* o, const float* z, const float* w, float eps, int64_t rows, int32_t s,

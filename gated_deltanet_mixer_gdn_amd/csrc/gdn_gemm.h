@@ -36,8 +36,11 @@ struct PackParams {
     int n, k;           // k a multiple of 8
 };
 
-// res[r][j] = sum_e w[j][e] * (hi + lo)[r][e]; columns j < n1 go to out [rows][n1],
-// the others to out2 [rows][n - n1] (n1 = n: one output)
+constexpr int kMaxOuts = 4;
+
+// res[r][j] = sum_e w[j][e] * (hi + lo)[r][e]; output o takes the columns
+// c0[o] <= j < c0[o + 1] as out[o] [rows][c0[o + 1] - c0[o]] (c0[0] = 0; the entries
+// past the last output are n, so their ranges are empty)
 //
 // parts > 1 (tile shapes with kw = 4 only): the k chunks are split into `parts`
 // contiguous ranges, one workgroup per (tile, range), each writing its partial block
@@ -45,10 +48,10 @@ struct PackParams {
 struct GemmParams {
     const uint16_t* xs;  // split activations, tiled
     const uint16_t* wp;  // packed weights, tiled
-    float* out;
-    float* out2;
+    float* out[kMaxOuts];
+    int c0[kMaxOuts + 1];
     long long rows;
-    int k, n, n1;
+    int k, n;
     int parts = 1;
     float* ws = nullptr;   // [tiles][parts][32 WM x 32 WN block] partial sums
 };

@@ -106,7 +106,9 @@ __device__ __forceinline__ int xcd_tile(int b, int tiles_total) {
 }
 
 // Accumulator element e of lane (i, h) holds row 8(e/4) + 4h + e%4, column i of its
-// 32 x 32 block; rows past p.rows and columns past p.n are not stored.
+// 32 x 32 block; rows past p.rows and columns past p.n are not stored.  The output a
+// column belongs to is picked with selects on the uniform range bounds (no indexed
+// access to the parameter block).
 template <int WM, int WN>
 __device__ __forceinline__ void store_blocks(const GemmParams& p, const f16v (&acc)[WM][WN], long long m0, int n0,
                                              int i, int h) {
@@ -116,8 +118,17 @@ __device__ __forceinline__ void store_blocks(const GemmParams& p, const f16v (&a
         for (int c = 0; c < WN; ++c) {
             const int col = n0 + 32 * c + i;
             if (col >= p.n) continue;
-            float* dst = col < p.n1 ? p.out + col : p.out2 + (col - p.n1);
-            const long long ld = col < p.n1 ? p.n1 : p.n - p.n1;
+            float* base = p.out[0];
+            int lo = 0, hi = p.c0[1];
+#pragma unroll
+            for (int o = 1; o < kMaxOuts; ++o)
+                if (col >= p.c0[o]) {
+                    base = p.out[o];
+                    lo = p.c0[o];
+                    hi = p.c0[o + 1];
+                }
+            float* dst = base + (col - lo);
+            const long long ld = hi - lo;
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const long long row = m0 + 32 * r + 8 * (e >> 2) + 4 * h + (e & 3);

@@ -23,7 +23,7 @@ EXPORTS = (
     "gdn_state_pool_slots", "gdn_state_pool_zero", "gdn_conv_silu_norm", "gdn_decode_step",
     "gdn_decode_step_norm", "gdn_decode_fused", "gdn_verify_window", "gdn_commit", "gdn_gated_rmsnorm",
     "gdn_ab_project", "gdn_split_bf16_bytes", "gdn_pack_bf16_bytes", "gdn_split_bf16", "gdn_pack_bf16",
-    "gdn_project_bf16", "gdn_project2_bf16", "gdn_project_workspace_bytes",
+    "gdn_project_bf16", "gdn_project2_bf16", "gdn_project_workspace_bytes", "gdn_project_multi_bf16",
 )
 
 
@@ -101,6 +101,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "gdn_project2_bf16": ([vp, vp, i64, i32, i32, vp, i32, vp, vp, i64, vp], ctypes.c_int),
         "gdn_project_bf16": ([vp, vp, i64, i32, i32, vp, vp, i64, vp], ctypes.c_int),
         "gdn_project_workspace_bytes": ([i64, i32, i32], ctypes.c_int64),
+        "gdn_project_multi_bf16": ([vp, vp, i64, i32, i32, vp, vp, vp, i64, vp], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -428,6 +429,25 @@ def gdn_project2_bf16(xs: SplitX, wp: PackedW, n1: int, out1=None, out2=None, wo
                                             _f32(out1, "out1"), n2, _f32(out2, "out2"), ws, ws_bytes,
                                             _stream(xs.data)))
     return out1, out2
+
+
+def gdn_project_multi_bf16(xs: SplitX, wp: PackedW, cols, outs=None, workspace=None):
+    """Up to 4 projections of the same activations in one launch: wp packs the weight
+    matrices stacked row-wise, cols[o] rows each; returns the outputs [rows][cols[o]]."""
+    import torch
+    cols = [int(c) for c in cols]
+    if xs.k != wp.k or sum(cols) != wp.n or not 1 <= len(cols) <= 4:
+        raise ValueError(f"x has k={xs.k}, w has k={wp.k} and {wp.n} rows, cols={cols}")
+    dev = xs.data.device
+    outs = [torch.empty(xs.rows, c, device=dev) for c in cols] if outs is None else list(outs)
+    if len(outs) != len(cols) or any(o.numel() != xs.rows * c for o, c in zip(outs, cols)):
+        raise ValueError("outs do not match cols")
+    ptrs = (ctypes.c_void_p * len(outs))(*[_f32(o, f"outs[{i}]") for i, o in enumerate(outs)])
+    col_arr = (ctypes.c_int32 * len(cols))(*cols)
+    ws, ws_bytes, _keep = _workspace(xs.rows, xs.k, wp.n, dev, workspace)
+    _check(load_library().gdn_project_multi_bf16(xs.data.data_ptr(), wp.data.data_ptr(), xs.rows, xs.k, len(cols),
+                                                 col_arr, ptrs, ws, ws_bytes, _stream(xs.data)))
+    return outs
 
 
 def gdn_project(x, wp: PackedW, out=None):

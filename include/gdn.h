@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 3
+#define GDN_ABI_VERSION 4
 
 enum {
     GDN_OK = 0,
@@ -302,6 +302,18 @@ int gdn_project_bf16(const uint16_t* xs, const uint16_t* wp, int64_t rows, int32
  * of the concatenated weights, column for column. */
 int gdn_project2_bf16(const uint16_t* xs, const uint16_t* wp, int64_t rows, int32_t k, int32_t n1, float* out1,
                       int32_t n2, float* out2, void* workspace, int64_t workspace_bytes, void* stream);
+
+/* Up to four projections of the same activations in one launch (qkv, z and the alpha /
+ * beta logits all read the layer input, so one launch serves the four): wp is
+ * gdn_pack_bf16 of the matrices stacked row-wise, cols[o] >= 1 rows each (host
+ * array of n_out entries, 1 <= n_out <= 4); the product's columns go, in that order,
+ * to outs[o] [rows][cols[o]] (host array of n_out device pointers, 4-byte aligned,
+ * overlapping neither each other nor an input).  The workspace is that of
+ * gdn_project_bf16 for n = the sum of cols.  Each output equals, column for column,
+ * the matching columns of gdn_project_bf16 of the stacked weights. */
+int gdn_project_multi_bf16(const uint16_t* xs, const uint16_t* wp, int64_t rows, int32_t k, int32_t n_out,
+                           const int32_t* cols, float* const* outs, void* workspace, int64_t workspace_bytes,
+                           void* stream);
 
 #ifdef __cplusplus
 }

@@ -71,7 +71,7 @@ def test_library_is_built_for_gfx950_only(tmp_path):
 
 
 def test_abi_version(L):
-    assert L.gdn_abi_version() == 3
+    assert L.gdn_abi_version() == 4
 
 
 def _geom(h_k=16, h_v=48, s=128, d_conv=4):
@@ -303,3 +303,31 @@ def test_projection_workspace(L):
     assert L.gdn_project_bf16(xs, wp, 1, 6144, 2560, out, ws, -1, None) == GDN_ERR_ARG
     assert b"negative" in L.gdn_last_error()
     assert L.gdn_project_bf16(None, None, 0, 6144, 2560, None, None, 0, None) == GDN_OK
+
+
+def test_projection_multi_argument_errors(L):
+    """Bad output counts, column counts, null or overlapping outputs are refused before
+    anything runs (every call below fails its checks)."""
+    import ctypes
+    from gated_deltanet_mixer_gdn_amd.gdn import GDN_ERR_ARG, GDN_OK
+    xs, wp, o = 1 << 30, 2 << 30, 3 << 30
+    cols = lambda *c: (ctypes.c_int32 * len(c))(*c)
+    outs = lambda *p: (ctypes.c_void_p * len(p))(*p)
+    M = L.gdn_project_multi_bf16
+    assert M(xs, wp, 4, 64, 0, cols(1), outs(o), None, 0, None) == GDN_ERR_ARG
+    assert b"n_out=0" in L.gdn_last_error()
+    assert M(xs, wp, 4, 64, 5, cols(1, 1, 1, 1, 1), outs(o, o, o, o, o), None, 0, None) == GDN_ERR_ARG
+    assert M(xs, wp, 4, 64, 2, None, outs(o, o + 4096), None, 0, None) == GDN_ERR_ARG
+    assert b"cols is null" in L.gdn_last_error()
+    assert M(xs, wp, 4, 64, 2, cols(8, 8), None, None, 0, None) == GDN_ERR_ARG
+    assert b"outs is null" in L.gdn_last_error()
+    assert M(xs, wp, 4, 64, 3, cols(8, 0, 8), outs(o, o + 4096, o + 8192), None, 0, None) == GDN_ERR_ARG
+    assert b"outs[1] has 0 columns" in L.gdn_last_error()
+    assert M(xs, wp, 4, 64, 3, cols(8, 8, 8), outs(o, None, o + 8192), None, 0, None) == GDN_ERR_ARG
+    assert b"outs[1] is null" in L.gdn_last_error()
+    assert M(xs, wp, 4, 64, 4, cols(8, 8, 8, 8), outs(o, o + 4096, o + 8192, o + 8192 + 64), None, 0, None) \
+        == GDN_ERR_ARG
+    assert b"outs[2] overlaps outs[3]" in L.gdn_last_error()
+    assert M(xs, wp, 4, 64, 4, cols(8, 8, 8, 8), outs(o, o + 4096, o + 8192, xs + 64), None, 0, None) == GDN_ERR_ARG
+    assert b"an output overlaps xs" in L.gdn_last_error()
+    assert M(None, None, 0, 64, 2, cols(8, 8), outs(None, None), None, 0, None) == GDN_OK

@@ -186,6 +186,35 @@ def test_projection_workspace_is_scratch():
     assert_close("out", a.cpu().numpy(), oracle.project(x, w), TOL)
 
 
+# the layer input's four projections in one launch (qkv, z, alpha and beta logits) at
+# a decode and a single-sequence batch, ragged small outputs, and a k-split launch
+MULTI = [(256, 2560, (10240, 6144, 48, 48)), (1, 2560, (10240, 6144, 48, 48)), (37, 200, (100, 60, 7, 9)),
+         (20, 4104, (3000, 900, 50, 50)), (5, 72, (40, 24, 8))]
+
+
+@pytest.mark.parametrize("rows,k,cols", MULTI)
+def test_multi_outputs_equal_the_stacked_projection(rows, k, cols):
+    """gdn_project_multi_bf16 writes, column for column, what gdn_project_bf16 writes for
+    the stacked weights, and matches the oracle (rows sampled at 256)."""
+    import torch
+    import gated_deltanet_mixer_gdn_amd as G
+    n = sum(cols)
+    log(f"multi-output rows={rows} k={k} cols={cols}")
+    x, w = W.make_proj(rows, k, n, seed=170 + rows + len(cols))
+    wp = G.gdn_pack_bf16(_w(w))
+    xs = G.gdn_split_bf16(dev(x))
+    outs = G.gdn_project_multi_bf16(xs, wp, cols)
+    whole = G.gdn_project_bf16(xs, wp)
+    torch.cuda.synchronize()
+    pick = np.unique(np.linspace(0, rows - 1, 9).astype(int))
+    ref = oracle.project(x[pick], w)
+    c0 = 0
+    for o, c in zip(outs, cols):
+        assert torch.equal(o, whole[:, c0:c0 + c]), f"columns {c0}..{c0 + c} differ"
+        assert_close(f"out[{c0}:{c0 + c}]", o.cpu().numpy()[pick], ref[:, c0:c0 + c], TOL)
+        c0 += c
+
+
 @pytest.mark.parametrize("rows", [256, 1])
 def test_projection_is_deterministic(rows):
     """Same inputs, same bits: the k-split launch (1 row) adds its parts in a fixed order."""
