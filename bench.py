@@ -213,10 +213,11 @@ def projections_context(G, W, rows: int, stream, reps: int = 50):
 
 def layer_decode(G, batches, reps: int = 50):
     """One decode token of a whole GDN layer, x [B][n_embd] -> out [B][n_embd]: split of x,
-    qkv + z in one launch, the alpha / beta projections, the single-launch mixer, split
-    of y and the out projection, captured in a HIP graph and replayed (so the host's
+    qkv, z and the alpha / beta logits in one launch, the single-launch mixer, split of
+    y and the out projection, captured in a HIP graph and replayed (so the host's
     launch cost is not in it), at each batch size; plus each call timed eagerly with
-    events.  Seeded random weights (bf16) and inputs; one JSON line per batch size."""
+    events, and the form with the alpha / beta projection as a launch of its own.
+    Seeded random weights (bf16) and inputs; one JSON line per batch size."""
     import torch
     n_embd, n_qkv, n_z = 2560, 10240, 6144
     geom = G.Geom()
@@ -225,8 +226,11 @@ def layer_decode(G, batches, reps: int = 50):
     gen.manual_seed(21)
     rnd = lambda *shape, std=1.0: torch.randn(*shape, generator=gen, device="cuda") * std
     bf16 = lambda t: t.to(torch.bfloat16).view(torch.int16).contiguous()
-    wp_qkvz = G.gdn_pack_bf16(bf16(rnd(n_qkv + n_z, n_embd, std=n_embd ** -0.5)))
+    w_qkvz = bf16(rnd(n_qkv + n_z, n_embd, std=n_embd ** -0.5))
     w_alpha, w_beta = bf16(rnd(hv, n_embd, std=n_embd ** -0.5)), bf16(rnd(hv, n_embd, std=n_embd ** -0.5))
+    wp_qkvz = G.gdn_pack_bf16(w_qkvz)
+    wp_in = G.gdn_pack_bf16(torch.cat([w_qkvz, w_alpha, w_beta]).contiguous())
+    cols_in = (n_qkv, n_z, hv, hv)
     wp_out = G.gdn_pack_bf16(bf16(rnd(n_embd, n_z, std=n_z ** -0.5)))
     conv_w, dt, norm_w = rnd(n_qkv, geom.d_conv, std=0.5), rnd(hv, std=0.5), 1.0 + rnd(s_, std=0.1)
     ssm_a = -torch.exp(torch.rand(hv, generator=gen, device="cuda") * 2.0 - 1.0)
@@ -245,15 +249,19 @@ def layer_decode(G, batches, reps: int = 50):
                          device="cuda")
         calls = {
             "split_x": lambda: G.gdn_split_bf16(x, xs),
-            "qkv_z": lambda: G.gdn_project2_bf16(xs, wp_qkvz, n_qkv, qkv, z, workspace=ws),
-            "alpha_beta": lambda: G.gdn_ab_project(x, w_alpha, w_beta, alpha, beta_logit),
+            "qkv_z_alpha_beta": lambda: G.gdn_project_multi_bf16(xs, wp_in, cols_in, (qkv, z, alpha, beta_logit),
+                                                                 workspace=ws),
             "mixer": lambda: G.gdn_decode_fused(pool, qkv, conv_w, alpha, beta_logit, dt, ssm_a, z, norm_w,
                                                 1e-6, y),
             "split_y": lambda: G.gdn_split_bf16(y, ys),
             "out": lambda: G.gdn_project_bf16(ys, wp_out, out, workspace=ws),
         }
+        separate_ab = {"split_x": calls["split_x"],
+                       "qkv_z": lambda: G.gdn_project2_bf16(xs, wp_qkvz, n_qkv, qkv, z, workspace=ws),
+                       "alpha_beta": lambda: G.gdn_ab_project(x, w_alpha, w_beta, alpha, beta_logit),
+                       **{kk: calls[kk] for kk in ("mixer", "split_y", "out")}}
         eager = {}
-        for name, fn in calls.items():
+        for name, fn in {**calls, **separate_ab}.items():
             for _ in range(3):
                 fn()
             ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
@@ -263,27 +271,32 @@ def layer_decode(G, batches, reps: int = 50):
             ev[1].record()
             torch.cuda.synchronize()
             eager[name] = ev[0].elapsed_time(ev[1]) / reps * 1000.0
-        step = lambda: [fn() for fn in calls.values()]
-        step()
-        torch.cuda.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
+        def graph_us(fns):
+            step = lambda: [fn() for fn in fns.values()]
             step()
-        graph.replay()
-        torch.cuda.synchronize()
-        best = None
-        for _ in range(5):
-            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-            ev[0].record()
-            for _ in range(reps):
-                graph.replay()
-            ev[1].record()
             torch.cuda.synchronize()
-            us = ev[0].elapsed_time(ev[1]) / reps * 1000.0
-            best = us if best is None else min(best, us)
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                step()
+            graph.replay()
+            torch.cuda.synchronize()
+            best = None
+            for _ in range(5):
+                ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+                ev[0].record()
+                for _ in range(reps):
+                    graph.replay()
+                ev[1].record()
+                torch.cuda.synchronize()
+                us = ev[0].elapsed_time(ev[1]) / reps * 1000.0
+                best = us if best is None else min(best, us)
+            return best
+        best = graph_us(calls)
+        best_separate = graph_us(separate_ab)
         state_bytes = 2 * B * hv * s_ * s_ * 4
         print(json.dumps({"layer_decode": {
-            "B": B, "graph_us_per_token": best, "eager_us": eager,
+            "B": B, "graph_us_per_token": best, "graph_us_separate_alpha_beta": best_separate,
+            "eager_us": eager,
             "weight_bytes": weight_bytes, "state_bytes_read_written": state_bytes,
             "gbps_weights_and_state": (weight_bytes + state_bytes) / best / 1e3,
             "note": "seeded random bf16 weights and fp32 inputs; n_embd 2560, h_k 16, h_v 48, S 128"}}),
