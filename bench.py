@@ -213,11 +213,13 @@ def projections_context(G, W, rows: int, stream, reps: int = 50):
 
 def layer_decode(G, batches, reps: int = 50):
     """One decode token of a whole GDN layer, x [B][n_embd] -> out [B][n_embd]: split of x,
-    qkv, z and the alpha / beta logits in one launch, the single-launch mixer, split of
-    y and the out projection, captured in a HIP graph and replayed (so the host's
-    launch cost is not in it), at each batch size; plus each call timed eagerly with
-    events, and the form with the alpha / beta projection as a launch of its own.
-    Seeded random weights (bf16) and inputs; one JSON line per batch size."""
+    qkv, z and the alpha / beta logits in one launch, the single-launch mixer writing y
+    already split for the out projection, and the out projection (4 launches),
+    captured in a HIP graph and replayed (so the host's launch cost is not in it), at
+    each batch size; plus each call timed eagerly with events, the 5-launch form
+    (alpha / beta projection as a launch of its own, better from 64 rows) and the
+    6-launch form (the split of y as a launch of its own too).  Seeded
+    random weights (bf16) and inputs; one JSON line per batch size."""
     import torch
     n_embd, n_qkv, n_z = 2560, 10240, 6144
     geom = G.Geom()
@@ -251,15 +253,17 @@ def layer_decode(G, batches, reps: int = 50):
             "split_x": lambda: G.gdn_split_bf16(x, xs),
             "qkv_z_alpha_beta": lambda: G.gdn_project_multi_bf16(xs, wp_in, cols_in, (qkv, z, alpha, beta_logit),
                                                                  workspace=ws),
-            "mixer": lambda: G.gdn_decode_fused(pool, qkv, conv_w, alpha, beta_logit, dt, ssm_a, z, norm_w,
-                                                1e-6, y),
-            "split_y": lambda: G.gdn_split_bf16(y, ys),
+            "mixer_ys": lambda: G.gdn_decode_fused(pool, qkv, conv_w, alpha, beta_logit, dt, ssm_a, z, norm_w,
+                                                   1e-6, None, ys=ys),
             "out": lambda: G.gdn_project_bf16(ys, wp_out, out, workspace=ws),
         }
         separate_ab = {"split_x": calls["split_x"],
                        "qkv_z": lambda: G.gdn_project2_bf16(xs, wp_qkvz, n_qkv, qkv, z, workspace=ws),
                        "alpha_beta": lambda: G.gdn_ab_project(x, w_alpha, w_beta, alpha, beta_logit),
-                       **{kk: calls[kk] for kk in ("mixer", "split_y", "out")}}
+                       "mixer": lambda: G.gdn_decode_fused(pool, qkv, conv_w, alpha, beta_logit, dt, ssm_a, z,
+                                                           norm_w, 1e-6, y),
+                       "split_y": lambda: G.gdn_split_bf16(y, ys),
+                       "out": calls["out"]}
         eager = {}
         for name, fn in {**calls, **separate_ab}.items():
             for _ in range(3):
@@ -291,11 +295,15 @@ def layer_decode(G, batches, reps: int = 50):
                 us = ev[0].elapsed_time(ev[1]) / reps * 1000.0
                 best = us if best is None else min(best, us)
             return best
+        five = {"split_x": calls["split_x"], "qkv_z": separate_ab["qkv_z"], "alpha_beta": separate_ab["alpha_beta"],
+                "mixer_ys": calls["mixer_ys"], "out": calls["out"]}
         best = graph_us(calls)
-        best_separate = graph_us(separate_ab)
+        best_five = graph_us(five)
+        best_separate = graph_us(separate_ab)   # 6 launches
         state_bytes = 2 * B * hv * s_ * s_ * 4
         print(json.dumps({"layer_decode": {
-            "B": B, "graph_us_per_token": best, "graph_us_separate_alpha_beta": best_separate,
+            "B": B, "graph_us_per_token": best, "graph_us_five_launches": best_five,
+            "graph_us_six_launches": best_separate,
             "eager_us": eager,
             "weight_bytes": weight_bytes, "state_bytes_read_written": state_bytes,
             "gbps_weights_and_state": (weight_bytes + state_bytes) / best / 1e3,

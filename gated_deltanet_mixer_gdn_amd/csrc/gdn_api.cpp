@@ -370,7 +370,8 @@ int gdn_decode_step_norm(gdn_pool* p, const int32_t* slots, const int32_t* n_tok
 
 int gdn_decode_fused(gdn_pool* p, const int32_t* slots, int32_t B, const float* qkv, const float* conv_w,
                      const float* alpha, const float* beta_logit, const float* dt, const float* ssm_a,
-                     const float* z, const float* norm_w, float eps, float* y, float* h, void* stream) {
+                     const float* z, const float* norm_w, float eps, float* y, float* h, uint16_t* ys,
+                     void* stream) {
     const char* fn = "gdn_decode_fused";
     if (int rc = check_pool(p, fn)) return rc;
     if (B < 0) return fail(GDN_ERR_ARG, fn, "B=%d is negative", B);
@@ -389,7 +390,9 @@ int gdn_decode_fused(gdn_pool* p, const int32_t* slots, int32_t B, const float* 
     if (int rc = check_f1(ssm_a, fn, "ssm_a")) return rc;
     if (int rc = check_f4(z, fn, "z")) return rc;
     if (int rc = check_f4(norm_w, fn, "norm_w")) return rc;
-    if (int rc = check_f4(y, fn, "y")) return rc;
+    if (!y && !ys) return fail(GDN_ERR_ARG, fn, "y and ys are both null");
+    if (y && !aligned(y, 16)) return fail(GDN_ERR_ARG, fn, "y is not 16-byte aligned");
+    if (ys && !aligned(ys, 16)) return fail(GDN_ERR_ARG, fn, "ys is not 16-byte aligned");
     if (h && !aligned(h, 16)) return fail(GDN_ERR_ARG, fn, "h is not 16-byte aligned");
     if (slots && !aligned(slots, 4)) return fail(GDN_ERR_ARG, fn, "slots is not 4-byte aligned");
     if (!slots && B > p->n_slots)
@@ -398,13 +401,24 @@ int gdn_decode_fused(gdn_pool* p, const int32_t* slots, int32_t B, const float* 
     const size_t y_bytes = (size_t) B * p->g.h_v * p->g.s * sizeof(float);
     const size_t c_bytes = (size_t) B * channels(p->g) * sizeof(float);
     const size_t pool_bytes = (size_t) ((p->base + p->bytes) - reinterpret_cast<char*>(p->state));
-    if (overlap(y, y_bytes, qkv, c_bytes)) return fail(GDN_ERR_ARG, fn, "y overlaps qkv");
-    if (overlap(y, y_bytes, z, y_bytes)) return fail(GDN_ERR_ARG, fn, "y overlaps z");
-    if (overlap(y, y_bytes, p->state, pool_bytes)) return fail(GDN_ERR_ARG, fn, "y overlaps the pool");
-    if (h) {
-        if (overlap(h, c_bytes, qkv, c_bytes)) return fail(GDN_ERR_ARG, fn, "h overlaps qkv");
-        if (overlap(h, c_bytes, y, y_bytes)) return fail(GDN_ERR_ARG, fn, "h overlaps y");
-        if (overlap(h, c_bytes, p->state, pool_bytes)) return fail(GDN_ERR_ARG, fn, "h overlaps the pool");
+    const int32_t vdim = p->g.h_v * p->g.s;
+    const size_t ys_bytes = ys ? (size_t) gdn_split_bf16_bytes(B, vdim) : 0;
+    // (pointer, bytes, name) of every output, then of every input an output may not overlap
+    struct Span {
+        const void* ptr;
+        size_t bytes;
+        const char* name;
+    };
+    const Span outs[3] = {{y, y ? y_bytes : 0, "y"}, {h, h ? c_bytes : 0, "h"}, {ys, ys_bytes, "ys"}};
+    const Span ins[3] = {{qkv, c_bytes, "qkv"}, {z, y_bytes, "z"}, {p->state, pool_bytes, "the pool"}};
+    for (int a = 0; a < 3; ++a) {
+        if (!outs[a].ptr) continue;
+        for (const Span& in : ins)
+            if (overlap(outs[a].ptr, outs[a].bytes, in.ptr, in.bytes))
+                return fail(GDN_ERR_ARG, fn, "%s overlaps %s", outs[a].name, in.name);
+        for (int q = 0; q < a; ++q)
+            if (outs[q].ptr && overlap(outs[a].ptr, outs[a].bytes, outs[q].ptr, outs[q].bytes))
+                return fail(GDN_ERR_ARG, fn, "%s overlaps %s", outs[a].name, outs[q].name);
     }
     gdn::FusedParams f;
     f.state = p->state;
@@ -420,6 +434,8 @@ int gdn_decode_fused(gdn_pool* p, const int32_t* slots, int32_t B, const float* 
     f.norm_w = norm_w;
     f.y = y;
     f.h = h;
+    f.ys = ys;
+    f.ys_chunks = vdim / gdn::kTileK;
     f.flags = p->flags;
     f.n_slots = p->n_slots;
     f.B = B;

@@ -30,6 +30,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include "gdn_bf16.h"
 #include "gdn_kernels.h"
 
 namespace gdn {
@@ -122,6 +123,47 @@ __device__ __forceinline__ f4 gather4(float v) {
     const auto a = __builtin_amdgcn_permlane16_swap(h[0], h[0], false, false);
     const auto b = __builtin_amdgcn_permlane16_swap(h[1], h[1], false, false);
     return f4{__uint_as_float(a[0]), __uint_as_float(b[0]), __uint_as_float(a[1]), __uint_as_float(b[1])};
+}
+
+// Where the single-launch decode also writes y split for the projections: row `row` of
+// a [rows][chunks * 64] activation in the tiled layout of gdn_split_bf16 (tile = 32
+// rows x 64 k; fragment (s, lane = i + 32h) of a tile holds the 8 values
+// [32R + i][64C + 32h + 8s + j] as bf16, the hi fragment at (2s)*64 + lane and the lo
+// fragment at (2s + 1)*64 + lane, in 16-byte units, 512 per tile), columns of value
+// head `head` at head*128 ..
+struct SplitOut {
+    uint16_t* ys;   // null: not written
+    int row, chunks, head;
+};
+
+// 16-byte slot of the fragment that column group cg (columns 4cg..4cg+3 of the head)
+// writes: the pair (cg, cg ^ 1) covers 8 consecutive columns; the even member writes
+// their hi fragment, the odd one their lo fragment.
+__device__ __forceinline__ long long split_slot(const SplitOut& so, int cg) {
+    const int kin = (4 * (cg & ~1)) & 63;            // column of the pair in its 64-chunk
+    const long long tile = (long long) (so.row >> 5) * so.chunks + 2 * so.head + ((cg & ~1) >= 16);
+    return tile * 512 + (2 * ((kin & 31) >> 3) + (cg & 1)) * 64 + (so.row & 31) + 32 * (kin >> 5);
+}
+
+// The 32 lanes of a half-wave hold y columns 4cg..4cg+3 (cg = lane % 32) of one head:
+// each pair swaps its 4 values (a DPP move inside the quad) and writes its fragment,
+// hi or lo, with the split pass's arithmetic (so the same bits as gdn_split_bf16 of y).
+__device__ __forceinline__ void store_split8(const SplitOut& so, int cg, f4 v) {
+    auto mate = [](float x) {
+        return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xf, 0xf, false));
+    };
+    const f4 pv = {mate(v.x), mate(v.y), mate(v.z), mate(v.w)};
+    const bool odd = cg & 1;
+    const f4 a = odd ? pv : v;   // the pair's first 4 columns
+    const f4 c = odd ? v : pv;   // its last 4
+    const float x[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
+    unsigned hi[8], lo[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) split_bf16(x[j], hi[j], lo[j]);
+    const unsigned* w = odd ? lo : hi;
+    typedef unsigned u4 __attribute__((ext_vector_type(4)));
+    const u4 frag = {w[0] | w[1] << 16, w[2] | w[3] << 16, w[4] | w[5] << 16, w[6] | w[7] << 16};
+    ((u4*) so.ys)[split_slot(so, cg)] = frag;
 }
 
 // Sum over each 8-lane block, then over the 32 lanes of a half-wave (lanes 0-31 or

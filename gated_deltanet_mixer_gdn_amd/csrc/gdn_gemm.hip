@@ -15,6 +15,7 @@
 // engine converts an activation once for the GEMVs that follow.
 #include <hip/hip_runtime.h>
 
+#include "gdn_bf16.h"
 #include "gdn_gemm.h"
 
 namespace gdn {
@@ -24,16 +25,6 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f16v __attribute__((ext_vector_type(16)));
 typedef float f4v __attribute__((ext_vector_type(4)));
 typedef unsigned u4v __attribute__((ext_vector_type(4)));
-
-// fp32 -> bf16 bits, round to nearest even.  NaN stays a quiet NaN; a finite value
-// that would round up to infinity is truncated instead (stays finite).
-__device__ __forceinline__ unsigned bf16_rne(float x) {
-    const unsigned u = __float_as_uint(x);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-    const unsigned r = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-    const bool finite = (u & 0x7f800000u) != 0x7f800000u;
-    return (finite && (r & 0x7f80u) == 0x7f80u) ? (u >> 16) : r;
-}
 
 // ------------------------------------------------------------------ split and pack
 // One thread per fragment position (tile, step, lane) of the output layout, so the
@@ -55,11 +46,7 @@ __global__ __launch_bounds__(256) void split_bf16_kernel(SplitParams p) {
             const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
             unsigned hi[8], lo[8];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                hi[j] = bf16_rne(v[j]);
-                // x - hi is exact in fp32; an infinite or NaN hi carries the whole value
-                lo[j] = (hi[j] & 0x7f80u) == 0x7f80u ? 0u : bf16_rne(v[j] - __uint_as_float(hi[j] << 16));
-            }
+            for (int j = 0; j < 8; ++j) split_bf16(v[j], hi[j], lo[j]);
             H = u4v{hi[0] | hi[1] << 16, hi[2] | hi[3] << 16, hi[4] | hi[5] << 16, hi[6] | hi[7] << 16};
             L = u4v{lo[0] | lo[1] << 16, lo[2] | lo[3] << 16, lo[4] | lo[5] << 16, lo[6] | lo[7] << 16};
         }

@@ -74,8 +74,10 @@ struct FusedParams {
     const float* ssm_a;     // [h_v]
     const float* z;         // [B][h_v*128]
     const float* norm_w;    // [128]
-    float* y;               // [B][h_v*128]
+    float* y;               // [B][h_v*128] or null (then ys is set)
     float* h;               // [B][C] or null: the conv/SiLU/L2 output, if wanted
+    uint16_t* ys;           // y split into bf16 hi / lo in the projections' tiled layout, or null
+    int ys_chunks;          // 64-column chunks per row of ys (h_v * 128 / 64)
     uint32_t* flags;
     long long n_slots;
     int B, h_k, h_v, group;

@@ -51,11 +51,12 @@ struct HeadReduce {
 // for bit.
 // oscale multiplies o after the readout (1 unless the 1/sqrt(S) is applied there
 // rather than to q); gate_silu picks the epilogue's gate.
+// y_row may be null; so.ys (if set) also takes y split for the projections.
 template <bool kNorm>
 __device__ __forceinline__ void head_token_256(f4 (&s)[16], const f4* qk, f4 v, float beta, float eg,
                                                HeadReduce& red, float* o_row, const float* z_row,
-                                               const float* norm_w, float* y_row, float eps, float oscale,
-                                               int gate_silu, int tid) {
+                                               const float* norm_w, float* y_row, const SplitOut& so, float eps,
+                                               float oscale, int gate_silu, int tid) {
     const int cg = tid & 31;
     const int rg = tid >> 5;
     const int wave = tid >> 6;
@@ -97,7 +98,9 @@ __device__ __forceinline__ void head_token_256(f4 (&s)[16], const f4* qk, f4 v, 
             const float inv = rms_inv(ss, eps);
             const f4 zz = *(const f4*) (z_row + cg * 4);
             const f4 wn = *(const f4*) (norm_w + cg * 4);
-            *(f4*) (y_row + cg * 4) = out * inv * wn * gate4(zz, gate_silu);
+            const f4 yv = out * inv * wn * gate4(zz, gate_silu);
+            if (y_row) *(f4*) (y_row + cg * 4) = yv;
+            if (so.ys) store_split8(so, cg, yv);
         }
     }
 #pragma unroll
@@ -154,8 +157,8 @@ __global__ __launch_bounds__(256) void decode_one_kernel(StepParams p) {
     __syncthreads();
 
     head_token_256<kNorm>(s, qk_lds, v, beta, eg, red, p.o ? p.o + e * kS : nullptr,
-                          kNorm ? p.z + e * kS : nullptr, p.norm_w, kNorm ? p.y + e * kS : nullptr, p.eps,
-                          p.oscale, p.gate_silu, tid);
+                          kNorm ? p.z + e * kS : nullptr, p.norm_w, kNorm ? p.y + e * kS : nullptr,
+                          SplitOut{nullptr, 0, 0, 0}, p.eps, p.oscale, p.gate_silu, tid);
     if (p.persist) store_tile(s, tile);
 }
 
@@ -201,14 +204,17 @@ __device__ __forceinline__ void fused_conv_prologue(const FusedParams& p, int b,
     dst[16 + cl] = hb;
 }
 
-// Outputs of the single-launch decode for a sequence with an unknown slot: y of the
-// group's heads and (if asked for) their h channels are zero; the pool is untouched.
+// Outputs of the single-launch decode for a sequence with an unknown slot: y (and its
+// split) of the group's heads and (if asked for) their h channels are zero; the pool
+// is untouched.
 __device__ __forceinline__ void fused_zero_outputs(const FusedParams& p, int b, int j, int tid, int nthreads) {
     const int g = p.group;
     const long long C = (long long) (2 * p.h_k + p.h_v) * kS;
     const f4 zero = {0.f, 0.f, 0.f, 0.f};
-    for (int u = tid; u < g * 32; u += nthreads)
-        *(f4*) (p.y + ((long long) b * p.h_v + g * j + u / 32) * kS + (u % 32) * 4) = zero;
+    for (int u = tid; u < g * 32; u += nthreads) {
+        if (p.y) *(f4*) (p.y + ((long long) b * p.h_v + g * j + u / 32) * kS + (u % 32) * 4) = zero;
+        if (p.ys) ((f4*) p.ys)[split_slot(SplitOut{p.ys, b, p.ys_chunks, g * j + u / 32}, u % 32)] = zero;
+    }
     if (p.h)
         for (int u = tid; u < (2 + g) * 32; u += nthreads) {
             const int crow = u / 32;
@@ -257,8 +263,9 @@ __global__ __launch_bounds__(256 * G) void decode_fused_par_kernel(FusedParams p
     const long long e = (long long) b * p.h_v + i;
     const float beta = sigmoid_f(p.beta_logit[e]);
     const float eg = expf(softplus_f(p.alpha[e] + p.dt[i]) * p.ssm_a[i]);
-    head_token_256<true>(s, qk_lds, v_lds[n][cg], beta, eg, red[n], nullptr, p.z + e * kS, p.norm_w, p.y + e * kS,
-                         p.eps, p.oscale, p.gate_silu, lt);
+    head_token_256<true>(s, qk_lds, v_lds[n][cg], beta, eg, red[n], nullptr, p.z + e * kS, p.norm_w,
+                         p.y ? p.y + e * kS : nullptr, SplitOut{p.ys, b, p.ys_chunks, i}, p.eps, p.oscale,
+                         p.gate_silu, lt);
     store_tile(s, tile);
 }
 
@@ -298,7 +305,8 @@ __global__ __launch_bounds__(256) void decode_fused_kernel(FusedParams p) {
         const float beta = sigmoid_f(p.beta_logit[e]);
         const float eg = expf(softplus_f(p.alpha[e] + p.dt[i]) * p.ssm_a[i]);
         head_token_256<true>(s, qk_lds, v_lds[n][cg], beta, eg, red[n & 1], nullptr, p.z + e * kS, p.norm_w,
-                             p.y + e * kS, p.eps, p.oscale, p.gate_silu, tid);
+                             p.y ? p.y + e * kS : nullptr, SplitOut{p.ys, b, p.ys_chunks, i}, p.eps, p.oscale,
+                             p.gate_silu, tid);
         store_tile(s, tile);
     }
 }

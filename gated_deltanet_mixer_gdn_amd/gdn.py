@@ -88,7 +88,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "gdn_decode_step": ([vp, vp, vp, i32, i32, vp, vp, vp, vp, vp, vp, vp], ctypes.c_int),
         "gdn_decode_step_norm": ([vp, vp, vp, i32, i32, vp, vp, vp, vp, vp, vp, vp, f32, vp, vp, vp],
                                  ctypes.c_int),
-        "gdn_decode_fused": ([vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, f32, vp, vp, vp], ctypes.c_int),
+        "gdn_decode_fused": ([vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, f32, vp, vp, vp, vp], ctypes.c_int),
         "gdn_verify_window": ([vp, vp, vp, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, f32, vp, vp, vp],
                               ctypes.c_int),
         "gdn_commit": ([vp, vp, vp, i32, i32, vp, vp, vp, vp, vp, vp, vp], ctypes.c_int),
@@ -235,9 +235,11 @@ def gdn_decode_step_norm(pool: StatePool, h, alpha, beta_logit, dt, ssm_a, z, no
 
 
 def gdn_decode_fused(pool: StatePool, qkv, conv_w, alpha, beta_logit, dt, ssm_a, z, norm_w, eps: float, y,
-                     h=None, slots=None):
+                     h=None, slots=None, ys: Optional["SplitX"] = None):
     """One decode token of the whole mixer in one launch. qkv [B][C] (or [B][1][C]);
-    alpha, beta_logit [B][h_v]; z, y [B][h_v*s]; h optional [B][C]."""
+    alpha, beta_logit [B][h_v]; z, y [B][h_v*s]; h optional [B][C]; ys optional: y
+    split for the out projection (a SplitX of B rows x h_v*s, as gdn_split_bf16 makes),
+    written by the same launch; y may then be None."""
     g = pool.geom
     B = qkv.shape[0]
 
@@ -246,13 +248,18 @@ def gdn_decode_fused(pool: StatePool, qkv, conv_w, alpha, beta_logit, dt, ssm_a,
         if t.numel() != n:
             raise ValueError(f"{name} must hold {n} elements, not {t.numel()}")
         return p_
+    vdim = g.h_v * g.s
+    if ys is not None and ((ys.rows, ys.k) != (B, vdim)
+                           or ys.data.numel() * 2 < load_library().gdn_split_bf16_bytes(B, vdim)):
+        raise ValueError(f"ys must be the split of a [{B}][{vdim}] activation")
     args = (ptr(qkv, "qkv", B * g.channels), _f32(conv_w, "conv_w", (g.channels, g.d_conv)),
             ptr(alpha, "alpha", B * g.h_v), ptr(beta_logit, "beta_logit", B * g.h_v),
-            _f32(dt, "dt", (g.h_v,)), _f32(ssm_a, "ssm_a", (g.h_v,)), ptr(z, "z", B * g.h_v * g.s),
+            _f32(dt, "dt", (g.h_v,)), _f32(ssm_a, "ssm_a", (g.h_v,)), ptr(z, "z", B * vdim),
             _f32(norm_w, "norm_w", (g.s,)))
     _check(load_library().gdn_decode_fused(pool.handle, _i32(slots, "slots", B), B, *args, float(eps),
-                                           ptr(y, "y", B * g.h_v * g.s),
-                                           None if h is None else ptr(h, "h", B * g.channels), _stream(qkv)))
+                                           None if y is None else ptr(y, "y", B * vdim),
+                                           None if h is None else ptr(h, "h", B * g.channels),
+                                           None if ys is None else ys.data.data_ptr(), _stream(qkv)))
 
 
 def gdn_verify_window(pool: StatePool, qkv, conv_w, alpha, beta_logit, dt, ssm_a, z, norm_w, eps: float, h, y,

@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 4
+#define GDN_ABI_VERSION 5
 
 enum {
     GDN_OK = 0,
@@ -186,13 +186,19 @@ int gdn_decode_step_norm(gdn_pool* p, const int32_t* slots, const int32_t* n_tok
  * slots   int32 [B] (NULL: slot b for sequence b)
  * qkv     [B][C];  conv_w [C][d_conv];  alpha, beta_logit [B][h_v];  dt, ssm_a [h_v]
  * z       [B][h_v*s];  norm_w [s];  eps (>= 0, used by both norms)
- * y       [B][h_v*s]   output
+ * y       [B][h_v*s]   output (NULL allowed when ys is given)
  * h       [B][C]       optional: NULL skips writing the conv/SiLU/L2 output
+ * ys      optional: y split for the projection after the mixer, in the layout and with
+ *                      the bits of gdn_split_bf16(y, B, h_v*s) (gdn_split_bf16_bytes(B,
+ *                      h_v*s) bytes, 16-byte aligned), so that pass is not needed; rows
+ *                      past B in its last 32-row tile are left as they are (the product
+ *                      only reads them into rows it does not store)
+ * The outputs may not overlap each other, qkv, z or the pool.
  * h_v/h_k must be at most 14 (GDN_ERR_UNSUPPORTED otherwise). */
 int gdn_decode_fused(gdn_pool* p, const int32_t* slots, int32_t B, const float* qkv,
                      const float* conv_w, const float* alpha, const float* beta_logit,
                      const float* dt, const float* ssm_a, const float* z, const float* norm_w,
-                     float eps, float* y, float* h, void* stream);
+                     float eps, float* y, float* h, uint16_t* ys, void* stream);
 
 /* ---------------------------------------------------------------- speculative window
  * The pages' second GDN workload: a verify window runs T drafted tokens from the

@@ -71,7 +71,7 @@ def test_library_is_built_for_gfx950_only(tmp_path):
 
 
 def test_abi_version(L):
-    assert L.gdn_abi_version() == 4
+    assert L.gdn_abi_version() == 5
 
 
 def _geom(h_k=16, h_v=48, s=128, d_conv=4):
@@ -205,7 +205,7 @@ def test_new_entry_points_reject_null_pool(L):
     assert L.gdn_last_error().startswith(b"gdn_decode_step_norm: pool is null")
     assert L.gdn_decode_step_norm(None, None, None, 1, 1, 16, 16, 16, 16, 16, 16, 16, 1e-6, None, None, None) == GDN_ERR_ARG
     assert b"y is null" in L.gdn_last_error()
-    assert L.gdn_decode_fused(None, None, 1, 16, 16, 16, 16, 16, 16, 16, 16, 1e-6, 16, None, None) == GDN_ERR_ARG
+    assert L.gdn_decode_fused(None, None, 1, 16, 16, 16, 16, 16, 16, 16, 16, 1e-6, 16, None, None, None) == GDN_ERR_ARG
     assert L.gdn_last_error().startswith(b"gdn_decode_fused: pool is null")
     assert L.gdn_verify_window(None, None, None, 1, 2, 16, 16, 16, 16, 16, 16, 16, 16, 1e-6, 16, 16, None) == GDN_ERR_ARG
     assert L.gdn_last_error().startswith(b"gdn_verify_window: pool is null")

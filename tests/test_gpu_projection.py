@@ -238,6 +238,58 @@ def test_projection_empty_is_a_no_op():
     assert out.shape == (0, 64)
 
 
+@pytest.mark.parametrize("B,geom", [(37, W.Geom()), (1, W.Geom()), (64, W.Geom()), (5, W.Geom(h_k=2, h_v=4)),
+                                    (33, W.Geom(h_k=1, h_v=14))],
+                         ids=lambda v: str(v) if isinstance(v, int) else f"hk{v.h_k}hv{v.h_v}")
+def test_single_launch_decode_writes_the_split_of_y(B, geom):
+    """gdn_decode_fused with ys writes, bit for bit, what gdn_split_bf16 writes for its y
+    (the 32-row padding it leaves alone stays as it was: zero here), with and without
+    y, for groups of 3 and 2 value heads per qk head and for the heads-in-turn form."""
+    import torch
+    import gated_deltanet_mixer_gdn_amd as G
+    wl = W.make("ys", B, 1, seed=180 + B, geom=geom, n_slots=B + 3, state_std=0.02, conv_std=1.0,
+                slot_choice="random")
+    vdim = geom.h_v * geom.s
+    log(f"decode with ys B={B} h_k={geom.h_k} h_v={geom.h_v}")
+    runs = []
+    for with_y in (True, False):
+        gm = GpuMixer(wl)
+        y = torch.empty(B, vdim, device="cuda") if with_y else None
+        ys = G.gdn_split_bf16(torch.zeros(B, vdim, device="cuda"))
+        G.gdn_decode_fused(gm.pool, gm.qkv[:, 0].contiguous(), gm.conv_w, gm.alpha[:, 0].contiguous(),
+                           gm.beta_logit[:, 0].contiguous(), gm.dt, gm.ssm_a, gm.z[:, 0].contiguous(), gm.norm_w,
+                           wl.eps, y, None, gm.slots, ys=ys)
+        runs.append((gm, y, ys))
+    (ga, y, ys), (gb, _, ys_noy) = runs
+    ref = G.gdn_split_bf16(y)
+    torch.cuda.synchronize()
+    assert y.abs().max().item() > 0
+    assert torch.equal(ys.data, ref.data), "the fused split differs from gdn_split_bf16(y)"
+    assert torch.equal(ys_noy.data, ys.data), "without y the split differs"
+    assert torch.equal(ga.pool.state, gb.pool.state) and torch.equal(ga.pool.conv, gb.pool.conv)
+
+
+def test_single_launch_decode_split_of_y_for_an_unknown_slot():
+    """A sequence whose slot is unknown gets zero fragments; the others get the split of
+    their y."""
+    import torch
+    import gated_deltanet_mixer_gdn_amd as G
+    wl = W.make("ys-bad", 3, 1, seed=185, n_slots=4, state_std=0.02, conv_std=1.0)
+    gm = GpuMixer(wl)
+    vdim = wl.geom.value_dim
+    y = torch.empty(3, vdim, device="cuda")
+    ys = G.gdn_split_bf16(torch.full((3, vdim), 5.0, device="cuda"))
+    G.gdn_decode_fused(gm.pool, gm.qkv[:, 0].contiguous(), gm.conv_w, gm.alpha[:, 0].contiguous(),
+                       gm.beta_logit[:, 0].contiguous(), gm.dt, gm.ssm_a, gm.z[:, 0].contiguous(), gm.norm_w,
+                       wl.eps, y, None, dev(np.array([2, 9, 0], np.int32)), ys=ys)
+    ref = G.gdn_split_bf16(y)
+    torch.cuda.synchronize()
+    _, got = _untile(ys.data.cpu().numpy().view(np.uint16), 3, vdim, 2)
+    _, want = _untile(ref.data.cpu().numpy().view(np.uint16), 3, vdim, 2)
+    assert not got[:, 1].any(), "the unknown slot's fragments are not zero"
+    np.testing.assert_array_equal(got[:, [0, 2]], want[:, [0, 2]])
+
+
 def test_projections_around_the_mixer():
     """x -> qkv, z, alpha, beta projections -> mixer -> out projection, against the
     oracle's projections and mixer on the same x (small geometry, 3 tokens)."""
