@@ -312,6 +312,61 @@ def layer_decode(G, batches, reps: int = 50):
         del pool
 
 
+def verify_round(G, W, B: int, T: int, reps: int = 20):
+    """One speculative round at batch B: gdn_verify_window over T drafted tokens from the
+    untouched pool (writes h and y, persists nothing), then gdn_commit of n_keep ~
+    U{1..T} tokens per sequence (conv history and state advance).  Seeded synthetic
+    inputs of the decode shapes; one JSON line with the two calls' event-timed mean
+    durations and algorithmic bytes.  The window's h between its two kernels is not
+    counted (the decode step's accounting); the commit reads it as an input."""
+    import numpy as np
+    import torch
+    wl = W.make(f"verify_b{B}_t{T}", B, T, seed=31, state_std=0.02, conv_std=1.0)
+    g = wl.geom
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    pool = G.StatePool(wl.n_slots)
+    pool.state.copy_(dev(wl.state))
+    pool.conv.copy_(dev(wl.conv_state))
+    pool.flags.zero_()
+    n_keep_h = np.random.default_rng(32).integers(1, T + 1, B).astype(np.int32)
+    qkv, alpha, bl, z = dev(wl.qkv), dev(wl.alpha), dev(wl.beta_logit), dev(wl.z)
+    conv_w, dt, ssm_a, norm_w = dev(wl.conv_w), dev(wl.dt), dev(wl.ssm_a), dev(wl.norm_w)
+    n_keep = dev(n_keep_h)
+    h = torch.empty(B, T, g.channels, device="cuda")
+    y = torch.empty(B, T, g.value_dim, device="cuda")
+    window = lambda: G.gdn_verify_window(pool, qkv, conv_w, alpha, bl, dt, ssm_a, z, norm_w, wl.eps, h, y)
+    commit = lambda: G.gdn_commit(pool, qkv, h, alpha, bl, dt, ssm_a, n_keep)
+
+    def mean_us(fn):
+        for _ in range(3):
+            fn()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record()
+        for _ in range(reps):
+            fn()
+        ev[1].record()
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[1]) / reps * 1000.0
+    window()
+    win_us = mean_us(window)
+    com_us = mean_us(commit)
+    C, V, hv = g.channels, g.value_dim, g.h_v
+    state = B * hv * g.s * g.s * 4
+    hist = B * C * (g.d_conv - 1) * 4
+    kept = int(n_keep_h.sum())
+    win_bytes = B * T * C * 4 + hist + state + 2 * B * T * V * 4 + 2 * B * T * hv * 4 + C * g.d_conv * 4
+    com_bytes = 2 * hist + kept * C * 4 + 2 * state + kept * C * 4 + 2 * kept * hv * 4 + C * g.d_conv * 4
+    print(json.dumps({"verify_round": {
+        "B": B, "T": T, "tokens_kept": kept, "window_us": win_us, "commit_us": com_us,
+        "round_us": win_us + com_us,
+        "window_gbps": win_bytes / win_us / 1e3, "commit_gbps": com_bytes / com_us / 1e3,
+        "round_gbps": (win_bytes + com_bytes) / (win_us + com_us) / 1e3,
+        "frac_of_hbm_peak": (win_bytes + com_bytes) / (win_us + com_us) / 1e3 / HBM_PEAK_GBPS,
+        "window_bytes": win_bytes, "commit_bytes": com_bytes,
+        "note": "seeded synthetic inputs of the decode shapes; n_keep ~ U{1..T}; event-timed means"}}),
+        flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -324,6 +379,9 @@ def main():
     ap.add_argument("--layer", default="",
                     help="comma-separated batch sizes: time one decode token of a whole layer "
                          "(projections + mixer) from a HIP graph, instead of the step")
+    ap.add_argument("--verify", default="",
+                    help="B,T: time one speculative round (verify window of T tokens + commit) "
+                         "instead of the step")
     ap.add_argument("--event-every", type=int, default=8,
                     help="record per-kernel HIP events on every N-th timed step")
     args = ap.parse_args()
@@ -352,6 +410,10 @@ def main():
         return
     if args.layer:
         layer_decode(G, [int(v) for v in args.layer.split(",")])
+        return
+    if args.verify:
+        vb, vt = (int(v) for v in args.verify.split(","))
+        verify_round(G, W, vb, vt)
         return
 
     wl = W.CONFIGS[args.config]()
