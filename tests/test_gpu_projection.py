@@ -323,3 +323,44 @@ def test_projections_around_the_mixer():
     torch.cuda.synchronize()
     assert_close("y", gm.y.cpu().numpy().reshape(y_ref.shape), y_ref, 2 * TOL)
     assert_close("out", out.cpu().numpy(), out_ref, 2 * TOL)
+
+
+def test_four_launch_layer_decode_matches_the_oracle():
+    """One decode token of a layer in 4 launches: split x -> qkv, z, alpha and beta logits
+    in one launch -> the single-launch mixer writing y already split -> out projection,
+    against the oracle's projections, mixer and out projection on the same x (a decode
+    batch of 37 sequences, the model's geometry, random slots)."""
+    import torch
+    import gated_deltanet_mixer_gdn_amd as G
+    geom = W.Geom()
+    B, n_embd = 37, 2560
+    wl = W.make("layer4", B, 1, seed=190, geom=geom, n_slots=48, state_std=0.02, conv_std=1.0,
+                slot_choice="random")
+    x, wqkv = W.make_proj(B, n_embd, geom.channels, seed=191)
+    _, wgate = W.make_proj(1, n_embd, geom.value_dim, seed=192)
+    _, wab = W.make_proj(1, n_embd, 2 * geom.h_v, seed=193)
+    _, wout = W.make_proj(1, geom.value_dim, n_embd, seed=194)
+    # the oracle's chain
+    wl.qkv = oracle.project(x, wqkv).reshape(B, 1, -1).astype(np.float32)
+    wl.z = oracle.project(x, wgate).reshape(B, 1, -1).astype(np.float32)
+    ab = oracle.project(x, wab)
+    wl.alpha = ab[:, :geom.h_v].reshape(B, 1, -1).astype(np.float32)
+    wl.beta_logit = ab[:, geom.h_v:].reshape(B, 1, -1).astype(np.float32)
+    res = oracle.run_workload(wl)
+    y_ref = np.stack([r["y"] for r in res]).reshape(B, -1)
+    out_ref = oracle.project(y_ref, wout)
+    # the HIP chain
+    gm = GpuMixer(wl)
+    wp_in = G.gdn_pack_bf16(_w(np.concatenate([wqkv, wgate, wab])))
+    wp_out = G.gdn_pack_bf16(_w(wout))
+    xs = G.gdn_split_bf16(dev(x))
+    qkv, z, alpha, beta = G.gdn_project_multi_bf16(xs, wp_in, (geom.channels, geom.value_dim, geom.h_v, geom.h_v))
+    ys = G.gdn_split_bf16(torch.zeros(B, geom.value_dim, device="cuda"))
+    G.gdn_decode_fused(gm.pool, qkv, gm.conv_w, alpha, beta, gm.dt, gm.ssm_a, z, gm.norm_w, wl.eps, None,
+                       None, gm.slots, ys=ys)
+    out = G.gdn_project_bf16(ys, wp_out)
+    torch.cuda.synchronize()
+    assert_close("out", out.cpu().numpy(), out_ref, 2 * TOL)
+    for b in range(B):
+        slot = int(wl.slots[b])
+        assert_close(f"state[{b}]", gm.pool.state[slot].cpu().numpy(), res[b]["state"], 2 * TOL)
