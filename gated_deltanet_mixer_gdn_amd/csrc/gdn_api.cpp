@@ -219,17 +219,15 @@ int conv_common(const char* fn, gdn_pool* p, const int32_t* slots, const int32_t
     const int n_tb = (T + gdn::kConvTokensPerBlock - 1) / gdn::kConvTokensPerBlock;
     if ((int64_t) B * n_tb > INT32_MAX) return fail(GDN_ERR_ARG, fn, "B*T too large");
     if (int rc = check_f4(qkv, fn, "qkv")) return rc;
-    if (h) {
-        if (int rc = check_f4(conv_w, fn, "conv_w")) return rc;
-        if (int rc = check_f4(h, fn, "h")) return rc;
-    }
+    if (int rc = check_f4(conv_w, fn, "conv_w")) return rc;
+    if (int rc = check_f4(h, fn, "h")) return rc;
     if (slots && !aligned(slots, 4)) return fail(GDN_ERR_ARG, fn, "slots is not 4-byte aligned");
     if (n_tok && !aligned(n_tok, 4)) return fail(GDN_ERR_ARG, fn, "n_tok is not 4-byte aligned");
     if (!slots && B > p->n_slots)
         return fail(GDN_ERR_ARG, fn, "slots is null and B=%d exceeds the pool's %lld slots", B,
                     (long long) p->n_slots);
     const size_t io = (size_t) B * T * channels(p->g) * sizeof(float);
-    if (h && overlap(qkv, io, h, io)) return fail(GDN_ERR_ARG, fn, "h overlaps qkv");
+    if (overlap(qkv, io, h, io)) return fail(GDN_ERR_ARG, fn, "h overlaps qkv");
     gdn::ConvParams c;
     c.conv = p->conv;
     c.slots = slots;
@@ -251,11 +249,12 @@ int conv_common(const char* fn, gdn_pool* p, const int32_t* slots, const int32_t
 }
 
 // Shared by gdn_decode_step (o required, no epilogue), gdn_decode_step_norm (y
-// required, o optional), gdn_verify_window (y, no persist) and gdn_commit (no outputs).
+// required, o optional), gdn_verify_window (y, no persist) and gdn_commit (no outputs;
+// adv_qkv: the raw rows whose first n_tok[b] advance the conv history in the same launch).
 int decode_common(const char* fn, gdn_pool* p, const int32_t* slots, const int32_t* n_tok, int32_t B,
                   int32_t T, const float* h, const float* alpha, const float* beta_logit, const float* dt,
                   const float* ssm_a, const float* z, const float* norm_w, float eps, float* o, float* y,
-                  bool persist, bool outputs, void* stream) {
+                  bool persist, bool outputs, void* stream, const float* adv_qkv = nullptr) {
     if (int rc = check_pool(p, fn)) return rc;
     if (B < 0) return fail(GDN_ERR_ARG, fn, "B=%d is negative", B);
     if (T < 1) return fail(GDN_ERR_ARG, fn, "T=%d must be >= 1", T);
@@ -290,6 +289,10 @@ int decode_common(const char* fn, gdn_pool* p, const int32_t* slots, const int32
         if (overlap(out, o_bytes, p->state, pool_bytes)) return fail(GDN_ERR_ARG, fn, "%s overlaps the pool", name);
     }
     if (o && y && overlap(o, o_bytes, y, o_bytes)) return fail(GDN_ERR_ARG, fn, "o overlaps y");
+    if (adv_qkv) {
+        if (int rc = check_f4(adv_qkv, fn, "qkv")) return rc;
+        if (overlap(adv_qkv, h_bytes, p->state, pool_bytes)) return fail(GDN_ERR_ARG, fn, "qkv overlaps the pool");
+    }
     if (y && overlap(y, o_bytes, z, o_bytes)) return fail(GDN_ERR_ARG, fn, "y overlaps z");
     gdn::StepParams s;
     s.state = p->state;
@@ -304,6 +307,8 @@ int decode_common(const char* fn, gdn_pool* p, const int32_t* slots, const int32
     s.z = y ? z : nullptr;
     s.norm_w = y ? norm_w : nullptr;
     s.y = y;
+    s.conv = adv_qkv ? p->conv : nullptr;
+    s.adv_qkv = adv_qkv;
     s.flags = p->flags;
     s.n_slots = p->n_slots;
     s.B = B;
@@ -353,9 +358,10 @@ int gdn_commit(gdn_pool* p, const int32_t* slots, const int32_t* n_keep, int32_t
                void* stream) {
     const char* fn = "gdn_commit";
     if (B > 0 && !h) return fail(GDN_ERR_ARG, fn, "h is null");
-    if (int rc = conv_common(fn, p, slots, n_keep, B, T, qkv, nullptr, 0.0f, nullptr, true, stream)) return rc;
+    if (B > 0 && !qkv) return fail(GDN_ERR_ARG, fn, "qkv is null");
+    // one launch: the replay of the kept tokens and the advance of their conv history
     return decode_common(fn, p, slots, n_keep, B, T, h, alpha, beta_logit, dt, ssm_a, nullptr, nullptr, 0.0f,
-                         nullptr, nullptr, true, false, stream);
+                         nullptr, nullptr, true, false, stream, qkv);
 }
 
 int gdn_decode_step_norm(gdn_pool* p, const int32_t* slots, const int32_t* n_tok, int32_t B, int32_t T,

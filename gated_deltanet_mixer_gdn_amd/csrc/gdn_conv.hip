@@ -12,8 +12,7 @@ namespace gdn {
 // head's L2 norm is a 16-lane DPP sum.  Inputs are loaded one token ahead.  Only
 // token block 0 reads or writes the stored history; later blocks take their first
 // three history entries from qkv, so blocks never race on it.  persist = 0 leaves
-// the stored history as it was (a speculative window); h = null only advances the
-// history by the sequence's raw rows (the commit of a window).
+// the stored history as it was (a speculative window).
 __global__ __launch_bounds__(256) void conv_silu_norm_kernel(ConvParams p) {
     const int tid = threadIdx.x;
     const int head = blockIdx.y * 16 + (tid >> 4);
@@ -37,21 +36,6 @@ __global__ __launch_bounds__(256) void conv_silu_norm_kernel(ConvParams p) {
 
     ConvGroup ga, gb;
     float* X = p.conv + ((long long) (slot < 0 ? 0 : slot) * C) * kHist;
-    if (!p.h) {
-        // history only: the new history is entries nt, nt+1, nt+2 of the sequence
-        // (stored history x3 x2 x1, raw rows 0..nt-1), written by token block 0
-        if (tb != 0 || nt == 0) return;
-        for (int g = 0; g < 2; ++g) {
-            const long long c = g ? cb : ca;
-            ConvGroup old;
-            old.load_history(X + c * kHist);
-            auto entry = [&](int k) -> f4 {
-                return k == 0 ? old.x3 : k == 1 ? old.x2 : k == 2 ? old.x1 : *(const f4*) (xq + (k - 3) * C + c);
-            };
-            ConvGroup::store_history(X + c * kHist, entry(nt), entry(nt + 1), entry(nt + 2));
-        }
-        return;
-    }
     f4 xa_n = {0.f, 0.f, 0.f, 0.f}, xb_n = xa_n;   // next token's inputs
     if (t_end > t0) {
         ga.load_taps(p.w, ca);

@@ -238,4 +238,16 @@ struct ConvGroup {
     }
 };
 
+// The conv history of channels c..c+3 after their sequence advances by nt >= 1 tokens:
+// entries nt, nt+1, nt+2 of (stored history x3 x2 x1, raw rows 0..nt-1 of xq).  Raw
+// values are only moved, so every kernel that advances a history gets the same bits.
+__device__ __forceinline__ void advance_history(float* X, const float* xq, long long C, long long c, int nt) {
+    ConvGroup old;
+    old.load_history(X + c * kHist);
+    auto entry = [&](int k) -> f4 {
+        return k == 0 ? old.x3 : k == 1 ? old.x2 : k == 2 ? old.x1 : *(const f4*) (xq + (k - 3) * C + c);
+    };
+    ConvGroup::store_history(X + c * kHist, entry(nt), entry(nt + 1), entry(nt + 2));
+}
+
 }  // namespace gdn

@@ -26,8 +26,7 @@ struct ConvParams {
     const int32_t* n_tok;   // [B] or null
     const float* qkv;       // [B][T][C]
     const float* w;         // [C][4]
-    float* h;               // [B][T][C], or null: history-only mode (advance the stored
-                            // history by n_tok raw rows, compute nothing)
+    float* h;               // [B][T][C]
     uint32_t* flags;        // pool flag word
     long long n_slots;
     int B, T, h_k, n_heads; // n_heads = 2*h_k + h_v (128-channel heads)
@@ -49,6 +48,10 @@ struct StepParams {
     const float* z;         // fused gated RMSNorm epilogue: [B][T][h_v*128], or null
     const float* norm_w;    // [128]
     float* y;               // [B][T][h_v*128], or null: no epilogue
+    // commit only (else null): the pool's conv region and the raw qkv rows [B][T][C]
+    // whose first n_tok[b] rows advance the conv history of each sequence
+    float* conv;
+    const float* adv_qkv;
     uint32_t* flags;
     long long n_slots;
     int B, T, h_k, h_v, group;  // group = h_v / h_k

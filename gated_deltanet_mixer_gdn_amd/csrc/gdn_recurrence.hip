@@ -359,6 +359,17 @@ __global__ __launch_bounds__(256) void decode_multi_kernel(StepParams p) {
 #pragma unroll
         for (int m = 0; m < 16; ++m) s[m] = __builtin_nontemporal_load((const f4*) (tile + m * kS));
     }
+    if (p.conv && nt > 0 && tid < 96) {
+        // commit: while the tile loads, advance the conv history by the nt kept rows,
+        // v of this head by every workgroup, q and k of the qk head by the group's
+        // first value head only (no other workgroup touches those channels)
+        const int part = tid >> 5;   // 0: v of head i, 1: q_j, 2: k_j
+        if (part == 0 || i % p.group == 0) {
+            const long long head = part == 0 ? 2 * p.h_k + i : part == 1 ? job.j : p.h_k + job.j;
+            advance_history(p.conv + (long long) job.slot * C * kHist, p.adv_qkv + tok0 * C, C,
+                            head * kS + 4 * (tid & 31), nt);
+        }
+    }
     const float dt_i = p.dt[i];
     const float a_i = p.ssm_a[i];
 
@@ -482,7 +493,7 @@ hipError_t launch_decode_fused(const FusedParams& p, hipStream_t stream) {
 
 hipError_t launch_decode_step(const StepParams& p, hipStream_t stream) {
     const dim3 grid((unsigned) ((long long) p.B * p.h_v));
-    const bool one = p.T == 1;
+    const bool one = p.T == 1 && !p.conv;   // the commit's history advance lives in the multi-token kernel
     if (p.y) {
         if (one) hipLaunchKernelGGL((decode_one_kernel<true>), grid, dim3(256), 0, stream, p);
         else hipLaunchKernelGGL((decode_multi_kernel<true>), grid, dim3(256), 0, stream, p);
