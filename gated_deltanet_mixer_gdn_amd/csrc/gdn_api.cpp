@@ -294,7 +294,7 @@ int decode_common(const char* fn, gdn_pool* p, const int32_t* slots, const int32
         if (overlap(adv_qkv, h_bytes, p->state, pool_bytes)) return fail(GDN_ERR_ARG, fn, "qkv overlaps the pool");
     }
     if (y && overlap(y, o_bytes, z, o_bytes)) return fail(GDN_ERR_ARG, fn, "y overlaps z");
-    gdn::StepParams s;
+    gdn::StepParams s{};
     s.state = p->state;
     s.slots = slots;
     s.n_tok = n_tok;

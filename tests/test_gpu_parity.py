@@ -475,6 +475,34 @@ def test_verify_window_then_commit(T):
     assert torch.equal(win.next_y, kept.next_y)
 
 
+@pytest.mark.parametrize("T", [6, 20])
+def test_verify_window_ragged_with_an_unknown_slot(T):
+    """A window with per-sequence token counts and one unknown slot (a short and a long
+    window): y and h equal decoding the same tokens directly, bit for bit; the unknown
+    slot's rows are zero and flagged; the pool is untouched."""
+    import torch
+    import gated_deltanet_mixer_gdn_amd as G
+    wl = W.make("window-ragged", 4, T, seed=95 + T, n_slots=6, state_std=0.02, conv_std=1.0,
+                slot_choice="random")
+    n_tok = np.array([T, 1, 0, max(T - 2, 1)], np.int32)
+    slots = wl.slots.copy()
+    slots[3] = 99                                    # outside the pool
+    log(f"ragged window T={T} n_tok={n_tok.tolist()} slots={slots.tolist()}")
+    win = GpuMixer(wl)
+    before_s, before_c = win.pool.state.clone(), win.pool.conv.clone()
+    h = torch.full_like(win.h, 3.0)
+    y = torch.full_like(win.y, 3.0)
+    G.gdn_verify_window(win.pool, win.qkv, win.conv_w, win.alpha, win.beta_logit, win.dt, win.ssm_a, win.z,
+                        win.norm_w, wl.eps, h, y, dev(slots), dev(n_tok))
+    torch.cuda.synchronize()
+    assert torch.equal(win.pool.state, before_s) and torch.equal(win.pool.conv, before_c), "window wrote the pool"
+    assert int(win.pool.flags.item()) & G.GDN_FLAG_BAD_SLOT
+    assert not y[3].any() and not h[3].any()
+    direct = GpuMixer(wl)
+    direct.run(fused=True, slots=dev(slots), n_tok=dev(n_tok))
+    assert torch.equal(y, direct.y) and torch.equal(h, direct.h)
+
+
 # ------------------------------------------------------------------ alpha / beta projections
 @pytest.mark.parametrize("B,T,n_embd,h_v", [(1, 1, 2560, 48), (3, 1, 2560, 48), (256, 1, 2560, 48),
                                             (16, 512, 2560, 48), (5, 2, 260, 6), (2, 3, 4, 3)])
