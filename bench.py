@@ -318,7 +318,9 @@ def verify_round(G, W, B: int, T: int, reps: int = 20):
     U{1..T} tokens per sequence (conv history and state advance).  Seeded synthetic
     inputs of the decode shapes; one JSON line with the two calls' event-timed mean
     durations and algorithmic bytes.  The window's h between its two kernels is not
-    counted (the decode step's accounting); the commit reads it as an input."""
+    counted (the decode step's accounting); the commit reads it as an input.  Also
+    timed: gdn_commit_window, the commit of one window fused with the next window (a
+    second set of window buffers), which reads each state tile and history once."""
     import numpy as np
     import torch
     wl = W.make(f"verify_b{B}_t{T}", B, T, seed=31, state_std=0.02, conv_std=1.0)
@@ -336,6 +338,10 @@ def verify_round(G, W, B: int, T: int, reps: int = 20):
     y = torch.empty(B, T, g.value_dim, device="cuda")
     window = lambda: G.gdn_verify_window(pool, qkv, conv_w, alpha, bl, dt, ssm_a, z, norm_w, wl.eps, h, y)
     commit = lambda: G.gdn_commit(pool, qkv, h, alpha, bl, dt, ssm_a, n_keep)
+    qkv2, alpha2, bl2, z2 = qkv.clone(), alpha.clone(), bl.clone(), z.clone()
+    h2, y2 = torch.empty_like(h), torch.empty_like(y)
+    fused = lambda: G.gdn_commit_window(pool, (qkv, h, alpha, bl), n_keep, qkv2, conv_w, alpha2, bl2, dt, ssm_a,
+                                        z2, norm_w, wl.eps, h2, y2)
 
     def mean_us(fn):
         for _ in range(3):
@@ -350,12 +356,14 @@ def verify_round(G, W, B: int, T: int, reps: int = 20):
     window()
     win_us = mean_us(window)
     com_us = mean_us(commit)
+    fused_us = mean_us(fused)
     C, V, hv = g.channels, g.value_dim, g.h_v
     state = B * hv * g.s * g.s * 4
     hist = B * C * (g.d_conv - 1) * 4
     kept = int(n_keep_h.sum())
     win_bytes = B * T * C * 4 + hist + state + 2 * B * T * V * 4 + 2 * B * T * hv * 4 + C * g.d_conv * 4
     com_bytes = 2 * hist + kept * C * 4 + 2 * state + kept * C * 4 + 2 * kept * hv * 4 + C * g.d_conv * 4
+    fused_bytes = win_bytes + com_bytes - state - hist   # one state read and one history read fewer
     print(json.dumps({"verify_round": {
         "B": B, "T": T, "tokens_kept": kept, "window_us": win_us, "commit_us": com_us,
         "round_us": win_us + com_us,
@@ -363,6 +371,9 @@ def verify_round(G, W, B: int, T: int, reps: int = 20):
         "round_gbps": (win_bytes + com_bytes) / (win_us + com_us) / 1e3,
         "frac_of_hbm_peak": (win_bytes + com_bytes) / (win_us + com_us) / 1e3 / HBM_PEAK_GBPS,
         "window_bytes": win_bytes, "commit_bytes": com_bytes,
+        "commit_window_us": fused_us, "commit_window_bytes": fused_bytes,
+        "commit_window_gbps": fused_bytes / fused_us / 1e3,
+        "commit_window_frac_of_hbm_peak": fused_bytes / fused_us / 1e3 / HBM_PEAK_GBPS,
         "note": "seeded synthetic inputs of the decode shapes; n_keep ~ U{1..T}; event-timed means"}}),
         flush=True)
 

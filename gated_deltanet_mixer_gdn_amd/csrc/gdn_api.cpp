@@ -207,10 +207,11 @@ int gdn_state_pool_zero(gdn_pool* p, const int32_t* slots, int32_t n, void* stre
 
 namespace {
 
-// Shared by gdn_conv_silu_norm (persist, h required), gdn_verify_window (no persist)
-// and gdn_commit (persist, h = null: history only).
+// Shared by gdn_conv_silu_norm (persist) and gdn_verify_window / gdn_commit_window
+// (no persist).  With built set, the checked parameters go there and nothing launches.
 int conv_common(const char* fn, gdn_pool* p, const int32_t* slots, const int32_t* n_tok, int32_t B, int32_t T,
-                const float* qkv, const float* conv_w, float eps, float* h, bool persist, void* stream) {
+                const float* qkv, const float* conv_w, float eps, float* h, bool persist, void* stream,
+                gdn::ConvParams* built = nullptr) {
     if (int rc = check_pool(p, fn)) return rc;
     if (B < 0) return fail(GDN_ERR_ARG, fn, "B=%d is negative", B);
     if (T < 1) return fail(GDN_ERR_ARG, fn, "T=%d must be >= 1", T);
@@ -228,7 +229,7 @@ int conv_common(const char* fn, gdn_pool* p, const int32_t* slots, const int32_t
                     (long long) p->n_slots);
     const size_t io = (size_t) B * T * channels(p->g) * sizeof(float);
     if (overlap(qkv, io, h, io)) return fail(GDN_ERR_ARG, fn, "h overlaps qkv");
-    gdn::ConvParams c;
+    gdn::ConvParams c{};
     c.conv = p->conv;
     c.slots = slots;
     c.n_tok = n_tok;
@@ -245,16 +246,22 @@ int conv_common(const char* fn, gdn_pool* p, const int32_t* slots, const int32_t
     c.persist = persist ? 1 : 0;
     c.eps = eps;
     c.qscale = p->g.scale_after_readout ? 1.0f : 1.0f / std::sqrt((float) p->g.s);
+    if (built) {
+        *built = c;
+        return ok();
+    }
     return launched(gdn::launch_conv_silu_norm(c, static_cast<hipStream_t>(stream)), fn);
 }
 
 // Shared by gdn_decode_step (o required, no epilogue), gdn_decode_step_norm (y
 // required, o optional), gdn_verify_window (y, no persist) and gdn_commit (no outputs;
 // adv_qkv: the raw rows whose first n_tok[b] advance the conv history in the same launch).
+// With built set, the checked parameters go there and nothing launches.
 int decode_common(const char* fn, gdn_pool* p, const int32_t* slots, const int32_t* n_tok, int32_t B,
                   int32_t T, const float* h, const float* alpha, const float* beta_logit, const float* dt,
                   const float* ssm_a, const float* z, const float* norm_w, float eps, float* o, float* y,
-                  bool persist, bool outputs, void* stream, const float* adv_qkv = nullptr) {
+                  bool persist, bool outputs, void* stream, const float* adv_qkv = nullptr,
+                  gdn::StepParams* built = nullptr) {
     if (int rc = check_pool(p, fn)) return rc;
     if (B < 0) return fail(GDN_ERR_ARG, fn, "B=%d is negative", B);
     if (T < 1) return fail(GDN_ERR_ARG, fn, "T=%d must be >= 1", T);
@@ -320,6 +327,10 @@ int decode_common(const char* fn, gdn_pool* p, const int32_t* slots, const int32
     s.gate_silu = p->g.gate_silu;
     s.eps = eps;
     s.oscale = p->g.scale_after_readout ? 1.0f / std::sqrt((float) p->g.s) : 1.0f;
+    if (built) {
+        *built = s;
+        return ok();
+    }
     return launched(gdn::launch_decode_step(s, static_cast<hipStream_t>(stream)), fn);
 }
 
@@ -362,6 +373,47 @@ int gdn_commit(gdn_pool* p, const int32_t* slots, const int32_t* n_keep, int32_t
     // one launch: the replay of the kept tokens and the advance of their conv history
     return decode_common(fn, p, slots, n_keep, B, T, h, alpha, beta_logit, dt, ssm_a, nullptr, nullptr, 0.0f,
                          nullptr, nullptr, true, false, stream, qkv);
+}
+
+int gdn_commit_window(gdn_pool* p, const int32_t* slots, int32_t B, const int32_t* n_keep, int32_t T0,
+                      const float* qkv0, const float* h0, const float* alpha0, const float* beta_logit0,
+                      const int32_t* n_tok, int32_t T1, const float* qkv1, const float* conv_w,
+                      const float* alpha1, const float* beta_logit1, const float* dt, const float* ssm_a,
+                      const float* z1, const float* norm_w, float eps, float* h1, float* y1, void* stream) {
+    const char* fn = "gdn_commit_window";
+    if (B > 0 && (!h0 || !qkv0)) return fail(GDN_ERR_ARG, fn, "qkv0 or h0 is null");
+    if (B > 0 && (!h1 || !y1)) return fail(GDN_ERR_ARG, fn, "h1 or y1 is null");
+    gdn::StepParams com, win;
+    gdn::ConvParams cv;
+    if (int rc = decode_common(fn, p, slots, n_keep, B, T0, h0, alpha0, beta_logit0, dt, ssm_a, nullptr, nullptr,
+                               0.0f, nullptr, nullptr, true, false, stream, qkv0, &com))
+        return rc;
+    if (int rc = conv_common(fn, p, slots, n_tok, B, T1, qkv1, conv_w, eps, h1, false, stream, &cv)) return rc;
+    if (int rc = decode_common(fn, p, slots, n_tok, B, T1, h1, alpha1, beta_logit1, dt, ssm_a, z1, norm_w, eps,
+                               nullptr, y1, false, true, stream, nullptr, &win))
+        return rc;
+    if (B == 0) return ok();
+    // the conv launch writes h1 while the round launch still reads the previous
+    // window's arrays, and the round launch writes y1 beside those reads
+    const size_t ch0 = (size_t) B * T0 * channels(p->g) * sizeof(float);
+    const size_t ab0 = (size_t) B * T0 * p->g.h_v * sizeof(float);
+    const size_t h1_bytes = (size_t) B * T1 * channels(p->g) * sizeof(float);
+    const size_t y1_bytes = (size_t) B * T1 * p->g.h_v * p->g.s * sizeof(float);
+    const struct { const void* ptr; size_t n; const char* name; } prev[] = {
+        {qkv0, ch0, "qkv0"}, {h0, ch0, "h0"}, {alpha0, ab0, "alpha0"}, {beta_logit0, ab0, "beta_logit0"}};
+    for (const auto& a : prev) {
+        if (overlap(h1, h1_bytes, a.ptr, a.n)) return fail(GDN_ERR_ARG, fn, "h1 overlaps %s", a.name);
+        if (overlap(y1, y1_bytes, a.ptr, a.n)) return fail(GDN_ERR_ARG, fn, "y1 overlaps %s", a.name);
+    }
+    // the history advance moves from the recurrence into the conv launch
+    cv.adv_qkv = qkv0;
+    cv.n_adv = n_keep;
+    cv.adv_T = T0;
+    com.conv = nullptr;
+    com.adv_qkv = nullptr;
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    if (int rc = launched(gdn::launch_conv_silu_norm(cv, st), fn)) return rc;
+    return launched(gdn::launch_commit_window(com, win, st), fn);
 }
 
 int gdn_decode_step_norm(gdn_pool* p, const int32_t* slots, const int32_t* n_tok, int32_t B, int32_t T,

@@ -36,6 +36,17 @@ __global__ __launch_bounds__(256) void conv_silu_norm_kernel(ConvParams p) {
 
     ConvGroup ga, gb;
     float* X = p.conv + ((long long) (slot < 0 ? 0 : slot) * C) * kHist;
+    if (p.adv_qkv && tb == 0 && slot >= 0) {
+        // the commit of the previous window comes first: its kept rows advance the
+        // stored history (kept whatever this call's tokens do), and token 0 below
+        // starts from the advanced history (each thread rereads only what it wrote)
+        const int na = read_ntok(p.n_adv, b, p.adv_T, p.flags, reporter);
+        if (na > 0) {
+            const float* xa = p.adv_qkv + (long long) b * p.adv_T * C;
+            advance_history(X, xa, C, ca, na);
+            advance_history(X, xa, C, cb, na);
+        }
+    }
     f4 xa_n = {0.f, 0.f, 0.f, 0.f}, xb_n = xa_n;   // next token's inputs
     if (t_end > t0) {
         ga.load_taps(p.w, ca);

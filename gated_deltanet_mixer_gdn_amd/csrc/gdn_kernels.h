@@ -33,6 +33,11 @@ struct ConvParams {
     int n_tb;               // token blocks per sequence
     int persist;            // 0: leave the stored history untouched (speculative window)
     float eps, qscale;
+    // a commit first (else null): the stored history advances by the first n_adv[b] raw
+    // rows of adv_qkv [B][adv_T][C] and is stored, and this call's tokens start from it
+    const float* adv_qkv;
+    const int32_t* n_adv;
+    int adv_T;
 };
 
 struct StepParams {
@@ -111,6 +116,7 @@ struct ZeroParams {
 
 hipError_t launch_conv_silu_norm(const ConvParams& p, hipStream_t stream);
 hipError_t launch_decode_step(const StepParams& p, hipStream_t stream);
+hipError_t launch_commit_window(const StepParams& com, const StepParams& win, hipStream_t stream);
 hipError_t launch_decode_fused(const FusedParams& p, hipStream_t stream);
 hipError_t launch_gated_rmsnorm(const NormParams& p, hipStream_t stream);
 hipError_t launch_zero(const ZeroParams& p, hipStream_t stream);

@@ -327,10 +327,21 @@ __global__ __launch_bounds__(256) void decode_fused_kernel(FusedParams p) {
 // single-token kernel's order), with the chunk's z loaded one chunk ahead.
 constexpr int kNormChunk = 8;
 
+// Shared memory of one multi-token workgroup.
+struct MultiLds {
+    f4 qk[4][64];                        // per wave: q as 32 float4, then k as 32 float4
+    f4 o_ring[2][kNormChunk][32];        // [chunk parity][token][float4 column group]
+};
+
+// The token loop of the multi-token recurrence for head (job.b, job.i): tokens 0..nt-1
+// of the inputs p describes (rows of h, alpha, beta_logit and z of sequence job.b, T
+// per sequence), the state in s[] (in and out).  Outputs of tokens nt..T-1 are written
+// as zero.  Every thread of the workgroup calls it.
 template <bool kNorm>
-__global__ __launch_bounds__(256) void decode_multi_kernel(StepParams p) {
-    __shared__ f4 qk_lds[4][64];                    // per wave: q as 32 float4, then k as 32 float4
-    __shared__ f4 o_ring[2][kNormChunk][32];        // [chunk parity][token][float4 column group]
+__device__ __forceinline__ void multi_tokens(const StepParams& p, const HeadJob& job, int nt, f4 (&s)[16],
+                                             MultiLds& lds) {
+    f4 (&qk_lds)[4][64] = lds.qk;
+    f4 (&o_ring)[2][kNormChunk][32] = lds.o_ring;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -338,9 +349,7 @@ __global__ __launch_bounds__(256) void decode_multi_kernel(StepParams p) {
     const int cg = lane & 7;
     const int rg = lane >> 3;
     const int col = wave * 32 + cg * 4;
-    const HeadJob job = head_job(p, tid == 0);
     const int i = job.i;
-    const int nt = job.nt;
     const long long C = (long long) (2 * p.h_k + p.h_v) * kS;
     const long long tok0 = (long long) job.b * p.T;
     const long long q_off = (long long) job.j * kS + (lane & 31) * 4 + (lane < 32 ? 0 : (long long) p.h_k * kS);
@@ -352,24 +361,6 @@ __global__ __launch_bounds__(256) void decode_multi_kernel(StepParams p) {
     const int oc = (int) (scatter_sum4(f4{0.f, 1.f, 2.f, 3.f}) * 0.25f);
     const bool reads_out = (lane & 8) == 0;
 
-    float* tile = nullptr;
-    f4 s[16];
-    if (nt > 0) {
-        tile = p.state + ((long long) job.slot * p.h_v + i) * (kS * kS) + (rg * 16) * kS + col;
-#pragma unroll
-        for (int m = 0; m < 16; ++m) s[m] = __builtin_nontemporal_load((const f4*) (tile + m * kS));
-    }
-    if (p.conv && nt > 0 && tid < 96) {
-        // commit: while the tile loads, advance the conv history by the nt kept rows,
-        // v of this head by every workgroup, q and k of the qk head by the group's
-        // first value head only (no other workgroup touches those channels)
-        const int part = tid >> 5;   // 0: v of head i, 1: q_j, 2: k_j
-        if (part == 0 || i % p.group == 0) {
-            const long long head = part == 0 ? 2 * p.h_k + i : part == 1 ? job.j : p.h_k + job.j;
-            advance_history(p.conv + (long long) job.slot * C * kHist, p.adv_qkv + tok0 * C, C,
-                            head * kS + 4 * (tid & 31), nt);
-        }
-    }
     const float dt_i = p.dt[i];
     const float a_i = p.ssm_a[i];
 
@@ -476,7 +467,71 @@ __global__ __launch_bounds__(256) void decode_multi_kernel(StepParams p) {
             if (kNorm) *(f4*) (p.y + e) = zero;
         }
     }
+}
+
+template <bool kNorm>
+__global__ __launch_bounds__(256) void decode_multi_kernel(StepParams p) {
+    __shared__ MultiLds lds;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int rg = lane >> 3;
+    const int col = wave * 32 + (lane & 7) * 4;
+    const HeadJob job = head_job(p, tid == 0);
+    const int i = job.i;
+    const int nt = job.nt;
+    const long long C = (long long) (2 * p.h_k + p.h_v) * kS;
+    const long long tok0 = (long long) job.b * p.T;
+    float* tile = nullptr;
+    f4 s[16];
+    if (nt > 0) {
+        tile = p.state + ((long long) job.slot * p.h_v + i) * (kS * kS) + (rg * 16) * kS + col;
+#pragma unroll
+        for (int m = 0; m < 16; ++m) s[m] = __builtin_nontemporal_load((const f4*) (tile + m * kS));
+    }
+    if (p.conv && nt > 0 && tid < 96) {
+        // commit: while the tile loads, advance the conv history by the nt kept rows,
+        // v of this head by every workgroup, q and k of the qk head by the group's
+        // first value head only (no other workgroup touches those channels)
+        const int part = tid >> 5;   // 0: v of head i, 1: q_j, 2: k_j
+        if (part == 0 || i % p.group == 0) {
+            const long long head = part == 0 ? 2 * p.h_k + i : part == 1 ? job.j : p.h_k + job.j;
+            advance_history(p.conv + (long long) job.slot * C * kHist, p.adv_qkv + tok0 * C, C,
+                            head * kS + 4 * (tid & 31), nt);
+        }
+    }
+    multi_tokens<kNorm>(p, job, nt, s, lds);
     if (nt > 0 && p.persist) store_tile(s, tile);
+}
+
+// A commit and the next speculative window in one launch, for a decode loop that
+// verifies the next drafts right after accepting the last ones.  One workgroup per
+// (sequence, value head) reads its state tile once, replays the previous window's
+// n_keep accepted tokens from that window's h (com: the commit, no outputs), stores
+// the committed tile, and runs the next window's tokens from it in registers (win:
+// y out, nothing stored).  The conv launch before this one advanced the history by
+// the kept rows and computed the next window's h from it.  With the same token loop
+// the results equal gdn_commit followed by gdn_verify_window bit for bit, at one state
+// read per round instead of two.
+__global__ __launch_bounds__(256) void commit_window_kernel(StepParams com, StepParams win) {
+    __shared__ MultiLds lds;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int rg = lane >> 3;
+    const int col = (tid >> 6) * 32 + (lane & 7) * 4;
+    const HeadJob job = head_job(win, tid == 0);   // the slot and the window's token count
+    const int nk = job.slot < 0 ? 0 : read_ntok(com.n_tok, job.b, com.T, win.flags, tid == 0 && job.i == 0);
+    float* tile = nullptr;
+    f4 s[16];
+    if (nk > 0 || job.nt > 0) {
+        tile = win.state + ((long long) job.slot * win.h_v + job.i) * (kS * kS) + (rg * 16) * kS + col;
+        load_tile(s, tile);
+    }
+    if (nk > 0) {
+        multi_tokens<false>(com, job, nk, s, lds);
+        store_tile(s, tile);
+    }
+    multi_tokens<true>(win, job, job.nt, s, lds);
 }
 
 // ------------------------------------------------------------------ launch
@@ -488,6 +543,12 @@ hipError_t launch_decode_fused(const FusedParams& p, hipStream_t stream) {
     case 3: hipLaunchKernelGGL(decode_fused_par_kernel<3>, grid, dim3(768), 0, stream, p); break;
     default: hipLaunchKernelGGL(decode_fused_kernel, grid, dim3(256), 0, stream, p); break;
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_commit_window(const StepParams& com, const StepParams& win, hipStream_t stream) {
+    hipLaunchKernelGGL(commit_window_kernel, dim3((unsigned) ((long long) win.B * win.h_v)), dim3(256), 0, stream,
+                       com, win);
     return hipGetLastError();
 }
 

@@ -21,7 +21,8 @@ EXPORTS = (
     "gdn_abi_version", "gdn_last_error", "gdn_state_pool_bytes", "gdn_state_pool_create",
     "gdn_state_pool_destroy", "gdn_state_pool_state", "gdn_state_pool_conv", "gdn_state_pool_flags",
     "gdn_state_pool_slots", "gdn_state_pool_zero", "gdn_conv_silu_norm", "gdn_decode_step",
-    "gdn_decode_step_norm", "gdn_decode_fused", "gdn_verify_window", "gdn_commit", "gdn_gated_rmsnorm",
+    "gdn_decode_step_norm", "gdn_decode_fused", "gdn_verify_window", "gdn_commit", "gdn_commit_window",
+    "gdn_gated_rmsnorm",
     "gdn_ab_project", "gdn_split_bf16_bytes", "gdn_pack_bf16_bytes", "gdn_split_bf16", "gdn_pack_bf16",
     "gdn_project_bf16", "gdn_project2_bf16", "gdn_project_workspace_bytes", "gdn_project_multi_bf16",
 )
@@ -92,6 +93,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "gdn_verify_window": ([vp, vp, vp, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, f32, vp, vp, vp],
                               ctypes.c_int),
         "gdn_commit": ([vp, vp, vp, i32, i32, vp, vp, vp, vp, vp, vp, vp], ctypes.c_int),
+        "gdn_commit_window": ([vp, vp, i32, vp, i32, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp,
+                               f32, vp, vp, vp], ctypes.c_int),
         "gdn_gated_rmsnorm": ([vp, vp, vp, f32, i64, i32, i32, vp, vp], ctypes.c_int),
         "gdn_ab_project": ([vp, vp, vp, i64, i32, i32, vp, vp, vp], ctypes.c_int),
         "gdn_split_bf16_bytes": ([i64, i32], ctypes.c_int64),
@@ -287,6 +290,29 @@ def gdn_commit(pool: StatePool, qkv, h, alpha, beta_logit, dt, ssm_a, n_keep=Non
             _f32(dt, "dt", (g.h_v,)), _f32(ssm_a, "ssm_a", (g.h_v,)))
     _check(load_library().gdn_commit(pool.handle, _i32(slots, "slots", B), _i32(n_keep, "n_keep", B), B, T,
                                      *ptrs, _stream(qkv)))
+
+
+def gdn_commit_window(pool: StatePool, prev, n_keep, qkv, conv_w, alpha, beta_logit, dt, ssm_a, z, norm_w,
+                      eps: float, h, y, slots=None, n_tok=None):
+    """One speculative round: gdn_commit of the previous window (prev = its
+    (qkv, h, alpha, beta_logit), n_keep of its tokens) then gdn_verify_window of the
+    next (qkv, alpha, beta_logit, z -> h, y), with each state tile read once."""
+    g = pool.geom
+    qkv0, h0, alpha0, beta0 = prev
+    B, T0 = qkv0.shape[0], qkv0.shape[1]
+    T1 = qkv.shape[1]
+    if qkv.shape[0] != B:
+        raise ValueError(f"the two windows have {B} and {qkv.shape[0]} sequences")
+    p0 = (_f32(qkv0, "qkv0", (B, T0, g.channels)), _f32(h0, "h0", (B, T0, g.channels)),
+          _f32(alpha0, "alpha0", (B, T0, g.h_v)), _f32(beta0, "beta_logit0", (B, T0, g.h_v)))
+    p1 = (_f32(qkv, "qkv", (B, T1, g.channels)), _f32(conv_w, "conv_w", (g.channels, g.d_conv)),
+          _f32(alpha, "alpha", (B, T1, g.h_v)), _f32(beta_logit, "beta_logit", (B, T1, g.h_v)),
+          _f32(dt, "dt", (g.h_v,)), _f32(ssm_a, "ssm_a", (g.h_v,)), _f32(z, "z", (B, T1, g.h_v * g.s)),
+          _f32(norm_w, "norm_w", (g.s,)))
+    _check(load_library().gdn_commit_window(pool.handle, _i32(slots, "slots", B), B, _i32(n_keep, "n_keep", B), T0,
+                                            *p0, _i32(n_tok, "n_tok", B), T1, *p1, float(eps),
+                                            _f32(h, "h", (B, T1, g.channels)), _f32(y, "y", (B, T1, g.h_v * g.s)),
+                                            _stream(qkv)))
 
 
 def gdn_gated_rmsnorm(o, z, w, eps: float, y, gate_silu: bool = False):

@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 5
+#define GDN_ABI_VERSION 6
 
 enum {
     GDN_OK = 0,
@@ -222,6 +222,20 @@ int gdn_verify_window(gdn_pool* p, const int32_t* slots, const int32_t* n_tok, i
 int gdn_commit(gdn_pool* p, const int32_t* slots, const int32_t* n_keep, int32_t B, int32_t T,
                const float* qkv, const float* h, const float* alpha, const float* beta_logit,
                const float* dt, const float* ssm_a, void* stream);
+
+/* One speculative round: gdn_commit of the previous window (n_keep [B] of its T0
+ * tokens, its qkv0, h0, alpha0, beta_logit0) followed by gdn_verify_window of the next
+ * (T1 tokens, n_tok, qkv1, alpha1, beta_logit1, z1 -> h1, y1), with the same slots.
+ * The results (state, conv history, h1, y1, flags) equal those two calls bit for bit;
+ * each state tile is read once instead of twice (two launches: the conv of the
+ * window after the history advance, then the replay, the tile store and the window
+ * from the committed tile in registers).  Besides the two calls' own checks, h1 and y1
+ * may not overlap qkv0, h0, alpha0 or beta_logit0 (GDN_ERR_ARG).  B = 0 is a no-op. */
+int gdn_commit_window(gdn_pool* p, const int32_t* slots, int32_t B, const int32_t* n_keep, int32_t T0,
+                      const float* qkv0, const float* h0, const float* alpha0, const float* beta_logit0,
+                      const int32_t* n_tok, int32_t T1, const float* qkv1, const float* conv_w,
+                      const float* alpha1, const float* beta_logit1, const float* dt, const float* ssm_a,
+                      const float* z1, const float* norm_w, float eps, float* h1, float* y1, void* stream);
 
 /* Step 7 of gdn_layer: per row of s values,
  *   y = o / sqrt(mean(o^2) + eps) * w * sigmoid(z)      (gate_silu = 0)

@@ -71,7 +71,7 @@ def test_library_is_built_for_gfx950_only(tmp_path):
 
 
 def test_abi_version(L):
-    assert L.gdn_abi_version() == 5
+    assert L.gdn_abi_version() == 6
 
 
 def _geom(h_k=16, h_v=48, s=128, d_conv=4):
@@ -213,6 +213,15 @@ def test_new_entry_points_reject_null_pool(L):
     assert b"h is null" in L.gdn_last_error()
     assert L.gdn_commit(None, None, None, 1, 2, 16, 16, 16, 16, 16, 16, None) == GDN_ERR_ARG
     assert L.gdn_last_error().startswith(b"gdn_commit: pool is null")
+    args = [None, None, 1, None, 2, 16, 16, 16, 16, None, 3, 16, 16, 16, 16, 16, 16, 16, 16, 1e-6, 16, 16, None]
+    assert L.gdn_commit_window(*args) == GDN_ERR_ARG
+    assert L.gdn_last_error().startswith(b"gdn_commit_window: pool is null")
+    for k in (6, 20, 21):                             # h0, h1, y1
+        bad = list(args)
+        bad[k] = None
+        assert L.gdn_commit_window(*bad) == GDN_ERR_ARG
+        assert b"is null" in L.gdn_last_error()
+    assert L.gdn_commit_window(*(args[:2] + [0] + args[3:])) == GDN_ERR_ARG   # B = 0 still checks the pool
 
 
 def test_ab_project_argument_errors(L):

@@ -503,6 +503,70 @@ def test_verify_window_ragged_with_an_unknown_slot(T):
     assert torch.equal(y, direct.y) and torch.equal(h, direct.h)
 
 
+@pytest.mark.parametrize("T0,T1,ragged", [(4, 4, True), (6, 1, True), (20, 9, True), (4, 3, False)])
+def test_commit_window_equals_commit_then_window(T0, T1, ragged):
+    """gdn_commit_window (the commit of one window and the next window with each state
+    tile read once) equals gdn_commit followed by gdn_verify_window bit for bit: state,
+    conv history, h, y and flags.  Ragged: per-sequence n_keep (0, all, some) and window
+    token counts (0 included) and one unknown slot.  With everything kept, the next
+    window's y and h also equal decoding all T0 + T1 tokens directly, and the oracle."""
+    import torch
+    import gated_deltanet_mixer_gdn_amd as G
+    B = 5
+    wl = W.make("round", B, T0 + T1, seed=170 + T0 + T1, n_slots=9, state_std=0.02, conv_std=1.0,
+                slot_choice="random")
+    slots = wl.slots.copy()
+    if ragged:
+        n_keep = np.array([T0, 0, 1, max(T0 - 1, 0), 2], np.int32)
+        n_tok = np.array([T1, max(T1 - 1, 0), 0, 1, T1], np.int32)
+        slots[4] = 77                                 # outside the pool
+        nk, nt = dev(n_keep), dev(n_tok)
+    else:
+        nk = nt = None
+    log(f"commit window T0={T0} T1={T1} ragged={ragged}")
+    sl = dev(slots)
+    two, one = GpuMixer(wl), GpuMixer(wl)
+    w0 = lambda gm, a: getattr(gm, a)[:, :T0].contiguous()
+    w1 = lambda gm, a: getattr(gm, a)[:, T0:].contiguous()
+    outs = {}
+    for name, gm in (("two", two), ("one", one)):
+        g = wl.geom
+        h0 = torch.empty(B, T0, g.channels, device="cuda")
+        y0 = torch.empty(B, T0, g.value_dim, device="cuda")
+        G.gdn_verify_window(gm.pool, w0(gm, "qkv"), gm.conv_w, w0(gm, "alpha"), w0(gm, "beta_logit"), gm.dt,
+                            gm.ssm_a, w0(gm, "z"), gm.norm_w, wl.eps, h0, y0, sl)
+        h1 = torch.full((B, T1, g.channels), 3.0, device="cuda")
+        y1 = torch.full((B, T1, g.value_dim), 3.0, device="cuda")
+        prev = (w0(gm, "qkv"), h0, w0(gm, "alpha"), w0(gm, "beta_logit"))
+        if name == "two":
+            G.gdn_commit(gm.pool, prev[0], h0, prev[2], prev[3], gm.dt, gm.ssm_a, nk, sl)
+            G.gdn_verify_window(gm.pool, w1(gm, "qkv"), gm.conv_w, w1(gm, "alpha"), w1(gm, "beta_logit"), gm.dt,
+                                gm.ssm_a, w1(gm, "z"), gm.norm_w, wl.eps, h1, y1, sl, nt)
+        else:
+            G.gdn_commit_window(gm.pool, prev, nk, w1(gm, "qkv"), gm.conv_w, w1(gm, "alpha"), w1(gm, "beta_logit"),
+                                gm.dt, gm.ssm_a, w1(gm, "z"), gm.norm_w, wl.eps, h1, y1, sl, nt)
+        outs[name] = (h1, y1)
+    torch.cuda.synchronize()
+    for a, b_, what in ((two.pool.state, one.pool.state, "state"), (two.pool.conv, one.pool.conv, "conv history"),
+                        (outs["two"][0], outs["one"][0], "h"), (outs["two"][1], outs["one"][1], "y"),
+                        (two.pool.flags, one.pool.flags, "flags")):
+        assert torch.equal(a, b_), f"{what} differs"
+    h1, y1 = outs["one"]
+    assert y1.abs().max().item() > 0
+    if ragged:
+        assert int(one.pool.flags.item()) & G.GDN_FLAG_BAD_SLOT
+        assert not y1[4].any() and not h1[4].any()
+        assert not y1[2].any()
+    else:
+        assert int(one.pool.flags.item()) == 0
+        direct = GpuMixer(wl)
+        direct.run(fused=True)
+        assert torch.equal(y1, direct.y[:, T0:]) and torch.equal(h1, direct.h[:, T0:])
+        res = oracle.run_workload(wl)
+        ref = np.stack([r["y"] for r in res])[:, T0:]
+        assert_close("round y", y1.cpu().numpy(), ref, 2 * STEP_TOL)
+
+
 # ------------------------------------------------------------------ alpha / beta projections
 @pytest.mark.parametrize("B,T,n_embd,h_v", [(1, 1, 2560, 48), (3, 1, 2560, 48), (256, 1, 2560, 48),
                                             (16, 512, 2560, 48), (5, 2, 260, 6), (2, 3, 4, 3)])
