@@ -361,11 +361,12 @@ def verify_round(G, W, B: int, T: int, reps: int = 20):
     state = B * hv * g.s * g.s * 4
     hist = B * C * (g.d_conv - 1) * 4
     kept = int(n_keep_h.sum())
+    adv = int(np.minimum(n_keep_h, g.d_conv - 1).sum())    # raw rows that end up in the history
     win_bytes = B * T * C * 4 + hist + state + 2 * B * T * V * 4 + 2 * B * T * hv * 4 + C * g.d_conv * 4
-    com_bytes = 2 * hist + kept * C * 4 + 2 * state + kept * C * 4 + 2 * kept * hv * 4 + C * g.d_conv * 4
+    com_bytes = 2 * hist + adv * C * 4 + 2 * state + kept * C * 4 + 2 * kept * hv * 4 + C * g.d_conv * 4
     fused_bytes = win_bytes + com_bytes - state - hist   # one state read and one history read fewer
     print(json.dumps({"verify_round": {
-        "B": B, "T": T, "tokens_kept": kept, "window_us": win_us, "commit_us": com_us,
+        "B": B, "T": T, "tokens_kept": kept, "history_rows_read": adv, "window_us": win_us, "commit_us": com_us,
         "round_us": win_us + com_us,
         "window_gbps": win_bytes / win_us / 1e3, "commit_gbps": com_bytes / com_us / 1e3,
         "round_gbps": (win_bytes + com_bytes) / (win_us + com_us) / 1e3,

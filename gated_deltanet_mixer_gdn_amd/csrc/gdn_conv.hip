@@ -13,6 +13,20 @@ namespace gdn {
 // token block 0 reads or writes the stored history; later blocks take their first
 // three history entries from qkv, so blocks never race on it.  persist = 0 leaves
 // the stored history as it was (a speculative window).
+// advance_history for channels c..c+3 that also leaves the new history in g
+__device__ __forceinline__ void advance_and_keep(ConvGroup& g, float* X, const float* xq, long long C, long long c,
+                                                 int nt) {
+    ConvGroup old;
+    old.load_history(X + c * kHist);
+    auto entry = [&](int k) -> f4 {
+        return k == 0 ? old.x3 : k == 1 ? old.x2 : k == 2 ? old.x1 : *(const f4*) (xq + (k - 3) * C + c);
+    };
+    g.x3 = entry(nt);
+    g.x2 = entry(nt + 1);
+    g.x1 = entry(nt + 2);
+    ConvGroup::store_history(X + c * kHist, g.x3, g.x2, g.x1);
+}
+
 __global__ __launch_bounds__(256) void conv_silu_norm_kernel(ConvParams p) {
     const int tid = threadIdx.x;
     const int head = blockIdx.y * 16 + (tid >> 4);
@@ -36,15 +50,17 @@ __global__ __launch_bounds__(256) void conv_silu_norm_kernel(ConvParams p) {
 
     ConvGroup ga, gb;
     float* X = p.conv + ((long long) (slot < 0 ? 0 : slot) * C) * kHist;
+    bool advanced = false;
     if (p.adv_qkv && tb == 0 && slot >= 0) {
         // the commit of the previous window comes first: its kept rows advance the
         // stored history (kept whatever this call's tokens do), and token 0 below
-        // starts from the advanced history (each thread rereads only what it wrote)
+        // starts from the advanced history, kept in registers
         const int na = read_ntok(p.n_adv, b, p.adv_T, p.flags, reporter);
         if (na > 0) {
             const float* xa = p.adv_qkv + (long long) b * p.adv_T * C;
-            advance_history(X, xa, C, ca, na);
-            advance_history(X, xa, C, cb, na);
+            advance_and_keep(ga, X, xa, C, ca, na);
+            advance_and_keep(gb, X, xa, C, cb, na);
+            advanced = true;
         }
     }
     f4 xa_n = {0.f, 0.f, 0.f, 0.f}, xb_n = xa_n;   // next token's inputs
@@ -52,8 +68,10 @@ __global__ __launch_bounds__(256) void conv_silu_norm_kernel(ConvParams p) {
         ga.load_taps(p.w, ca);
         gb.load_taps(p.w, cb);
         if (t0 == 0) {
-            ga.load_history(X + ca * kHist);
-            gb.load_history(X + cb * kHist);
+            if (!advanced) {
+                ga.load_history(X + ca * kHist);
+                gb.load_history(X + cb * kHist);
+            }
         } else {
             ga.x3 = *(const f4*) (xq + (t0 - 3) * C + ca);
             ga.x2 = *(const f4*) (xq + (t0 - 2) * C + ca);

@@ -150,3 +150,61 @@ def test_graph_replays_split_k_projection():
         torch.cuda.synchronize()
         assert torch.equal(out, ref), f"replay {r}: out differs"
         assert out.abs().max().item() > 0
+
+
+def test_graph_replays_commit_window():
+    """gdn_commit_window (the conv launch with the history advance, then the round
+    launch) captured once and replayed over several rounds: each replay commits a new
+    window (run eagerly on each pool, so both pools hold the same window h) with new
+    device-resident n_keep and window token counts, and is compared bit for bit with
+    the eager call on the second pool."""
+    import torch
+    import gated_deltanet_mixer_gdn_amd as G
+    B, T0, T1 = 4, 3, 5
+    wl = W.make("graph_round", B, T1, seed=144, n_slots=10, state_std=0.02, conv_std=1.0,
+                slot_choice="random")
+    g = wl.geom
+    eager, graph = GpuMixer(wl), GpuMixer(wl)
+    prev = [torch.zeros(B, T0, n, device="cuda") for n in (g.channels, g.channels, g.h_v, g.h_v)]
+    z0 = torch.zeros(B, T0, g.value_dim, device="cuda")
+    y0 = torch.empty(B, T0, g.value_dim, device="cuda")
+    n_keep = torch.zeros(B, dtype=torch.int32, device="cuda")
+    n_tok = torch.ones(B, dtype=torch.int32, device="cuda")
+    qkv, alpha, beta_logit, z = (torch.zeros(B, T1, n, device="cuda")
+                                 for n in (g.channels, g.h_v, g.h_v, g.value_dim))
+    h = torch.empty(B, T1, g.channels, device="cuda")
+    y = torch.empty(B, T1, g.value_dim, device="cuda")
+
+    def window0(gm):
+        G.gdn_verify_window(gm.pool, prev[0], gm.conv_w, prev[2], prev[3], gm.dt, gm.ssm_a, z0, gm.norm_w, wl.eps,
+                            prev[1], y0, gm.slots)
+
+    def step(gm, hh, yy):
+        G.gdn_commit_window(gm.pool, tuple(prev), n_keep, qkv, gm.conv_w, alpha, beta_logit, gm.dt, gm.ssm_a, z,
+                            gm.norm_w, wl.eps, hh, yy, gm.slots, n_tok)
+    step(graph, h, y)
+    _restore(graph, wl)
+    torch.cuda.synchronize()
+    cg = _capture(lambda: step(graph, h, y))
+    for r in range(REPLAYS):
+        w0 = W.make("graph_round_prev", B, T0, seed=170 + r, n_slots=10, ragged_max=T0)
+        w1 = W.make("graph_round_next", B, T1, seed=180 + r, n_slots=10, ragged_max=T1)
+        keep = np.random.default_rng(190 + r).integers(0, T0 + 1, B).astype(np.int32)
+        log(f"round replay {r}: n_keep {keep.tolist()} n_tok {w1.n_tok.tolist()}")
+        for t, a in zip(prev, (w0.qkv, None, w0.alpha, w0.beta_logit)):
+            if a is not None:
+                t.copy_(dev(a))
+        z0.copy_(dev(w0.z))
+        n_keep.copy_(dev(keep))
+        for t, a in zip((qkv, alpha, beta_logit, z, n_tok), (w1.qkv, w1.alpha, w1.beta_logit, w1.z, w1.n_tok)):
+            t.copy_(dev(a))
+        window0(graph)                    # h of the window being committed, from the graph pool
+        cg.replay()
+        window0(eager)                    # the same from the eager pool (same state, same bits)
+        h_e, y_e = torch.empty_like(h), torch.empty_like(y)
+        step(eager, h_e, y_e)
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_e), f"replay {r}: y differs"
+        assert torch.equal(h, h_e), f"replay {r}: h differs"
+        assert torch.equal(graph.pool.state, eager.pool.state), f"replay {r}: state differs"
+        assert torch.equal(graph.pool.conv, eager.pool.conv), f"replay {r}: conv history differs"
