@@ -567,6 +567,59 @@ def test_commit_window_equals_commit_then_window(T0, T1, ragged):
         assert_close("round y", y1.cpu().numpy(), ref, 2 * STEP_TOL)
 
 
+def test_speculative_round_b256_t4_full_size():
+    """The speculative round at the size the benchmark times (256 sequences, 768 MiB of
+    state, windows of 4 drafted tokens, n_keep ~ U{1..4} from the benchmark's seed):
+    gdn_verify_window, then gdn_commit_window with the next window.  The fused round
+    equals gdn_commit + gdn_verify_window bit for bit on the whole pool, and sampled
+    sequences match the oracle run over their kept tokens followed by the next window
+    (y of the next window; the committed state)."""
+    import torch
+    import gated_deltanet_mixer_gdn_amd as G
+    B, T = 256, 4
+    wl = W.make("round_b256", B, 2 * T, seed=31, state_std=0.02, conv_std=1.0)
+    g = wl.geom
+    n_keep = np.random.default_rng(32).integers(1, T + 1, B).astype(np.int32)
+    log(f"round b256 t4: {int(n_keep.sum())} kept")
+    fused, two = GpuMixer(wl), GpuMixer(wl)
+    part = lambda gm, a, lo: getattr(gm, a)[:, lo:lo + T].contiguous()
+    nk = dev(n_keep)
+    res = {}
+    for name, gm in (("fused", fused), ("two", two)):
+        h0 = torch.empty(B, T, g.channels, device="cuda")
+        y0 = torch.empty(B, T, g.value_dim, device="cuda")
+        G.gdn_verify_window(gm.pool, part(gm, "qkv", 0), gm.conv_w, part(gm, "alpha", 0), part(gm, "beta_logit", 0),
+                            gm.dt, gm.ssm_a, part(gm, "z", 0), gm.norm_w, wl.eps, h0, y0)
+        prev = (part(gm, "qkv", 0), h0, part(gm, "alpha", 0), part(gm, "beta_logit", 0))
+        h1 = torch.empty(B, T, g.channels, device="cuda")
+        y1 = torch.empty(B, T, g.value_dim, device="cuda")
+        nxt = [part(gm, a, T) for a in ("qkv", "alpha", "beta_logit", "z")]
+        if name == "fused":
+            G.gdn_commit_window(gm.pool, prev, nk, nxt[0], gm.conv_w, nxt[1], nxt[2], gm.dt, gm.ssm_a, nxt[3],
+                                gm.norm_w, wl.eps, h1, y1)
+        else:
+            G.gdn_commit(gm.pool, prev[0], h0, prev[2], prev[3], gm.dt, gm.ssm_a, nk)
+            G.gdn_verify_window(gm.pool, nxt[0], gm.conv_w, nxt[1], nxt[2], gm.dt, gm.ssm_a, nxt[3], gm.norm_w,
+                                wl.eps, h1, y1)
+        res[name] = (h1, y1)
+    torch.cuda.synchronize()
+    assert torch.equal(res["fused"][1], res["two"][1]) and torch.equal(res["fused"][0], res["two"][0])
+    assert torch.equal(fused.pool.state, two.pool.state) and torch.equal(fused.pool.conv, two.pool.conv)
+    assert int(fused.pool.flags.item()) == 0
+    y1 = res["fused"][1]
+    for b in (0, 97, 255):
+        k = int(n_keep[b])
+        idx = np.r_[0:k, T:2 * T]                     # the kept tokens, then the next window
+        slot = int(wl.slots[b])
+        ref = oracle.mixer(g, wl.qkv[b, idx], wl.conv_w, wl.alpha[b, idx], wl.beta_logit[b, idx], wl.dt, wl.ssm_a,
+                           wl.z[b, idx], wl.norm_w, wl.eps, wl.conv_state[slot], wl.state[slot])
+        assert_close(f"round y seq {b}", y1[b].cpu().numpy(), ref["y"][k:], 2 * STEP_TOL)
+        com = oracle.mixer(g, wl.qkv[b, :k], wl.conv_w, wl.alpha[b, :k], wl.beta_logit[b, :k], wl.dt, wl.ssm_a,
+                           wl.z[b, :k], wl.norm_w, wl.eps, wl.conv_state[slot], wl.state[slot])
+        assert_close(f"committed state seq {b}", fused.pool.state[slot].cpu().numpy(), com["state"], STEP_TOL)
+        assert_close(f"committed conv seq {b}", fused.pool.conv[slot].cpu().numpy(), com["conv_state"], STEP_TOL)
+
+
 # ------------------------------------------------------------------ alpha / beta projections
 @pytest.mark.parametrize("B,T,n_embd,h_v", [(1, 1, 2560, 48), (3, 1, 2560, 48), (256, 1, 2560, 48),
                                             (16, 512, 2560, 48), (5, 2, 260, 6), (2, 3, 4, 3)])
