@@ -5,11 +5,11 @@ namespace gdn {
 
 // ------------------------------------------------------------------ conv + SiLU + L2
 //
-// grid.x = B * n_tb (sequence, token block of kConvTokensPerBlock tokens),
+// grid.x = B * n_tb (sequence, token block of tpb tokens),
 // grid.y = ceil(n_heads / 16); 256 threads.  A 16-lane row (one DPP row) owns one
 // 128-channel head: lane l has the channel groups 4l..4l+3 and 64+4l..64+4l+3, so
 // every load and store instruction of the row covers 256 contiguous bytes and the
-// head's L2 norm is a 16-lane DPP sum.  Inputs are loaded one token ahead.  Only
+// head's L2 norm is a 16-lane DPP sum.  Inputs are loaded three tokens ahead.  Only
 // token block 0 reads or writes the stored history; later blocks take their first
 // three history entries from qkv, so blocks never race on it.  persist = 0 leaves
 // the stored history as it was (a speculative window).
@@ -37,8 +37,8 @@ __global__ __launch_bounds__(256) void conv_silu_norm_kernel(ConvParams p) {
     const long long C = (long long) p.n_heads * kS;
     const long long ca = (long long) head * kS + 4 * l;
     const long long cb = ca + 64;
-    const int t0 = tb * kConvTokensPerBlock;
-    const int t1 = min(t0 + kConvTokensPerBlock, p.T);
+    const int t0 = tb * p.tpb;
+    const int t1 = min(t0 + p.tpb, p.T);
     const float* xq = p.qkv + (long long) b * p.T * C;   // this sequence's qkv rows
     float* hq = p.h + (long long) b * p.T * C;
     const bool reporter = (tid == 0 && blockIdx.y == 0 && tb == 0);
@@ -63,7 +63,8 @@ __global__ __launch_bounds__(256) void conv_silu_norm_kernel(ConvParams p) {
             advanced = true;
         }
     }
-    f4 xa_n = {0.f, 0.f, 0.f, 0.f}, xb_n = xa_n;   // next token's inputs
+    // inputs of tokens t, t + 1 and t + 2, loaded ahead
+    f4 xa_1 = {0.f, 0.f, 0.f, 0.f}, xb_1 = xa_1, xa_2 = xa_1, xb_2 = xa_1, xa_3 = xa_1, xb_3 = xa_1;
     if (t_end > t0) {
         ga.load_taps(p.w, ca);
         gb.load_taps(p.w, cb);
@@ -80,17 +81,29 @@ __global__ __launch_bounds__(256) void conv_silu_norm_kernel(ConvParams p) {
             gb.x2 = *(const f4*) (xq + (t0 - 2) * C + cb);
             gb.x1 = *(const f4*) (xq + (t0 - 1) * C + cb);
         }
-        xa_n = *(const f4*) (xq + t0 * C + ca);
-        xb_n = *(const f4*) (xq + t0 * C + cb);
+        xa_1 = *(const f4*) (xq + t0 * C + ca);
+        xb_1 = *(const f4*) (xq + t0 * C + cb);
+        if (t0 + 1 < t_end) {
+            xa_2 = *(const f4*) (xq + (t0 + 1) * C + ca);
+            xb_2 = *(const f4*) (xq + (t0 + 1) * C + cb);
+        }
+        if (t0 + 2 < t_end) {
+            xa_3 = *(const f4*) (xq + (t0 + 2) * C + ca);
+            xb_3 = *(const f4*) (xq + (t0 + 2) * C + cb);
+        }
     }
 
     const bool normed = head < 2 * p.h_k;
     const float extra = head < p.h_k ? p.qscale : 1.0f;
     for (int t = t0; t < t_end; ++t) {
-        const f4 xa = xa_n, xb = xb_n;
-        if (t + 1 < t_end) {
-            xa_n = *(const f4*) (xq + (t + 1) * C + ca);
-            xb_n = *(const f4*) (xq + (t + 1) * C + cb);
+        const f4 xa = xa_1, xb = xb_1;
+        xa_1 = xa_2;
+        xb_1 = xb_2;
+        xa_2 = xa_3;
+        xb_2 = xb_3;
+        if (t + 3 < t_end) {
+            xa_3 = *(const f4*) (xq + (t + 3) * C + ca);
+            xb_3 = *(const f4*) (xq + (t + 3) * C + cb);
         }
         const f4 ua = ga.step(xa);
         const f4 ub = gb.step(xb);

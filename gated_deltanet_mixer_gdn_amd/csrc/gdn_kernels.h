@@ -16,7 +16,11 @@ constexpr int kDConv = 4;
 constexpr int kHist = kDConv - 1;
 // Tokens of one sequence handled by one conv workgroup (>= kHist, so only the
 // first token block of a sequence ever reads or writes the stored conv history).
+// Tokens per conv workgroup: 32, or fewer (down to 4) when a call has too few
+// (sequence, token block) pairs to fill the chip.  At least 3, so a later block takes
+// its whole history from qkv and never reads the stored one.
 constexpr int kConvTokensPerBlock = 32;
+constexpr int kConvMinTokensPerBlock = 4;
 // Rows (value heads x tokens) per gated-RMSNorm workgroup: one half-wave per row.
 constexpr int kNormRowsPerBlock = 8;
 
@@ -31,6 +35,7 @@ struct ConvParams {
     long long n_slots;
     int B, T, h_k, n_heads; // n_heads = 2*h_k + h_v (128-channel heads)
     int n_tb;               // token blocks per sequence
+    int tpb;                // tokens per block (kConvMinTokensPerBlock..kConvTokensPerBlock)
     int persist;            // 0: leave the stored history untouched (speculative window)
     float eps, qscale;
     // a commit first (else null): the stored history advances by the first n_adv[b] raw
