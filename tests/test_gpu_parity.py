@@ -158,8 +158,50 @@ def test_ragged_pool2048_b1024(fused):
     assert torch.equal(gm2.y[mask], gm.y[mask])
 
 
+def test_pool_beyond_2g_floats_top_slots():
+    """A pool of 2,800 slots (8.2 GiB of state: element offsets pass 2^31 from slot 2,731
+    on, byte offsets pass 2^32 from slot 1,366 on).  Sequences sit on the top slots and
+    on both sides of those boundaries; every call form must address them right and leave
+    the other slots bit-identical."""
+    import torch
+    import gated_deltanet_mixer_gdn_amd as G
+    n_big = 2800
+    g = W.Geom()
+    assert (n_big - 1) * g.h_v * g.s * g.s > 2 ** 31
+    log(f"big pool: {n_big} slots")
+    big = G.StatePool(n_big)
+    big.state.fill_(0.25)
+    big.conv.fill_(-0.5)
+    big.flags.zero_()
+    forms = [("3calls", 3, False, [2799, 2731, 2730, 1366]), ("fused_norm", 3, True, [2798, 2732, 1365, 0]),
+             ("one_launch", 1, "one", [2797, 2733, 2729, 1367])]
+    used = []
+    for k, (tag, T, fused, hi) in enumerate(forms):
+        wl = W.make("bigpool", len(hi), T, seed=62 + k, n_slots=len(hi), state_std=0.02, conv_std=1.0)
+        res = oracle.run_workload(wl)
+        hi_d = dev(np.array(hi, np.int32))
+        big.state[hi_d.long()] = dev(wl.state)
+        big.conv[hi_d.long()] = dev(wl.conv_state)
+        log(f"big pool {tag}: slots {hi}")
+        gm = GpuMixer(wl, pool=big)
+        gm.run(slots=hi_d, fused=fused)
+        torch.cuda.synchronize()
+        for key in ("o", "y", "h") if fused != "one" else ("y", "h"):
+            assert_close(f"big pool {tag} {key}", getattr(gm, key).cpu().numpy(), _stack(res, key), STEP_TOL)
+        assert_close(f"big pool {tag} state", big.state[hi_d.long()].cpu().numpy(), _stack(res, "state"), STEP_TOL)
+        assert_close(f"big pool {tag} conv", big.conv[hi_d.long()].cpu().numpy(), _stack(res, "conv_state"),
+                     STEP_TOL)
+        used += hi
+    assert int(big.flags.item()) == 0
+    # untouched slots, among them the neighbours of every slot used
+    probe = sorted({s + d for s in used for d in (-1, 1) if 0 <= s + d < n_big} - set(used))
+    p_d = dev(np.array(probe, np.int64))
+    assert bool((big.state[p_d] == 0.25).all()), "an untouched slot's state changed"
+    assert bool((big.conv[p_d] == -0.5).all()), "an untouched slot's conv history changed"
+
+
 # ------------------------------------------------------------------ properties and edges
-SMALL_GEOMS = [W.Geom(h_k=1, h_v=3), W.Geom(h_k=2, h_v=4), W.Geom(h_k=2, h_v=6)]
+SMALL_GEOMS =[W.Geom(h_k=1, h_v=3), W.Geom(h_k=2, h_v=4), W.Geom(h_k=2, h_v=6)]
 
 
 @pytest.mark.parametrize("geom", SMALL_GEOMS, ids=lambda g: f"hk{g.h_k}hv{g.h_v}")
