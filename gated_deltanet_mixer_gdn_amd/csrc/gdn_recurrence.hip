@@ -337,9 +337,12 @@ struct MultiLds {
 // of the inputs p describes (rows of h, alpha, beta_logit and z of sequence job.b, T
 // per sequence), the state in s[] (in and out).  Outputs of tokens nt..T-1 are written
 // as zero.  Every thread of the workgroup calls it.
+// keep_state = false: the caller discards s[] afterwards (a speculative window), so
+// the last token's state update is skipped; its outputs come from the old state in
+// the one-pass form, so they do not change.
 template <bool kNorm>
 __device__ __forceinline__ void multi_tokens(const StepParams& p, const HeadJob& job, int nt, f4 (&s)[16],
-                                             MultiLds& lds) {
+                                             MultiLds& lds, bool keep_state) {
     f4 (&qk_lds)[4][64] = lds.qk;
     f4 (&o_ring)[2][kNormChunk][32] = lds.o_ring;
 
@@ -446,6 +449,7 @@ __device__ __forceinline__ void multi_tokens(const StepParams& p, const HeadJob&
                 }
             }
         }
+        if (!keep_state && t + 1 == nt) break;   // uniform over the workgroup
         // re-read k from LDS rather than keeping 16 rows live across the reduction (the
         // fence stops the compiler from reusing the values loaded above)
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -469,7 +473,9 @@ __device__ __forceinline__ void multi_tokens(const StepParams& p, const HeadJob&
     }
 }
 
-template <bool kNorm>
+// kKeep: the state is stored at the end (p.persist); a speculative window (kKeep false,
+// always with the norm) stores nothing and skips its last token's update.
+template <bool kNorm, bool kKeep>
 __global__ __launch_bounds__(256) void decode_multi_kernel(StepParams p) {
     __shared__ MultiLds lds;
     const int tid = threadIdx.x;
@@ -500,8 +506,8 @@ __global__ __launch_bounds__(256) void decode_multi_kernel(StepParams p) {
                             head * kS + 4 * (tid & 31), nt);
         }
     }
-    multi_tokens<kNorm>(p, job, nt, s, lds);
-    if (nt > 0 && p.persist) store_tile(s, tile);
+    multi_tokens<kNorm>(p, job, nt, s, lds, kKeep);
+    if (nt > 0 && kKeep) store_tile(s, tile);
 }
 
 // A commit and the next speculative window in one launch, for a decode loop that
@@ -528,10 +534,10 @@ __global__ __launch_bounds__(256) void commit_window_kernel(StepParams com, Step
         load_tile(s, tile);
     }
     if (nk > 0) {
-        multi_tokens<false>(com, job, nk, s, lds);
+        multi_tokens<false>(com, job, nk, s, lds, true);
         store_tile(s, tile);
     }
-    multi_tokens<true>(win, job, job.nt, s, lds);
+    multi_tokens<true>(win, job, job.nt, s, lds, false);
 }
 
 // ------------------------------------------------------------------ launch
@@ -555,12 +561,14 @@ hipError_t launch_commit_window(const StepParams& com, const StepParams& win, hi
 hipError_t launch_decode_step(const StepParams& p, hipStream_t stream) {
     const dim3 grid((unsigned) ((long long) p.B * p.h_v));
     const bool one = p.T == 1 && !p.conv;   // the commit's history advance lives in the multi-token kernel
+    if (!p.y && !p.persist) return hipErrorInvalidValue;   // no caller leaves both out
     if (p.y) {
         if (one) hipLaunchKernelGGL((decode_one_kernel<true>), grid, dim3(256), 0, stream, p);
-        else hipLaunchKernelGGL((decode_multi_kernel<true>), grid, dim3(256), 0, stream, p);
+        else if (p.persist) hipLaunchKernelGGL((decode_multi_kernel<true, true>), grid, dim3(256), 0, stream, p);
+        else hipLaunchKernelGGL((decode_multi_kernel<true, false>), grid, dim3(256), 0, stream, p);
     } else {
         if (one) hipLaunchKernelGGL((decode_one_kernel<false>), grid, dim3(256), 0, stream, p);
-        else hipLaunchKernelGGL((decode_multi_kernel<false>), grid, dim3(256), 0, stream, p);
+        else hipLaunchKernelGGL((decode_multi_kernel<false, true>), grid, dim3(256), 0, stream, p);
     }
     return hipGetLastError();
 }
