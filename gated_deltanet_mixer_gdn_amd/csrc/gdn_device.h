@@ -208,9 +208,10 @@ struct ConvGroup {
     }
     // the stored history is [c][j]: 12 consecutive floats for channels c..c+3
     __device__ __forceinline__ void load_history(const float* X) {
-        const f4 a = *(const f4*) (X + 0);
-        const f4 m = *(const f4*) (X + 4);
-        const f4 z = *(const f4*) (X + 8);
+        set_history(*(const f4*) (X + 0), *(const f4*) (X + 4), *(const f4*) (X + 8));
+    }
+    // the history from its 12 stored floats (as three float4 loads)
+    __device__ __forceinline__ void set_history(f4 a, f4 m, f4 z) {
         x3 = f4{a.x, a.w, m.z, z.y};
         x2 = f4{a.y, m.x, m.w, z.z};
         x1 = f4{a.z, m.y, z.x, z.w};

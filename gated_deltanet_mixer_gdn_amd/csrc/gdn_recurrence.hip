@@ -165,26 +165,52 @@ __global__ __launch_bounds__(256) void decode_one_kernel(StepParams p) {
 // The conv prologue of the single-launch decode for (sequence b, qk head j): 16-lane
 // rows run the conv + SiLU + L2 norm exactly as conv_silu_norm_kernel does (row 0:
 // q_j, row 1: k_j, row 2+n: v of head g*j+n) into LDS and advance the conv history.
-// Threads tid >= 16 * (2 + g) do nothing.  slot >= 0.
-__device__ __forceinline__ void fused_conv_prologue(const FusedParams& p, int b, int j, int slot, int tid,
-                                                    f4* qk_lds, f4 (*v_lds)[32]) {
-    const int g = p.group;
-    const long long C = (long long) (2 * p.h_k + p.h_v) * kS;
+// Threads tid >= 16 * (2 + g) do nothing.  slot >= 0.  The loads (taps, history and
+// input of the thread's two channel groups) are a step of their own, so a kernel can
+// issue them ahead of its state tile and run the conv while the tile streams in.
+struct ConvPrologue {
+    ConvGroup ga, gb;   // taps loaded; the history is set in the finishing step
+    f4 ha[3], hb[3];    // the stored history as loaded (12 floats per channel group)
+    f4 xa, xb;
+};
+
+__device__ __forceinline__ long long prologue_channel(const FusedParams& p, int j, int tid) {
     const int crow = tid >> 4;
-    if (crow >= 2 + g) return;
+    const int hd = crow == 0 ? j : crow == 1 ? p.h_k + j : 2 * p.h_k + p.group * j + (crow - 2);
+    return (long long) hd * kS + 4 * (tid & 15);
+}
+
+// (the two steps below run only in threads tid < 16 * (2 + g); the caller checks)
+__device__ __forceinline__ void fused_conv_prologue_load(const FusedParams& p, int b, int j, int slot, int tid,
+                                                         ConvPrologue& cp) {
+    const long long C = (long long) (2 * p.h_k + p.h_v) * kS;
+    const long long ca = prologue_channel(p, j, tid);
+    const long long cb = ca + 64;
+    const float* X = p.conv + (long long) slot * C * kHist;
+    const float* xq = p.qkv + (long long) b * C;
+    cp.ga.load_taps(p.w, ca);
+    cp.gb.load_taps(p.w, cb);
+    for (int u = 0; u < 3; ++u) {
+        cp.ha[u] = *(const f4*) (X + ca * kHist + 4 * u);
+        cp.hb[u] = *(const f4*) (X + cb * kHist + 4 * u);
+    }
+    cp.xa = *(const f4*) (xq + ca);
+    cp.xb = *(const f4*) (xq + cb);
+}
+
+__device__ __forceinline__ void fused_conv_prologue_finish(const FusedParams& p, int b, int j, int slot, int tid,
+                                                           ConvPrologue& cp, f4* qk_lds, f4 (*v_lds)[32],
+                                                           bool store = true) {
+    const int crow = tid >> 4;
     const int cl = tid & 15;
-    const int hd = crow == 0 ? j : crow == 1 ? p.h_k + j : 2 * p.h_k + g * j + (crow - 2);
-    const long long ca = (long long) hd * kS + 4 * cl;
+    const long long C = (long long) (2 * p.h_k + p.h_v) * kS;
+    const long long ca = prologue_channel(p, j, tid);
     const long long cb = ca + 64;
     float* X = p.conv + (long long) slot * C * kHist;
-    const float* xq = p.qkv + (long long) b * C;
-    ConvGroup ga, gb;
-    ga.load_taps(p.w, ca);
-    gb.load_taps(p.w, cb);
-    ga.load_history(X + ca * kHist);
-    gb.load_history(X + cb * kHist);
-    const f4 ua = ga.step(*(const f4*) (xq + ca));
-    const f4 ub = gb.step(*(const f4*) (xq + cb));
+    cp.ga.set_history(cp.ha[0], cp.ha[1], cp.ha[2]);
+    cp.gb.set_history(cp.hb[0], cp.hb[1], cp.hb[2]);
+    const f4 ua = cp.ga.step(cp.xa);
+    const f4 ub = cp.gb.step(cp.xb);
     f4 ha = ua * sigmoid4(ua);
     f4 hb = ub * sigmoid4(ub);
     if (crow < 2) {
@@ -193,8 +219,9 @@ __device__ __forceinline__ void fused_conv_prologue(const FusedParams& p, int b,
         ha *= sc;
         hb *= sc;
     }
-    ConvGroup::store_history(X + ca * kHist, ga.x3, ga.x2, ga.x1);
-    ConvGroup::store_history(X + cb * kHist, gb.x3, gb.x2, gb.x1);
+    if (!store) return;
+    ConvGroup::store_history(X + ca * kHist, cp.ga.x3, cp.ga.x2, cp.ga.x1);
+    ConvGroup::store_history(X + cb * kHist, cp.gb.x3, cp.gb.x2, cp.gb.x1);
     if (p.h) {
         *(f4*) (p.h + (long long) b * C + ca) = ha;
         *(f4*) (p.h + (long long) b * C + cb) = hb;
@@ -202,6 +229,14 @@ __device__ __forceinline__ void fused_conv_prologue(const FusedParams& p, int b,
     f4* dst = crow < 2 ? qk_lds + 32 * crow : v_lds[crow - 2];
     dst[cl] = ha;
     dst[16 + cl] = hb;
+}
+
+__device__ __forceinline__ void fused_conv_prologue(const FusedParams& p, int b, int j, int slot, int tid,
+                                                    f4* qk_lds, f4 (*v_lds)[32]) {
+    if ((tid >> 4) >= 2 + p.group) return;
+    ConvPrologue cp;
+    fused_conv_prologue_load(p, b, j, slot, tid, cp);
+    fused_conv_prologue_finish(p, b, j, slot, tid, cp, qk_lds, v_lds);
 }
 
 // Outputs of the single-launch decode for a sequence with an unknown slot: y (and its
@@ -249,20 +284,34 @@ __global__ __launch_bounds__(256 * G) void decode_fused_par_kernel(FusedParams p
     if ((nwg & 7u) == 0) wid = (wid & 7u) * (nwg >> 3) + (wid >> 3);
     const int b = (int) (wid / (unsigned) p.h_k);
     const int j = (int) (wid - (unsigned) b * (unsigned) p.h_k);
-    const int slot = read_slot(p.slots, b, p.n_slots, p.flags, tid == 0 && j == 0);
+    // the same in every lane; said so, the branches below are per wave
+    const int slot = __builtin_amdgcn_readfirstlane(read_slot(p.slots, b, p.n_slots, p.flags, tid == 0 && j == 0));
     if (slot < 0) {
         fused_zero_outputs(p, b, j, tid, 256 * G);
         return;
     }
     const int i = G * j + n;
     float* tile = p.state + ((long long) slot * p.h_v + i) * (kS * kS) + (rg * 16) * kS + cg * 4;
+    // The waves that run the conv (16-lane rows, 2 + G of them) load its inputs first,
+    // then their tile rows, and run the conv while the tiles stream in.  The branch is
+    // per wave, so no lane waits on another lane's loads; rows past 2 + G load row
+    // 0's inputs and store nothing.
+    constexpr int kConvWaves = (16 * (2 + G) + 63) / 64;
     f4 s[16];
-    load_tile(s, tile);
-    fused_conv_prologue(p, b, j, slot, tid, qk_lds, v_lds);
-    __syncthreads();
+    if (__builtin_amdgcn_readfirstlane(tid >> 6) < kConvWaves) {
+        const int ctid = (tid >> 4) < 2 + G ? tid : (tid & 15);
+        ConvPrologue cp;
+        fused_conv_prologue_load(p, b, j, slot, ctid, cp);
+        load_tile(s, tile);
+        fused_conv_prologue_finish(p, b, j, slot, ctid, cp, qk_lds, v_lds, (tid >> 4) < 2 + G);
+    } else {
+        load_tile(s, tile);
+    }
     const long long e = (long long) b * p.h_v + i;
-    const float beta = sigmoid_f(p.beta_logit[e]);
-    const float eg = expf(softplus_f(p.alpha[e] + p.dt[i]) * p.ssm_a[i]);
+    const float beta_l = p.beta_logit[e], alpha = p.alpha[e], dt = p.dt[i], a = p.ssm_a[i];
+    __syncthreads();
+    const float beta = sigmoid_f(beta_l);
+    const float eg = expf(softplus_f(alpha + dt) * a);
     head_token_256<true>(s, qk_lds, v_lds[n][cg], beta, eg, red[n], nullptr, p.z + e * kS, p.norm_w,
                          p.y ? p.y + e * kS : nullptr, SplitOut{p.ys, b, p.ys_chunks, i}, p.eps, p.oscale,
                          p.gate_silu, lt);
