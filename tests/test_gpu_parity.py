@@ -117,6 +117,32 @@ def test_prefill_b16_t512_state_on_chip(fused):
     _compare_all(gm, wl, res, LONG_TOL, "prefill_b16_t512")
 
 
+def test_512_sequential_single_launch_decodes():
+    """512 decode tokens as 512 calls of the single-launch decode (the benchmark's step),
+    from a filled state, against the oracle for every token's y and the final state and
+    conv history (the 512-step bound), and bit for bit against the same 512 tokens as
+    one multi-token call of the two-launch form."""
+    import torch
+    T = 512
+    wl = W.make("seq512", 4, T, seed=71, n_slots=6, state_std=0.02, conv_std=1.0, slot_choice="random")
+    log("512 sequential single-launch decodes: oracle")
+    res = oracle.run_workload(wl)
+    one = GpuMixer(wl)
+    for t in range(T):
+        one.run(t, t + 1, fused="one")
+    torch.cuda.synchronize()
+    log("512 sequential single-launch decodes: compare")
+    _compare_all(one, wl, res, LONG_TOL, "seq512", keys=("y", "h"))
+    first = assert_close("seq512 y[t=0]", one.y[:, 0].cpu().numpy(), _stack(res, "y")[:, 0], STEP_TOL)
+    log(f"seq512: first-token y rel error {first:.2e}")
+    multi = GpuMixer(wl)
+    multi.run(fused=True)
+    assert torch.equal(one.pool.state, multi.pool.state)
+    assert torch.equal(one.pool.conv, multi.pool.conv)
+    assert torch.equal(one.y, multi.y) and torch.equal(one.h, multi.h)
+    assert int(one.pool.flags.item()) == 0
+
+
 @FUSED
 def test_ragged_pool2048_b1024(fused):
     """2048-slot pool, 1024 sequences at random unique slots, U{1..8} tokens each, one call
