@@ -312,6 +312,49 @@ def layer_decode(G, batches, reps: int = 50):
         del pool
 
 
+def small_batches(G, batches, reps: int = 200):
+    """One decode token at each batch size, in the single launch and in the two launches
+    (conv, then the recurrence with the fused norm), each call repeated `reps` times
+    back to back.  Seeded random inputs of the decode shapes.  At small batches an eager
+    call costs more host time than kernel time, so the per-call event figure printed
+    here is host-bound; the kernel durations come from a rocprofv3 kernel trace of
+    this run, grouped by grid size."""
+    import torch
+    geom = G.Geom()
+    C, hv, vd = geom.channels, geom.h_v, geom.h_v * geom.s
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(31)
+    rnd = lambda *shape, std=1.0: torch.randn(*shape, generator=gen, device="cuda") * std
+    conv_w, dt, norm_w = rnd(C, geom.d_conv, std=0.5), rnd(hv, std=0.5), 1.0 + rnd(geom.s, std=0.1)
+    ssm_a = -torch.exp(torch.rand(hv, generator=gen, device="cuda") * 2.0 - 1.0)
+    for B in batches:
+        pool = G.StatePool(B, geom)
+        pool.state.copy_(rnd(*pool.state.shape, std=0.02))
+        pool.conv.copy_(rnd(*pool.conv.shape))
+        pool.flags.zero_()
+        qkv, alpha, bl, z = rnd(B, 1, C), rnd(B, 1, hv), rnd(B, 1, hv), rnd(B, 1, vd)
+        h, y = torch.empty(B, 1, C, device="cuda"), torch.empty(B, 1, vd, device="cuda")
+        forms = {
+            "single_launch": lambda: G.gdn_decode_fused(pool, qkv[:, 0], conv_w, alpha[:, 0], bl[:, 0], dt, ssm_a,
+                                                        z[:, 0], norm_w, 1e-6, y[:, 0]),
+            "two_launches": lambda: G.gdn_mixer(pool, qkv, alpha, bl, z, conv_w, dt, ssm_a, norm_w, 1e-6, h, None, y,
+                                                fused=True),
+        }
+        out = {"B": B}
+        for name, fn in forms.items():
+            fn()
+            torch.cuda.synchronize()
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            ev[0].record()
+            for _ in range(reps):
+                fn()
+            ev[1].record()
+            torch.cuda.synchronize()
+            out[f"{name}_us_per_call_eager"] = ev[0].elapsed_time(ev[1]) / reps * 1000.0
+        print(json.dumps({"small_batch_decode": out}), flush=True)
+        del pool
+
+
 def verify_round(G, W, B: int, T: int, reps: int = 20):
     """One speculative round at batch B: gdn_verify_window over T drafted tokens from the
     untouched pool (writes h and y, persists nothing), then gdn_commit of n_keep ~
@@ -394,6 +437,9 @@ def main():
     ap.add_argument("--verify", default="",
                     help="B,T: time one speculative round (verify window of T tokens + commit) "
                          "instead of the step")
+    ap.add_argument("--batches", default="",
+                    help="comma-separated batch sizes: one decode token per sequence in the single "
+                         "launch and the two launches, for kernel traces, instead of the step")
     ap.add_argument("--event-every", type=int, default=8,
                     help="record per-kernel HIP events on every N-th timed step")
     args = ap.parse_args()
@@ -422,6 +468,9 @@ def main():
         return
     if args.layer:
         layer_decode(G, [int(v) for v in args.layer.split(",")])
+        return
+    if args.batches:
+        small_batches(G, [int(v) for v in args.batches.split(",")])
         return
     if args.verify:
         vb, vt = (int(v) for v in args.verify.split(","))
