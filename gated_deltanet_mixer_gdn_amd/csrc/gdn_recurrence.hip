@@ -36,8 +36,18 @@ __device__ __forceinline__ HeadJob head_job(const StepParams& p, bool report) {
 struct HeadReduce {
     f4 k[4][32];
     f4 q[4][32];
-    float kq[4];
 };
+
+// k . q over the 128 rows, the same in every lane of a full wave: lane l multiplies
+// rows 2l and 2l+1, then the 64 lane sums are added pairwise across the wave.  Every
+// recurrence kernel forms it this way, so they agree bit for bit.  qk: q as 128
+// floats, then k as 128 floats.
+__device__ __forceinline__ float wave_kq(const float* qk, int lane) {
+    const float2 q2 = ((const float2*) qk)[lane];
+    const float2 k2 = ((const float2*) (qk + kS))[lane];
+    const float part = __builtin_fmaf(k2.y, q2.y, k2.x * q2.x);
+    return add_xor32(add_xor16(add_xor8(block8_sum(part))));
+}
 
 // One token of one head for a group of 256 threads (tid = the thread's index in the
 // group; a larger workgroup runs one such group per head) whose thread tid holds columns
@@ -63,30 +73,24 @@ __device__ __forceinline__ void head_token_256(f4 (&s)[16], const f4* qk, f4 v, 
     const float* qrow = (const float*) qk + rg * 16;
     const float* krow = (const float*) qk + kS + rg * 16;
     f4 pk = {0.f, 0.f, 0.f, 0.f}, pq = pk;
-    float kq = 0.f;
 #pragma unroll
     for (int m = 0; m < 16; ++m) {
-        const float kk = krow[m];
-        const float qq = qrow[m];
-        pk = fma4(s[m], kk, pk);
-        pq = fma4(s[m], qq, pq);
-        kq = __builtin_fmaf(kk, qq, kq);
+        pk = fma4(s[m], krow[m], pk);
+        pq = fma4(s[m], qrow[m], pq);
     }
+    const float KQ = wave_kq((const float*) qk, tid & 63);
     // fold the two row groups of this wave (lanes l and l^32)
     pk = add_xor32(pk);
     pq = add_xor32(pq);
-    kq = add_xor32(kq);
     if ((tid & 32) == 0) {
         red.k[wave][cg] = pk;
         red.q[wave][cg] = pq;
-        if (cg == 0) red.kq[wave] = kq;
     }
     __syncthreads();
 
     // the 8 row groups summed as ((g0+g1)+(g2+g3))+((g4+g5)+(g6+g7))
     const f4 PK = (red.k[0][cg] + red.k[1][cg]) + (red.k[2][cg] + red.k[3][cg]);
     const f4 PQ = (red.q[0][cg] + red.q[1][cg]) + (red.q[2][cg] + red.q[3][cg]);
-    const float KQ = (red.kq[0] + red.kq[1]) + (red.kq[2] + red.kq[3]);
     const f4 d = beta * fma4(-eg, PK, v);
     if (rg == 0) {
         f4 out = fma4(KQ, d, eg * PQ);
@@ -459,18 +463,14 @@ __device__ __forceinline__ void multi_tokens(const StepParams& p, const HeadJob&
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
         f4 pk = {0.f, 0.f, 0.f, 0.f}, pq = pk;
-        float kq = 0.f;
 #pragma unroll
         for (int m = 0; m < 16; ++m) {
-            const float kk = krow[m];
-            const float qq = qrow[m];
-            pk = fma4(s[m], kk, pk);
-            pq = fma4(s[m], qq, pq);
-            kq = __builtin_fmaf(kk, qq, kq);
+            pk = fma4(s[m], krow[m], pk);
+            pq = fma4(s[m], qrow[m], pq);
         }
-        // sum over the 8 row groups of the wave (lane bits 3..5):
+        const float kq = wave_kq((const float*) buf, lane);
+        // column sums over the 8 row groups of the wave (lane bits 3..5):
         // ((g0+g1)+(g2+g3))+((g4+g5)+(g6+g7)), as in the single-token kernel
-        kq = add_xor32(add_xor16(add_xor8(kq)));
         const float pkc = scatter_sum4(add_xor8(pk));
         const float pqc = scatter_sum4(add_xor8(pq));
         // delta of column col + oc, then of all 4 columns for the update
