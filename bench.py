@@ -16,8 +16,8 @@ two-launch form.  Prints ONE JSON line on stdout; diagnostics go to stderr.
 The `roofline` object is for the dominant kernel of the timed step
 (decode_fused_par_kernel<3> for the default workload): its algorithmic bytes per
 launch over its average launch time, measured with HIP events recorded on the
-stream the kernels run on, around the kernels of every 8th step of the timed
-region.  `traffic` (HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE
+stream the kernels run on: one pair around all timed launches when the step is that
+one kernel, else around the kernels of every 8th step of the timed region.  `traffic` (HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE
 counters, scaled by a copy-kernel calibration) is read from
 profiles/decode_fused_b256_traffic.txt and reported only while the kernel sources
 it was measured on are unchanged.
@@ -535,20 +535,29 @@ def main():
         for _ in range(args.warmup):
             fn()
         # The timed region: K steps between two synchronisations, wall clock around it.
-        # HIP events on the launch stream bracket every kernel of every `every`-th step
-        # of this same region (an event record costs a few microseconds, so recording
-        # them on every step would inflate the step time it is meant to explain).
+        # A step of one kernel: one pair of HIP events on the launch stream around all K
+        # launches, so the kernel's average duration is the span over K (any gap between
+        # the queued launches counts against it).  A step of several kernels: events
+        # bracket every kernel of every `every`-th step of the same region (an event
+        # record costs a few microseconds, so recording them on every step would
+        # inflate the step time it is meant to explain).
+        single_kernel = len(names) == 1
         every = max(1, args.event_every)
-        sampled = range(0, args.steps, every)
+        sampled = [] if single_kernel else range(0, args.steps, every)
         evs = {k: [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for k in sampled}
+        span = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
         torch.cuda.synchronize()
         t0 = time.perf_counter()
+        span[0].record(stream)
         for k in range(args.steps):
             fn(evs.get(k))
+        span[1].record(stream)
         # the steps are queued and the GPU is still running them: sample its clocks
         clocks[fn.__name__] = gpu_clocks(card)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
+        if single_kernel:
+            return wall * 1000.0 / args.steps, {names[0]: span[0].elapsed_time(span[1]) / args.steps}, args.steps
         k_ms = {name: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs.values()]))
                 for i, name in enumerate(names)}
         return wall * 1000.0 / args.steps, k_ms, len(evs)
@@ -674,7 +683,9 @@ def main():
                      "algorithmic_bytes_per_launch": nbytes[dominant],
                      "algorithmic_flops_per_launch": flops,
                      "hbm_gbps": achieved,
-                     "event_samples": n_samples},
+                     "event_samples": n_samples,
+                     "event_timing": ("one event pair around all timed launches" if single else
+                                      "events around the kernels of every sampled step")},
         "gpu_clocks_during_timing": clocks.get("step_one" if single else "step_fused"),
         "cpu_baseline": cpu,
     }
