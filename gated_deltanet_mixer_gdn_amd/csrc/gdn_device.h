@@ -42,8 +42,16 @@ __device__ __forceinline__ float sigmoid_f(float x) { return 1.0f / (1.0f + expf
 // softplus in fp32: above 20 the log1p term is below half an ulp of x
 __device__ __forceinline__ float softplus_f(float x) { return x > 20.0f ? x : log1pf(expf(x)); }
 
+// The sigmoid of SiLU and of the output gate, per channel: e^-x as 2^(-x log2 e) on the
+// hardware exp2 and 1 / (1 + e^-x) on the hardware reciprocal (about 1 ulp each, the
+// rounding of -x log2 e adding |x| 2^-24 relative), four instructions where the
+// correctly rounded exp and division take about twenty.  Every kernel uses this one,
+// so the kernels still agree with one another bit for bit.
+__device__ __forceinline__ float sigmoid_hw(float x) {
+    return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(x * -1.44269504088896341f));
+}
 __device__ __forceinline__ f4 sigmoid4(f4 x) {
-    return f4{sigmoid_f(x.x), sigmoid_f(x.y), sigmoid_f(x.z), sigmoid_f(x.w)};
+    return f4{sigmoid_hw(x.x), sigmoid_hw(x.y), sigmoid_hw(x.z), sigmoid_hw(x.w)};
 }
 
 // output gate of the gated RMSNorm: sigmoid(z), or z * sigmoid(z) (SiLU, the earlier
