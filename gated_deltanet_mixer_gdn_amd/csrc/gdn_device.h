@@ -69,9 +69,10 @@ __device__ __forceinline__ f4 fma4(f4 a, f4 b, f4 c) {
 }
 __device__ __forceinline__ f4 fma4(f4 a, float b, f4 c) { return fma4(a, f4{b, b, b, b}, c); }
 __device__ __forceinline__ f4 fma4(float a, f4 b, f4 c) { return fma4(f4{a, a, a, a}, b, c); }
-// 1 / sqrt(mean of squares + eps) for a 128-wide row from its sum of squares
+// 1 / sqrt(mean of squares + eps) for a 128-wide row from its sum of squares, on the
+// hardware reciprocal square root (about 1 ulp; one function for every kernel)
 __device__ __forceinline__ float rms_inv(float sum_sq, float eps) {
-    return 1.0f / sqrtf(__builtin_fmaf(sum_sq, 1.0f / kS, eps));
+    return __builtin_amdgcn_rsqf(__builtin_fmaf(sum_sq, 1.0f / kS, eps));
 }
 __device__ __forceinline__ float sumsq4(f4 x) {
     return __builtin_fmaf(x.w, x.w, __builtin_fmaf(x.z, x.z, __builtin_fmaf(x.y, x.y, x.x * x.x)));

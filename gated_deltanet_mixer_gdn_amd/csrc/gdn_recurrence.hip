@@ -421,11 +421,12 @@ __device__ __forceinline__ void multi_tokens(const StepParams& p, const HeadJob&
     const float a_i = p.ssm_a[i];
 
     // q|k and v of the next token, loaded one token ahead
-    f4 qk_n = {0.f, 0.f, 0.f, 0.f}, v_n = qk_n;
+    f4 qk_n = {0.f, 0.f, 0.f, 0.f};
+    float v_n = 0.f;   // v of the one column (col + oc) whose delta this lane forms
     auto fetch = [&](int t) {
         const float* ht = p.h + (tok0 + t) * C;
         qk_n = *(const f4*) (ht + q_off);
-        v_n = *(const f4*) (ht + v_off);
+        v_n = ht[v_off + oc];
     };
     // beta and the decay e^g are the same for the whole head: lane l evaluates them for
     // token t0 + l of a 64-token window, and each token reads its pair with readlane
@@ -455,7 +456,7 @@ __device__ __forceinline__ void multi_tokens(const StepParams& p, const HeadJob&
         const float beta = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(beta_w), t & 63));
         const float eg = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(eg_w), t & 63));
         buf[lane] = qk_n;
-        const f4 v = v_n;
+        const float vc = v_n;
         if (t + 1 < nt) fetch(t + 1);
         // the staging above is wave-private: order it against this wave's reads
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -474,7 +475,6 @@ __device__ __forceinline__ void multi_tokens(const StepParams& p, const HeadJob&
         const float pkc = scatter_sum4(add_xor8(pk));
         const float pqc = scatter_sum4(add_xor8(pq));
         // delta of column col + oc, then of all 4 columns for the update
-        const float vc = oc == 0 ? v.x : oc == 1 ? v.y : oc == 2 ? v.z : v.w;
         const float dc = beta * __builtin_fmaf(-eg, pkc, vc);
         const f4 d = gather4(dc);
         // the readout of column col + oc (a scale of 1 multiplies exactly)
