@@ -246,8 +246,8 @@ int gdn_gated_rmsnorm(const float* o, const float* z, const float* w, float eps,
                       int32_t s, int32_t gate_silu, float* y, void* stream);
 
 /* ---------------------------------------------------------------- the step before the mixer
- * The alpha / beta projections of step 5 of gdn_layer ("The weights are BF16";
- * the native path consumes F32 activations): for every row r of x (one token),
+ * The alpha / beta projections of step 5 of gdn_layer (bf16 weights; the native
+ * path there reads fp32 activations): for every row r of x (one token),
  *   alpha[r][i]      = sum_e w_alpha[i][e] * x[r][e]
  *   beta_logit[r][i] = sum_e w_beta[i][e]  * x[r][e]
  * x [rows][n_embd] fp32 (16-byte aligned, n_embd a multiple of 4);

@@ -6,15 +6,21 @@
  * benchmark's CPU-baseline leg, and by nothing else.  It shares no code, header,
  * table or constant with the HIP library.
  *
- * What it computes is the op order written on the "include/strata/core/layer.hpp"
- * page (the docstring of the GDN layer, which states the order of the reference
- * specification) and the inline steps of `gdn_layer` on the "src/core/layer.cpp"
- * page:
+ * What it computes follows the operation order of the GDN layer docstring on the
+ * "include/strata/core/layer.hpp" page and the numbered steps of `gdn_layer` on the
+ * "src/core/layer.cpp" page (steps 3 to 7):
  *
- *   conv -> SiLU on the WHOLE conv output -> l2_norm on q and k only (v is not
- *   normalised) -> q scaled by 1/sqrt(S) after the norm -> beta = sigmoid(.) ->
- *   gate = softplus(alpha + dt) * ssm_a -> recurrent step ->
- *   y = rms_norm(o, ssm_norm) * sigmoid(z)   (sigmoid, not SiLU)
+ *   1. causal depthwise conv of the raw qkv row with the stored history;
+ *   2. SiLU applied to every one of the C conv outputs, before q, k and v are
+ *      taken apart;
+ *   3. an L2 norm of each q head and each k head (the v heads keep their
+ *      values), and then the extra factor 1/sqrt(S) on q;
+ *   4. beta from the sigmoid of its logit, the gate from softplus(alpha + dt)
+ *      times ssm_a;
+ *   5. the recurrent step on each value head's state;
+ *   6. the output: o divided by its root mean square, times the norm weight,
+ *      times the logistic sigmoid of z (the plain sigmoid here; SiLU belongs to
+ *      the earlier model, see the option below).
  *
  * Two variants the pages name are options of the functions below: an output gate
  * z * sigmoid(z) (SiLU), which the docstring on the layer.hpp page gives for an
@@ -70,9 +76,10 @@ double gdn_oracle_sigmoid(double x) { return sigmoid(x); }
 double gdn_oracle_softplus(double x) { return softplus(x); }
 
 /*
- * Step 3 of gdn_layer ("conv, then SiLU on the WHOLE conv output") and step 4
- * ("q,k = l2_norm; v is NOT normalised", then the 1/sqrt(S) scale on q after the
- * norm), for ONE sequence over T consecutive tokens.
+ * Steps 3 and 4 of gdn_layer (src/core/layer.cpp page) for ONE sequence over T
+ * consecutive tokens: the conv with its SiLU over all C channels (step 3), then the
+ * L2 norm of the q and k heads only, with the 1/sqrt(S) factor put on q once it is
+ * normalised (step 4).
  *
  *   qkv        [T][C]          raw projections, C = 2*h_k*s + h_v*s
  *   conv_w     [C][d_conv]
@@ -259,8 +266,8 @@ int gdn_oracle_mixer(int h_k, int h_v, int s, int d_conv, int T,
 
 /*
  * The step before the mixer: the alpha and beta projections of step 5 of gdn_layer
- * ("beta and the gate. The weights are BF16"; the native path consumes F32
- * activations).  For every row r of x:
+ * (src/core/layer.cpp page), whose weights are stored as bf16 while the native path
+ * reads fp32 activations.  For every row r of x:
  *   alpha[r][i]      = sum_e w_alpha[i][e] * x[r][e]
  *   beta_logit[r][i] = sum_e w_beta[i][e]  * x[r][e]
  * The weights are bf16 bit patterns: a bf16 value is the upper half of an IEEE
