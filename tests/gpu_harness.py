@@ -6,6 +6,8 @@ import sys
 
 import numpy as np
 
+from parity import assert_close, assert_exact, assert_tokens, tol  # noqa: F401  (the tests import them from here too)
+
 
 def log(msg: str):
     print(msg, flush=True)
@@ -15,18 +17,6 @@ def log(msg: str):
 def dev(a):
     import torch
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
-
-
-def assert_close(name: str, gpu, ref, rel: float):
-    """max |gpu - ref| <= rel * max |ref|, on the whole array."""
-    g = np.asarray(gpu, dtype=np.float64)
-    r = np.asarray(ref, dtype=np.float64)
-    assert g.shape == r.shape, f"{name}: shape {g.shape} vs {r.shape}"
-    assert np.isfinite(g).all(), f"{name}: non-finite values from the GPU"
-    m = float(np.abs(r).max()) if r.size else 0.0
-    err = float(np.abs(g - r).max()) if r.size else 0.0
-    assert err <= rel * m, f"{name}: max abs err {err:.3e} > {rel:g} x max|ref| ({m:.3e})"
-    return err / m if m else 0.0
 
 
 class GpuMixer:

@@ -1,21 +1,20 @@
 """Parity of the HIP path (through the C ABI) with the fp64 oracle on MI355X.
 
-Every workload is seeded and synthetic. Tolerances: max |gpu - ref| <= 1e-4 x
-max |ref| per decode step for o, y, h, state and conv state; <= 1e-3 x max |ref|
-after 512 sequential steps. Integer / placement results (untouched slots, skipped
-tokens, flags) are compared bit for bit.
+Every workload is seeded and synthetic. Every comparison uses the one bound of
+tests/parity.py: tol(n) = 1e-4 + 9e-4 (n - 1) / 511 times max |ref| for a value n
+sequential steps from the seeded inputs (o and y of token t: n = t + 1; a state after
+n_b tokens: n = n_b; h: n = 1), so 1e-4 per decode step and 1e-3 after 512 steps.
+The conv history (raw inputs, only moved), integer and placement results (untouched
+slots, skipped tokens, flags) are compared bit for bit.
 """
 import numpy as np
 import pytest
 
 import gdn_workloads as W
 import oracle
-from gpu_harness import GpuMixer, assert_close, dev, log
+from gpu_harness import GpuMixer, assert_close, assert_exact, assert_tokens, dev, log, tol
 
 pytestmark = pytest.mark.gpu
-
-STEP_TOL = 1e-4
-LONG_TOL = 1e-3
 
 _ORACLE = {}
 
@@ -36,29 +35,23 @@ def _stack(results, key, n=None):
     return np.stack([r[key] if n is None else r[key][:n] for r in results])
 
 
-def _compare_all(gm, wl, res, tol, tag, keys=("o", "y", "h")):
-    """Compare o, y, h for every valid token and the final state / conv of every slot."""
-    o = gm.o.cpu().numpy()
-    y = gm.y.cpu().numpy()
-    h = gm.h.cpu().numpy()
+def _compare_all(gm, wl, res, tag, keys=("o", "y", "h"), first_step=1):
+    """o and y of every valid token at tol(first_step + t) per token index t, h at tol(1)
+    at every token (first_step - 1 steps ran before this call), the final state of every
+    slot at tol(first_step - 1 + the most tokens a sequence took), the conv history bit
+    for bit.  Outputs of skipped tokens must be zero."""
+    counts = [wl.tokens_of(b) for b in range(wl.B)]
+    errs = {}
+    for key in keys:
+        arr = getattr(gm, key).cpu().numpy()
+        errs[key] = assert_tokens(f"{tag} {key}", arr, [r[key] for r in res], counts, first_step,
+                                  recurrent=key != "h")[0]
     st = gm.pool.state.cpu().numpy()
     cv = gm.pool.conv.cpu().numpy()
-    errs = {}
-    for key, arr in (("o", o), ("y", y), ("h", h)):
-        if key not in keys:
-            continue
-        g_parts, r_parts = [], []
-        for b in range(wl.B):
-            n = wl.tokens_of(b)
-            g_parts.append(arr[b, :n].reshape(-1))
-            r_parts.append(res[b][key].reshape(-1))
-            if n < wl.T:
-                assert (arr[b, n:] == 0).all(), f"{tag}: {key} of skipped tokens is not zero"
-        errs[key] = assert_close(f"{tag} {key}", np.concatenate(g_parts), np.concatenate(r_parts), tol)
     sl = wl.slots
-    errs["state"] = assert_close(f"{tag} state", st[sl], _stack(res, "state"), tol)
-    errs["conv"] = assert_close(f"{tag} conv", cv[sl], _stack(res, "conv_state"), tol)
-    log(f"{tag}: rel errors " + ", ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    errs["state"] = assert_close(f"{tag} state", st[sl], _stack(res, "state"), max(1, first_step - 1 + max(counts)))
+    assert_exact(f"{tag} conv", cv[sl], _stack(res, "conv_state"))
+    log(f"{tag}: rel errors " + ", ".join(f"{k}={v:.2e}" for k, v in errs.items()) + ", conv exact")
     return st, cv
 
 
@@ -74,12 +67,13 @@ def test_tiny_b1_t8_every_step(fused):
         h, o, y = gm.run(t, t + 1, fused=fused)
         r = oracle.run_sequence(wl, 0, t, t + 1, state=st, conv_state=cs)
         st, cs = r["state"], r["conv_state"]
-        assert_close(f"step {t} h", h.cpu().numpy()[0], r["h"], STEP_TOL)
+        # token t has gone through t + 1 steps of the recurrence; h through none
+        assert_close(f"step {t} h", h.cpu().numpy()[0], r["h"], 1)
         if fused != "one":
-            assert_close(f"step {t} o", o.cpu().numpy()[0], r["o"], STEP_TOL)
-        assert_close(f"step {t} y", y.cpu().numpy()[0], r["y"], STEP_TOL)
-        assert_close(f"step {t} state", gm.slot_state(0), st, STEP_TOL)
-        assert_close(f"step {t} conv", gm.slot_conv(0), cs, STEP_TOL)
+            assert_close(f"step {t} o", o.cpu().numpy()[0], r["o"], t + 1)
+        assert_close(f"step {t} y", y.cpu().numpy()[0], r["y"], t + 1)
+        assert_close(f"step {t} state", gm.slot_state(0), st, t + 1)
+        assert_exact(f"step {t} conv", gm.slot_conv(0), cs)
     assert int(gm.pool.flags.item()) == 0
 
 
@@ -89,7 +83,7 @@ def test_decode_b64_one_step(fused):
     wl, res = _workload_and_oracle("b64")
     gm = GpuMixer(wl)
     gm.run(fused=fused)
-    _compare_all(gm, wl, res, STEP_TOL, "decode_b64", keys=("y", "h") if fused == "one" else ("o", "y", "h"))
+    _compare_all(gm, wl, res, "decode_b64", keys=("y", "h") if fused == "one" else ("o", "y", "h"))
     assert int(gm.pool.flags.item()) == 0
 
 
@@ -101,7 +95,7 @@ def test_decode_b256_one_step(fused):
     wl, res = _workload_and_oracle("b256")
     gm = GpuMixer(wl)
     gm.run(fused=fused)
-    _compare_all(gm, wl, res, STEP_TOL, "decode_b256", keys=("y", "h") if fused == "one" else ("o", "y", "h"))
+    _compare_all(gm, wl, res, "decode_b256", keys=("y", "h") if fused == "one" else ("o", "y", "h"))
 
 
 @FUSED
@@ -111,10 +105,8 @@ def test_prefill_b16_t512_state_on_chip(fused):
     wl, res = _workload_and_oracle("prefill")
     gm = GpuMixer(wl)
     gm.run(fused=fused)
-    # the first token is a plain decode step; after 512 steps the looser bound applies
-    assert_close("prefill o[t=0]", gm.o[:, 0].cpu().numpy(), _stack(res, "o")[:, 0], STEP_TOL)
-    assert_close("prefill h", gm.h.cpu().numpy(), _stack(res, "h"), STEP_TOL)
-    _compare_all(gm, wl, res, LONG_TOL, "prefill_b16_t512")
+    # token t of o and y at tol(t + 1): 1e-4 for the first token, 1e-3 for the 512th
+    _compare_all(gm, wl, res, "prefill_b16_t512")
 
 
 def test_512_sequential_single_launch_decodes():
@@ -132,9 +124,7 @@ def test_512_sequential_single_launch_decodes():
         one.run(t, t + 1, fused="one")
     torch.cuda.synchronize()
     log("512 sequential single-launch decodes: compare")
-    _compare_all(one, wl, res, LONG_TOL, "seq512", keys=("y", "h"))
-    first = assert_close("seq512 y[t=0]", one.y[:, 0].cpu().numpy(), _stack(res, "y")[:, 0], STEP_TOL)
-    log(f"seq512: first-token y rel error {first:.2e}")
+    _compare_all(one, wl, res, "seq512", keys=("y", "h"))
     multi = GpuMixer(wl)
     multi.run(fused=True)
     assert torch.equal(one.pool.state, multi.pool.state)
@@ -152,7 +142,7 @@ def test_ragged_pool2048_b1024(fused):
     wl, res = _workload_and_oracle("ragged")
     gm = GpuMixer(wl)
     gm.run(fused=fused)
-    st, _ = _compare_all(gm, wl, res, STEP_TOL, "ragged")
+    st, _ = _compare_all(gm, wl, res, "ragged")
     untouched = np.setdiff1d(np.arange(wl.n_slots), wl.slots)
     assert np.array_equal(st[untouched], wl.state[untouched]), "an untouched slot changed"
     assert np.array_equal(gm.pool.conv.cpu().numpy()[untouched], wl.conv_state[untouched])
@@ -213,10 +203,10 @@ def test_pool_beyond_2g_floats_top_slots():
         gm.run(slots=hi_d, fused=fused)
         torch.cuda.synchronize()
         for key in ("o", "y", "h") if fused != "one" else ("y", "h"):
-            assert_close(f"big pool {tag} {key}", getattr(gm, key).cpu().numpy(), _stack(res, key), STEP_TOL)
-        assert_close(f"big pool {tag} state", big.state[hi_d.long()].cpu().numpy(), _stack(res, "state"), STEP_TOL)
-        assert_close(f"big pool {tag} conv", big.conv[hi_d.long()].cpu().numpy(), _stack(res, "conv_state"),
-                     STEP_TOL)
+            assert_tokens(f"big pool {tag} {key}", getattr(gm, key).cpu().numpy(), [r[key] for r in res],
+                          [T] * len(hi), recurrent=key != "h")
+        assert_close(f"big pool {tag} state", big.state[hi_d.long()].cpu().numpy(), _stack(res, "state"), T)
+        assert_exact(f"big pool {tag} conv", big.conv[hi_d.long()].cpu().numpy(), _stack(res, "conv_state"))
         used += hi
     assert int(big.flags.item()) == 0
     # untouched slots, among them the neighbours of every slot used
@@ -240,7 +230,7 @@ def test_small_geometries_several_tiles_ragged_tail(geom, B, T):
     gm = GpuMixer(wl)
     gm.run()
     res = oracle.run_workload(wl)
-    _compare_all(gm, wl, res, STEP_TOL if T == 1 else 2 * STEP_TOL, "small")
+    _compare_all(gm, wl, res, "small")
 
 
 @FUSED
@@ -288,7 +278,7 @@ def test_beta0_gate0_leaves_state_bit_identical():
     gm.run()
     assert torch.equal(gm.pool.state, before)
     res = oracle.run_workload(wl)
-    _compare_all(gm, wl, res, STEP_TOL, "beta0")
+    _compare_all(gm, wl, res, "beta0")
 
 
 def test_beta1_unit_k_recalls_v():
@@ -307,7 +297,7 @@ def test_beta1_unit_k_recalls_v():
             k = h[b, 0, (g.h_k + j) * g.s:(g.h_k + j + 1) * g.s].astype(np.float64)
             v = h[b, 0, (2 * g.h_k + i) * g.s:(2 * g.h_k + i + 1) * g.s].astype(np.float64)
             kv = st[b, i].astype(np.float64).T @ k
-            assert np.abs(kv - v).max() <= STEP_TOL * np.abs(v).max()
+            assert np.abs(kv - v).max() <= tol(1) * np.abs(v).max()
 
 
 def test_zero_tokens_and_bad_counts():
@@ -323,7 +313,7 @@ def test_zero_tokens_and_bad_counts():
     assert np.array_equal(st[wl.slots[0]], wl.state[wl.slots[0]])
     assert (gm.o[0] == 0).all() and (gm.h[0] == 0).all()
     res = oracle.run_workload(wl)
-    _compare_all(gm, wl, res, STEP_TOL * 2, "ntok")
+    _compare_all(gm, wl, res, "ntok")
     # out-of-range counts: 9 -> 5 (T) and -3 -> 0, with the flag raised
     wl2 = W.make("ntok", 2, 5, seed=55, state_std=0.02, conv_std=1.0)
     gm2 = GpuMixer(wl2)
@@ -333,7 +323,7 @@ def test_zero_tokens_and_bad_counts():
     assert torch.equal(gm2.pool.state[1], before[1])
     wl2.n_tok = np.array([5, 0], np.int32)
     res2 = oracle.run_workload(wl2)
-    _compare_all(gm2, wl2, res2, STEP_TOL * 2, "ntok-clamped")
+    _compare_all(gm2, wl2, res2, "ntok-clamped")
 
 
 def test_bad_slot_is_skipped_and_flagged():
@@ -347,7 +337,7 @@ def test_bad_slot_is_skipped_and_flagged():
     assert (gm.o[1:] == 0).all() and (gm.y[1:] == 0).all() and (gm.h[1:] == 0).all()
     assert torch.equal(gm.pool.state[1:], before[1:])
     res = oracle.run_workload(wl, seqs=[0])
-    assert_close("badslot o", gm.o[0].cpu().numpy(), res[0]["o"], STEP_TOL)
+    assert_tokens("badslot o", gm.o[:1].cpu().numpy(), [res[0]["o"]], [wl.T])
 
 
 def test_pool_zero():
@@ -377,7 +367,7 @@ def test_gated_rmsnorm_ragged_rows_and_in_place():
         od = dev(o)
         y = torch.empty_like(od)
         G.gdn_gated_rmsnorm(od, dev(z), dev(w), 1e-6, y)
-        assert_close(f"rmsnorm rows={rows}", y.cpu().numpy(), ref, STEP_TOL)
+        assert_close(f"rmsnorm rows={rows}", y.cpu().numpy(), ref, 1)
         G.gdn_gated_rmsnorm(od, dev(z), dev(w), 1e-6, od)   # y aliasing o
         assert torch.equal(od, y)
 
@@ -458,7 +448,7 @@ def test_token_counts_across_conv_blocks(fused, B):
     gm = GpuMixer(wl)
     gm.run(fused=fused)
     res = oracle.run_workload(wl)
-    _compare_all(gm, wl, res, 3 * STEP_TOL, "blocks")
+    _compare_all(gm, wl, res, "blocks")
 
 
 @pytest.mark.parametrize("geom", [W.Geom(), W.Geom(h_k=2, h_v=6), W.Geom(h_k=2, h_v=4), W.Geom(h_k=2, h_v=2),
@@ -479,7 +469,7 @@ def test_single_launch_decode_equals_two_calls_bitwise(geom):
     assert torch.equal(a.h, b.h) and torch.equal(a.y, b.y)
     assert torch.equal(a.pool.state, b.pool.state) and torch.equal(a.pool.conv, b.pool.conv)
     res = oracle.run_workload(wl)
-    _compare_all(b, wl, res, STEP_TOL, "one-launch", keys=("y", "h"))
+    _compare_all(b, wl, res, "one-launch", keys=("y", "h"))
     c = GpuMixer(wl)
     y = torch.empty_like(c.y[:, 0])
     G.gdn_decode_fused(c.pool, c.qkv[:, 0].contiguous(), c.conv_w, c.alpha[:, 0].contiguous(),
@@ -500,7 +490,7 @@ def test_single_launch_decode_bad_slot():
     assert torch.equal(gm.pool.state[keep], before_s[keep]) and torch.equal(gm.pool.conv[keep], before_c[keep])
     wl.slots = np.array([2, 0, 0], np.int32)
     res = oracle.run_workload(wl, seqs=[0])
-    assert_close("one-bad y", gm.y[0].cpu().numpy(), res[0]["y"], STEP_TOL)
+    assert_close("one-bad y", gm.y[0].cpu().numpy(), res[0]["y"], 1)
 
 
 @pytest.mark.parametrize("T", [1, 4, 37])
@@ -525,7 +515,7 @@ def test_verify_window_then_commit(T):
     direct.run(fused=True)                        # all T tokens, persisted
     assert torch.equal(y, direct.y) and torch.equal(h, direct.h)
     res = oracle.run_workload(wl)
-    assert_close("window y", y.cpu().numpy(), np.stack([r["y"] for r in res]), 2 * STEP_TOL)
+    assert_tokens("window y", y.cpu().numpy(), [r["y"] for r in res], [T] * wl.B)
 
     G.gdn_commit(win.pool, win.qkv, h, win.alpha, win.beta_logit, win.dt, win.ssm_a, dev(n_keep), win.slots)
     kept = GpuMixer(wl)
@@ -633,8 +623,8 @@ def test_commit_window_equals_commit_then_window(T0, T1, ragged):
         direct.run(fused=True)
         assert torch.equal(y1, direct.y[:, T0:]) and torch.equal(h1, direct.h[:, T0:])
         res = oracle.run_workload(wl)
-        ref = np.stack([r["y"] for r in res])[:, T0:]
-        assert_close("round y", y1.cpu().numpy(), ref, 2 * STEP_TOL)
+        # the next window's token t follows the T0 committed tokens: T0 + t + 1 steps
+        assert_tokens("round y", y1.cpu().numpy(), [r["y"][T0:] for r in res], [T1] * B, first_step=T0 + 1)
 
 
 def test_speculative_round_b256_t4_full_size():
@@ -683,11 +673,11 @@ def test_speculative_round_b256_t4_full_size():
         slot = int(wl.slots[b])
         ref = oracle.mixer(g, wl.qkv[b, idx], wl.conv_w, wl.alpha[b, idx], wl.beta_logit[b, idx], wl.dt, wl.ssm_a,
                            wl.z[b, idx], wl.norm_w, wl.eps, wl.conv_state[slot], wl.state[slot])
-        assert_close(f"round y seq {b}", y1[b].cpu().numpy(), ref["y"][k:], 2 * STEP_TOL)
+        assert_tokens(f"round y seq {b}", y1[b:b + 1].cpu().numpy(), [ref["y"][k:]], [T], first_step=k + 1)
         com = oracle.mixer(g, wl.qkv[b, :k], wl.conv_w, wl.alpha[b, :k], wl.beta_logit[b, :k], wl.dt, wl.ssm_a,
                            wl.z[b, :k], wl.norm_w, wl.eps, wl.conv_state[slot], wl.state[slot])
-        assert_close(f"committed state seq {b}", fused.pool.state[slot].cpu().numpy(), com["state"], STEP_TOL)
-        assert_close(f"committed conv seq {b}", fused.pool.conv[slot].cpu().numpy(), com["conv_state"], STEP_TOL)
+        assert_close(f"committed state seq {b}", fused.pool.state[slot].cpu().numpy(), com["state"], k)
+        assert_exact(f"committed conv seq {b}", fused.pool.conv[slot].cpu().numpy(), com["conv_state"])
 
 
 # ------------------------------------------------------------------ alpha / beta projections
@@ -707,8 +697,8 @@ def test_ab_projection(B, T, n_embd, h_v):
     beta = torch.full((B, T, h_v), 7.0, device="cuda")
     G.gdn_ab_project(x, wa, wb, alpha, beta)
     ra, rb = oracle.ab_project(ab.x, ab.w_alpha, ab.w_beta)
-    assert_close("alpha", alpha.cpu().numpy(), ra, STEP_TOL)
-    assert_close("beta_logit", beta.cpu().numpy(), rb, STEP_TOL)
+    assert_close("alpha", alpha.cpu().numpy(), ra, 1)
+    assert_close("beta_logit", beta.cpu().numpy(), rb, 1)
 
 
 def test_ab_projection_feeds_the_recurrence():
@@ -724,7 +714,8 @@ def test_ab_projection_feeds_the_recurrence():
                      torch.from_numpy(ab.w_beta.view(np.int16)).cuda(), gm.alpha, gm.beta_logit)
     gm.run(fused=True)
     res = oracle.run_workload(wl)
-    _compare_all(gm, wl, res, 2 * STEP_TOL, "proj->mixer", keys=("y", "h"))
+    # alpha and beta come out of one projection: the mixer's token t is t + 2 steps in
+    _compare_all(gm, wl, res, "proj->mixer", keys=("y", "h"), first_step=2)
 
 
 def test_ab_projection_empty_is_a_no_op():
@@ -751,7 +742,7 @@ def test_model_variants_decode(gate_silu, after, fused):
     res = oracle.run_workload(wl)
     gm = GpuMixer(wl)
     gm.run(fused=fused)
-    _compare_all(gm, wl, res, STEP_TOL, "variant", keys=("y", "h") if fused == "one" else ("o", "y", "h"))
+    _compare_all(gm, wl, res, "variant", keys=("y", "h") if fused == "one" else ("o", "y", "h"))
 
 
 @VARIANTS
@@ -765,7 +756,7 @@ def test_model_variants_multi_token_ragged(gate_silu, after, fused):
     res = oracle.run_workload(wl)
     gm = GpuMixer(wl)
     gm.run(fused=fused)
-    _compare_all(gm, wl, res, STEP_TOL, "variant ragged")
+    _compare_all(gm, wl, res, "variant ragged")
 
 
 @VARIANTS

@@ -1,20 +1,20 @@
 """Parity of the qkv / z / out projections (gdn_split_bf16 + gdn_project_bf16) with the
 fp64 oracle on MI355X, through the C ABI.
 
-Tolerance: max |gpu - ref| <= 1e-4 x max |ref| (the per-step bar of the mixer). The
-split of x into bf16 hi + lo keeps each activation to within 2^-16 |x| and the
-matrix cores sum in fp32, so the expected error is near 1e-6 of max |ref|.
+Tolerance: the one bound of tests/parity.py.  A projection is one step, so its output
+is held to tol(1) = 1e-4 x max |ref|; in the chains through the mixer every product
+and every mixer token is one more step.  The split of x into bf16 hi + lo keeps each
+activation to within 2^-16 |x| and the matrix cores sum in fp32, so the expected error
+is near 1e-6 of max |ref|.
 """
 import numpy as np
 import pytest
 
 import gdn_workloads as W
 import oracle
-from gpu_harness import GpuMixer, assert_close, dev, log
+from gpu_harness import GpuMixer, assert_close, assert_tokens, dev, log
 
 pytestmark = pytest.mark.gpu
-
-TOL = 1e-4
 
 
 def _w(bits):
@@ -91,7 +91,7 @@ def test_projection_matches_oracle(rows, k, n):
     out = torch.full((rows, n), 7.0, device="cuda")
     G.gdn_project(dev(x), G.gdn_pack_bf16(_w(w)), out)
     torch.cuda.synchronize()
-    assert_close("out", out.cpu().numpy(), oracle.project(x, w), TOL)
+    assert_close("out", out.cpu().numpy(), oracle.project(x, w))
 
 
 @pytest.mark.parametrize("name", ["qkv", "z", "out"])
@@ -107,7 +107,7 @@ def test_projection_full_size_sampled(name):
     out = G.gdn_project(dev(x), G.gdn_pack_bf16(_w(w)))
     torch.cuda.synchronize()
     pick = np.array([0, 1, 31, 32, 63, 64, 100, 127, 128, 191, 200, 223, 224, 254, 255])
-    assert_close(name, out.cpu().numpy()[pick], oracle.project(x[pick], w), TOL)
+    assert_close(name, out.cpu().numpy()[pick], oracle.project(x[pick], w))
 
 
 @pytest.mark.parametrize("rows,k", [(512, 2560), (520, 2624)])
@@ -122,7 +122,7 @@ def test_projection_lds_form_sampled(rows, k):
     out = G.gdn_project(dev(x), G.gdn_pack_bf16(_w(w)))
     torch.cuda.synchronize()
     pick = np.unique(np.concatenate([np.linspace(0, rows - 1, 13).astype(int), [63, 64, 255, 256, rows - 1]]))
-    assert_close("out", out.cpu().numpy()[pick], oracle.project(x[pick], w), TOL)
+    assert_close("out", out.cpu().numpy()[pick], oracle.project(x[pick], w))
 
 
 @pytest.mark.parametrize("rows,k,n1,n2", [(256, 2560, 10240, 6144), (37, 200, 100, 60), (300, 136, 8192, 40),
@@ -142,8 +142,8 @@ def test_two_outputs_equal_the_concatenated_projection(rows, k, n1, n2):
     assert torch.equal(o1, whole[:, :n1]) and torch.equal(o2, whole[:, n1:])
     pick = np.unique(np.linspace(0, rows - 1, 9).astype(int))
     ref = oracle.project(x[pick], w)
-    assert_close("out1", o1.cpu().numpy()[pick], ref[:, :n1], TOL)
-    assert_close("out2", o2.cpu().numpy()[pick], ref[:, n1:], TOL)
+    assert_close("out1", o1.cpu().numpy()[pick], ref[:, :n1])
+    assert_close("out2", o2.cpu().numpy()[pick], ref[:, n1:])
 
 
 # (rows, k, n) whose launch splits the k range over 4, 3 or 2 workgroups per tile and
@@ -164,7 +164,7 @@ def test_projection_split_k_matches_oracle(rows, k, n):
     out = torch.full((rows, n), 7.0, device="cuda")
     G.gdn_project(dev(x), G.gdn_pack_bf16(_w(w)), out)
     torch.cuda.synchronize()
-    assert_close("out", out.cpu().numpy(), oracle.project(x, w), TOL)
+    assert_close("out", out.cpu().numpy(), oracle.project(x, w))
 
 
 def test_projection_workspace_is_scratch():
@@ -183,7 +183,7 @@ def test_projection_workspace_is_scratch():
     b = G.gdn_project_bf16(G.gdn_split_bf16(dev(x[:1])), wp, workspace=ws)
     torch.cuda.synchronize()
     assert torch.equal(a, ref32) and torch.equal(b, ref1)
-    assert_close("out", a.cpu().numpy(), oracle.project(x, w), TOL)
+    assert_close("out", a.cpu().numpy(), oracle.project(x, w))
 
 
 # the layer input's four projections in one launch (qkv, z, alpha and beta logits) at
@@ -211,7 +211,7 @@ def test_multi_outputs_equal_the_stacked_projection(rows, k, cols):
     c0 = 0
     for o, c in zip(outs, cols):
         assert torch.equal(o, whole[:, c0:c0 + c]), f"columns {c0}..{c0 + c} differ"
-        assert_close(f"out[{c0}:{c0 + c}]", o.cpu().numpy()[pick], ref[:, c0:c0 + c], TOL)
+        assert_close(f"out[{c0}:{c0 + c}]", o.cpu().numpy()[pick], ref[:, c0:c0 + c])
         c0 += c
 
 
@@ -321,8 +321,11 @@ def test_projections_around_the_mixer():
     gm.run(fused=True)
     out = G.gdn_project(gm.y.view(B * T, -1), G.gdn_pack_bf16(_w(wout)))
     torch.cuda.synchronize()
-    assert_close("y", gm.y.cpu().numpy().reshape(y_ref.shape), y_ref, 2 * TOL)
-    assert_close("out", out.cpu().numpy(), out_ref, 2 * TOL)
+    # qkv, z, alpha and beta come out of one product each: token t of y is t + 2 steps
+    # from x, and the out projection adds one more
+    assert_tokens("y", gm.y.cpu().numpy(), list(y_ref), [T] * B, first_step=2)
+    assert_tokens("out", out.cpu().numpy().reshape(B, T, -1), list(out_ref.reshape(B, T, -1)), [T] * B,
+                  first_step=3)
 
 
 def test_four_launch_layer_decode_matches_the_oracle():
@@ -360,7 +363,8 @@ def test_four_launch_layer_decode_matches_the_oracle():
                        None, gm.slots, ys=ys)
     out = G.gdn_project_bf16(ys, wp_out)
     torch.cuda.synchronize()
-    assert_close("out", out.cpu().numpy(), out_ref, 2 * TOL)
+    # x -> projections (1) -> one mixer token (2) -> out projection (3)
+    assert_close("out", out.cpu().numpy(), out_ref, 3)
     for b in range(B):
         slot = int(wl.slots[b])
-        assert_close(f"state[{b}]", gm.pool.state[slot].cpu().numpy(), res[b]["state"], 2 * TOL)
+        assert_close(f"state[{b}]", gm.pool.state[slot].cpu().numpy(), res[b]["state"], 2)
