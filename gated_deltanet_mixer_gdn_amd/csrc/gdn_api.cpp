@@ -10,8 +10,11 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstdint>
+#include <algorithm>
 #include <new>
 #include <string>
+#include <utility>
+#include <vector>
 
 #include "gdn.h"
 #include "gdn_kernels.h"
@@ -124,14 +127,23 @@ int gdn_abi_version(void) { return GDN_ABI_VERSION; }
 const char* gdn_last_error(void) { return g_last_error.c_str(); }
 
 size_t gdn_state_pool_bytes(const gdn_geom* g, int64_t n_slots) {
-    if (check_geom(g, "gdn_state_pool_bytes") != GDN_OK) return 0;
+    const char* fn = "gdn_state_pool_bytes";
+    if (check_geom(g, fn) != GDN_OK) return 0;
     if (n_slots <= 0 || n_slots > ((int64_t) 1 << 31)) {
-        fail(GDN_ERR_ARG, "gdn_state_pool_bytes", "n_slots=%lld out of range", (long long) n_slots);
+        fail(GDN_ERR_ARG, fn, "n_slots=%lld out of range", (long long) n_slots);
+        return 0;
+    }
+    // each term below a quarter of the address space, so the roundings and the sum
+    // cannot wrap either
+    const size_t limit = SIZE_MAX / 4;
+    const size_t sp = state_bytes_per_slot(*g), cp = conv_bytes_per_slot(*g);
+    if ((size_t) n_slots > limit / sp || (size_t) n_slots > limit / cp) {
+        fail(GDN_ERR_ARG, fn, "a pool of %lld slots of %zu + %zu bytes does not fit in the address space",
+             (long long) n_slots, sp, cp);
         return 0;
     }
     ok();
-    return kFlagBytes + round_up((size_t) n_slots * state_bytes_per_slot(*g)) +
-           round_up((size_t) n_slots * conv_bytes_per_slot(*g));
+    return kFlagBytes + round_up((size_t) n_slots * sp) + round_up((size_t) n_slots * cp);
 }
 
 int gdn_state_pool_create(const gdn_geom* g, int64_t n_slots, void* dev_base, size_t bytes,
@@ -143,6 +155,7 @@ int gdn_state_pool_create(const gdn_geom* g, int64_t n_slots, void* dev_base, si
     if (n_slots <= 0 || n_slots > ((int64_t) 1 << 31))
         return fail(GDN_ERR_ARG, fn, "n_slots=%lld out of range", (long long) n_slots);
     const size_t need = gdn_state_pool_bytes(g, n_slots);
+    if (need == 0) return fail(GDN_ERR_ARG, fn, "%s", g_last_error.c_str());
     if (!dev_base) return fail(GDN_ERR_ARG, fn, "dev_base is null");
     if (!aligned(dev_base, kAlign)) return fail(GDN_ERR_ARG, fn, "dev_base is not 256-byte aligned");
     if (bytes < need)
@@ -176,6 +189,40 @@ int gdn_state_pool_create(const gdn_geom* g, int64_t n_slots, void* dev_base, si
 }
 
 void gdn_state_pool_destroy(gdn_pool* p) { delete p; }
+
+int gdn_check_slots(const int32_t* host_slots, int32_t n, int64_t n_slots) {
+    const char* fn = "gdn_check_slots";
+    if (n < 0) return fail(GDN_ERR_ARG, fn, "n=%d is negative", n);
+    if (n_slots <= 0) return fail(GDN_ERR_ARG, fn, "n_slots=%lld must be positive", (long long) n_slots);
+    if (n == 0) return ok();
+    if (!host_slots) return fail(GDN_ERR_ARG, fn, "host_slots is null");
+    for (int32_t b = 0; b < n; ++b)
+        if (host_slots[b] < 0 || (int64_t) host_slots[b] >= n_slots)
+            return fail(GDN_ERR_ARG, fn, "slots[%d]=%d is outside the pool's %lld slots", b, host_slots[b],
+                        (long long) n_slots);
+    // (slot, position) sorted: equal slots sit together, the earliest position first
+    std::vector<std::pair<int32_t, int32_t>> seen;
+    try {
+        seen.resize((size_t) n);
+    } catch (const std::bad_alloc&) {
+        return fail(GDN_ERR_ARG, fn, "out of host memory for %d slots", n);
+    }
+    for (int32_t b = 0; b < n; ++b) seen[(size_t) b] = {host_slots[b], b};
+    std::sort(seen.begin(), seen.end());
+    int32_t first_repeat = -1, of = -1;
+    for (size_t u = 1; u < seen.size(); ++u)
+        if (seen[u].first == seen[u - 1].first && (first_repeat < 0 || seen[u].second < first_repeat)) {
+            first_repeat = seen[u].second;
+            // the earliest position holding the same slot
+            size_t v = u;
+            while (v > 0 && seen[v - 1].first == seen[u].first) --v;
+            of = seen[v].second;
+        }
+    if (first_repeat >= 0)
+        return fail(GDN_ERR_ARG, fn, "slots[%d]=%d repeats slots[%d]: slots within a call must be unique",
+                    first_repeat, host_slots[first_repeat], of);
+    return ok();
+}
 
 float* gdn_state_pool_state(const gdn_pool* p) { return p ? p->state : nullptr; }
 float* gdn_state_pool_conv(const gdn_pool* p) { return p ? p->conv : nullptr; }

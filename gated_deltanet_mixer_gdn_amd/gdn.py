@@ -25,6 +25,7 @@ EXPORTS = (
     "gdn_gated_rmsnorm",
     "gdn_ab_project", "gdn_split_bf16_bytes", "gdn_pack_bf16_bytes", "gdn_split_bf16", "gdn_pack_bf16",
     "gdn_project_bf16", "gdn_project2_bf16", "gdn_project_workspace_bytes", "gdn_project_multi_bf16",
+    "gdn_check_slots",
 )
 
 
@@ -80,6 +81,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "gdn_state_pool_bytes": ([G, i64], ctypes.c_size_t),
         "gdn_state_pool_create": ([G, i64, vp, ctypes.c_size_t, ctypes.POINTER(vp)], ctypes.c_int),
         "gdn_state_pool_destroy": ([vp], None),
+        "gdn_check_slots": ([vp, i32, i64], ctypes.c_int),
         "gdn_state_pool_state": ([vp], vp),
         "gdn_state_pool_conv": ([vp], vp),
         "gdn_state_pool_flags": ([vp], vp),
@@ -144,6 +146,45 @@ def _i32(t, name: str, n: int):
     return t.data_ptr()
 
 
+# Debug mode: when on, every call that takes a device slot list first copies it to the
+# host and runs gdn_check_slots on it (a synchronising copy, so off by default).  Also
+# switched on by the environment variable GDN_CHECK_SLOTS=1.
+_check_slots_on = os.environ.get("GDN_CHECK_SLOTS", "") not in ("", "0")
+
+
+def set_slot_checks(on: bool) -> None:
+    """Switch the host-side slot validation of every mixer call on or off."""
+    global _check_slots_on
+    _check_slots_on = bool(on)
+
+
+def gdn_check_slots(slots, n_slots: int) -> None:
+    """Validate a slot list on the host (gdn_check_slots): every entry in [0, n_slots) and
+    none repeated.  slots: an int32 torch tensor (any device) or array-like.  Raises
+    GdnError (GDN_ERR_ARG) naming the first bad entry."""
+    import numpy as np
+    try:
+        import torch
+        if isinstance(slots, torch.Tensor):
+            slots = slots.detach().cpu().numpy()
+    except ImportError:
+        pass
+    a = np.ascontiguousarray(np.asarray(slots).reshape(-1))
+    if a.size and (a.dtype.kind not in "iu" or a.min() < -2 ** 31 or a.max() >= 2 ** 31):
+        raise ValueError("slots must hold 32-bit integers")
+    a = a.astype(np.int32)
+    _check(load_library().gdn_check_slots(a.ctypes.data if a.size else None, int(a.size), int(n_slots)))
+
+
+def _slots(pool: "StatePool", slots, n: int):
+    """The device pointer of a slot list (None: slot b for sequence b), validated on the
+    host first when slot checks are on."""
+    ptr = _i32(slots, "slots", n)
+    if _check_slots_on and slots is not None:
+        gdn_check_slots(slots, pool.n_slots)
+    return ptr
+
+
 def gdn_state_pool_bytes(n_slots: int, geom: Geom = Geom()) -> int:
     g = geom.c()
     n = load_library().gdn_state_pool_bytes(ctypes.byref(g), n_slots)
@@ -197,7 +238,7 @@ class StatePool:
 
 def gdn_state_pool_zero(pool: StatePool, slots=None):
     n = 0 if slots is None else slots.numel()
-    ptr = _i32(slots, "slots", n)
+    ptr = _slots(pool, slots, n)
     _check(load_library().gdn_state_pool_zero(pool.handle, ptr, n, _stream(pool.buffer)))
 
 
@@ -207,7 +248,7 @@ def gdn_conv_silu_norm(pool: StatePool, qkv, conv_w, eps: float, h, slots=None, 
     C = pool.geom.channels
     args = (_f32(qkv, "qkv", (B, T, C)), _f32(conv_w, "conv_w", (C, pool.geom.d_conv)),
             _f32(h, "h", (B, T, C)))
-    _check(load_library().gdn_conv_silu_norm(pool.handle, _i32(slots, "slots", B), _i32(n_tok, "n_tok", B),
+    _check(load_library().gdn_conv_silu_norm(pool.handle, _slots(pool, slots, B), _i32(n_tok, "n_tok", B),
                                              B, T, args[0], args[1], float(eps), args[2], _stream(qkv)))
 
 
@@ -218,7 +259,7 @@ def gdn_decode_step(pool: StatePool, h, alpha, beta_logit, dt, ssm_a, o, slots=N
     ptrs = (_f32(h, "h", (B, T, g.channels)), _f32(alpha, "alpha", (B, T, g.h_v)),
             _f32(beta_logit, "beta_logit", (B, T, g.h_v)), _f32(dt, "dt", (g.h_v,)),
             _f32(ssm_a, "ssm_a", (g.h_v,)), _f32(o, "o", (B, T, g.h_v, g.s)))
-    _check(load_library().gdn_decode_step(pool.handle, _i32(slots, "slots", B), _i32(n_tok, "n_tok", B), B, T,
+    _check(load_library().gdn_decode_step(pool.handle, _slots(pool, slots, B), _i32(n_tok, "n_tok", B), B, T,
                                           *ptrs, _stream(h)))
 
 
@@ -232,7 +273,7 @@ def gdn_decode_step_norm(pool: StatePool, h, alpha, beta_logit, dt, ssm_a, z, no
             _f32(ssm_a, "ssm_a", (g.h_v,)), _f32(z, "z", (B, T, g.h_v * g.s)),
             _f32(norm_w, "norm_w", (g.s,)))
     o_ptr = None if o is None else _f32(o, "o", (B, T, g.h_v, g.s))
-    _check(load_library().gdn_decode_step_norm(pool.handle, _i32(slots, "slots", B), _i32(n_tok, "n_tok", B),
+    _check(load_library().gdn_decode_step_norm(pool.handle, _slots(pool, slots, B), _i32(n_tok, "n_tok", B),
                                                B, T, *ptrs, float(eps), o_ptr,
                                                _f32(y, "y", (B, T, g.h_v * g.s)), _stream(h)))
 
@@ -259,7 +300,7 @@ def gdn_decode_fused(pool: StatePool, qkv, conv_w, alpha, beta_logit, dt, ssm_a,
             ptr(alpha, "alpha", B * g.h_v), ptr(beta_logit, "beta_logit", B * g.h_v),
             _f32(dt, "dt", (g.h_v,)), _f32(ssm_a, "ssm_a", (g.h_v,)), ptr(z, "z", B * vdim),
             _f32(norm_w, "norm_w", (g.s,)))
-    _check(load_library().gdn_decode_fused(pool.handle, _i32(slots, "slots", B), B, *args, float(eps),
+    _check(load_library().gdn_decode_fused(pool.handle, _slots(pool, slots, B), B, *args, float(eps),
                                            None if y is None else ptr(y, "y", B * vdim),
                                            None if h is None else ptr(h, "h", B * g.channels),
                                            None if ys is None else ys.data.data_ptr(), _stream(qkv)))
@@ -275,7 +316,7 @@ def gdn_verify_window(pool: StatePool, qkv, conv_w, alpha, beta_logit, dt, ssm_a
             _f32(alpha, "alpha", (B, T, g.h_v)), _f32(beta_logit, "beta_logit", (B, T, g.h_v)),
             _f32(dt, "dt", (g.h_v,)), _f32(ssm_a, "ssm_a", (g.h_v,)), _f32(z, "z", (B, T, g.h_v * g.s)),
             _f32(norm_w, "norm_w", (g.s,)))
-    _check(load_library().gdn_verify_window(pool.handle, _i32(slots, "slots", B), _i32(n_tok, "n_tok", B), B, T,
+    _check(load_library().gdn_verify_window(pool.handle, _slots(pool, slots, B), _i32(n_tok, "n_tok", B), B, T,
                                             *ptrs, float(eps), _f32(h, "h", (B, T, g.channels)),
                                             _f32(y, "y", (B, T, g.h_v * g.s)), _stream(qkv)))
 
@@ -288,7 +329,7 @@ def gdn_commit(pool: StatePool, qkv, h, alpha, beta_logit, dt, ssm_a, n_keep=Non
     ptrs = (_f32(qkv, "qkv", (B, T, g.channels)), _f32(h, "h", (B, T, g.channels)),
             _f32(alpha, "alpha", (B, T, g.h_v)), _f32(beta_logit, "beta_logit", (B, T, g.h_v)),
             _f32(dt, "dt", (g.h_v,)), _f32(ssm_a, "ssm_a", (g.h_v,)))
-    _check(load_library().gdn_commit(pool.handle, _i32(slots, "slots", B), _i32(n_keep, "n_keep", B), B, T,
+    _check(load_library().gdn_commit(pool.handle, _slots(pool, slots, B), _i32(n_keep, "n_keep", B), B, T,
                                      *ptrs, _stream(qkv)))
 
 
@@ -309,7 +350,7 @@ def gdn_commit_window(pool: StatePool, prev, n_keep, qkv, conv_w, alpha, beta_lo
           _f32(alpha, "alpha", (B, T1, g.h_v)), _f32(beta_logit, "beta_logit", (B, T1, g.h_v)),
           _f32(dt, "dt", (g.h_v,)), _f32(ssm_a, "ssm_a", (g.h_v,)), _f32(z, "z", (B, T1, g.h_v * g.s)),
           _f32(norm_w, "norm_w", (g.s,)))
-    _check(load_library().gdn_commit_window(pool.handle, _i32(slots, "slots", B), B, _i32(n_keep, "n_keep", B), T0,
+    _check(load_library().gdn_commit_window(pool.handle, _slots(pool, slots, B), B, _i32(n_keep, "n_keep", B), T0,
                                             *p0, _i32(n_tok, "n_tok", B), T1, *p1, float(eps),
                                             _f32(h, "h", (B, T1, g.channels)), _f32(y, "y", (B, T1, g.h_v * g.s)),
                                             _stream(qkv)))

@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 6
+#define GDN_ABI_VERSION 7
 
 enum {
     GDN_OK = 0,
@@ -106,7 +106,8 @@ const char* gdn_last_error(void);
  * Each region starts on a 256-byte boundary.  Per slot at the pages' geometry:
  * 3 MiB of state + 120 KiB of conv history. */
 
-/* Bytes a pool of n_slots needs (0 if the arguments are invalid).  Host call. */
+/* Bytes a pool of n_slots needs (0 if the arguments are invalid, n_slots is outside
+ * [1, 2^31] or the pool would not fit in the address space).  Host call. */
 size_t gdn_state_pool_bytes(const gdn_geom* g, int64_t n_slots);
 
 /* Describe a pool over `dev_base` (>= gdn_state_pool_bytes bytes of device memory
@@ -118,6 +119,18 @@ int gdn_state_pool_create(const gdn_geom* g, int64_t n_slots, void* dev_base, si
 
 /* Free the descriptor (not the device memory).  NULL is ignored. */
 void gdn_state_pool_destroy(gdn_pool* p);
+
+/* Host-side validation of a slot list before it goes to the device, for callers that
+ * want a debug check: the device calls skip and flag an index outside the pool but do
+ * not look for repeats, whose state updates would race.  host_slots: HOST int32 [n].
+ * GDN_OK when every entry lies in [0, n_slots) and none repeats; otherwise GDN_ERR_ARG,
+ * and gdn_last_error() names the first entry out of range or, if none is, the first
+ * entry that repeats an earlier one and the position of that earlier one.  n = 0 is
+ * valid; n_slots must be positive.  Touches no device and enqueues nothing.  (The
+ * pages' layer code turns inputs it cannot handle correctly into an error instead of
+ * carrying on with a guess: "src/core/layer.cpp" page, the planes lookup of the
+ * quantized forms.) */
+int gdn_check_slots(const int32_t* host_slots, int32_t n, int64_t n_slots);
 
 /* Device addresses of the regions above, and the pool's shape (NULL / 0 for p = NULL). */
 float* gdn_state_pool_state(const gdn_pool* p);

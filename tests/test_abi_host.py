@@ -71,7 +71,7 @@ def test_library_is_built_for_gfx950_only(tmp_path):
 
 
 def test_abi_version(L):
-    assert L.gdn_abi_version() == 6
+    assert L.gdn_abi_version() == 7
 
 
 def _geom(h_k=16, h_v=48, s=128, d_conv=4):
@@ -92,6 +92,82 @@ def test_pool_bytes(L):
     bad = _geom(s=64)
     assert L.gdn_state_pool_bytes(ctypes.byref(bad), 3) == 0
     assert b"built for" in L.gdn_last_error()
+
+
+def test_pool_bytes_that_would_wrap_are_refused(L):
+    """A pool whose byte count passes the address space (a wide geometry times 2^31
+    slots) is refused, and so is creating it, instead of wrapping to a small size."""
+    from gated_deltanet_mixer_gdn_amd.gdn import GDN_ERR_ARG
+    wide = _geom(h_k=1, h_v=1 << 22)              # 2^38 bytes of state per slot
+    assert L.gdn_state_pool_bytes(ctypes.byref(wide), 1) == 256 + (1 << 38) + (2 + (1 << 22)) * 128 * 3 * 4
+    assert L.gdn_state_pool_bytes(ctypes.byref(wide), 1 << 31) == 0
+    assert b"address space" in L.gdn_last_error()
+    h = ctypes.c_void_p()
+    assert L.gdn_state_pool_create(ctypes.byref(wide), 1 << 31, 4096, 1 << 40, ctypes.byref(h)) == GDN_ERR_ARG
+    assert b"address space" in L.gdn_last_error() and h.value is None
+    # the largest pool of the pages' geometry still has a size
+    g = _geom()
+    assert L.gdn_state_pool_bytes(ctypes.byref(g), 1 << 31) > (1 << 31) * 48 * 128 * 128 * 4
+
+
+def _slots_rc(L, slots, n_slots):
+    import numpy as np
+    a = np.ascontiguousarray(slots, dtype=np.int32)
+    return L.gdn_check_slots(a.ctypes.data if a.size else None, int(a.size), n_slots)
+
+
+def test_check_slots_clean_lists(L):
+    from gated_deltanet_mixer_gdn_amd.gdn import GDN_OK
+    import numpy as np
+    assert _slots_rc(L, [], 4) == GDN_OK
+    assert _slots_rc(L, [3, 0, 2, 1], 4) == GDN_OK
+    perm = np.random.default_rng(3).choice(2048, 1024, replace=False)
+    assert _slots_rc(L, perm, 2048) == GDN_OK
+    assert L.gdn_last_error() == b""
+
+
+def test_check_slots_out_of_range(L):
+    from gated_deltanet_mixer_gdn_amd.gdn import GDN_ERR_ARG
+    assert _slots_rc(L, [0, 4, 1], 4) == GDN_ERR_ARG
+    assert L.gdn_last_error() == b"gdn_check_slots: slots[1]=4 is outside the pool's 4 slots"
+    assert _slots_rc(L, [0, 1, -1, 9], 4) == GDN_ERR_ARG
+    assert b"slots[2]=-1" in L.gdn_last_error()
+    assert L.gdn_check_slots(None, 3, 4) == GDN_ERR_ARG
+    assert b"host_slots is null" in L.gdn_last_error()
+    assert L.gdn_check_slots(None, -1, 4) == GDN_ERR_ARG
+    assert _slots_rc(L, [0], 0) == GDN_ERR_ARG
+
+
+def test_check_slots_duplicates(L):
+    """The first entry that repeats an earlier one is named, with that earlier position,
+    whatever order the repeats come in."""
+    from gated_deltanet_mixer_gdn_amd.gdn import GDN_ERR_ARG
+    assert _slots_rc(L, [5, 2, 7, 2], 8) == GDN_ERR_ARG
+    assert L.gdn_last_error() == b"gdn_check_slots: slots[3]=2 repeats slots[1]: slots within a call must be unique"
+    assert _slots_rc(L, [1, 6, 6, 1, 6], 8) == GDN_ERR_ARG
+    assert b"slots[2]=6 repeats slots[1]" in L.gdn_last_error()
+    assert _slots_rc(L, [0, 0], 1) == GDN_ERR_ARG
+    assert b"slots[1]=0 repeats slots[0]" in L.gdn_last_error()
+
+
+def test_binding_check_slots_and_debug_switch():
+    """The binding's gdn_check_slots raises GdnError on a bad list; the debug switch
+    turns the host check of every mixer call on and off."""
+    import numpy as np
+    import gated_deltanet_mixer_gdn_amd as G
+    from gated_deltanet_mixer_gdn_amd import gdn
+    G.gdn_check_slots(np.array([2, 0, 1], np.int32), 3)
+    with pytest.raises(G.GdnError) as e:
+        G.gdn_check_slots([2, 0, 2], 3)
+    assert e.value.code == G.GDN_ERR_ARG and "repeats" in str(e.value)
+    was = gdn._check_slots_on
+    try:
+        G.set_slot_checks(True)
+        assert gdn._check_slots_on
+        G.set_slot_checks(False)
+        assert not gdn._check_slots_on
+    finally:
+        G.set_slot_checks(was)
 
 
 def test_pool_create_argument_errors(L):
