@@ -422,7 +422,226 @@ def verify_round(G, W, B: int, T: int, reps: int = 20):
         flush=True)
 
 
+def _algorithmic(geom, B, T, n_tok=None):
+    """algorithmic_bytes for a batch described by its shape alone."""
+    from types import SimpleNamespace
+    return algorithmic_bytes(SimpleNamespace(geom=geom, B=B, T=T, n_tok=n_tok))
+
+
+def _event_span(stream, fn, reps):
+    """Mean microseconds of fn over reps calls, one HIP event pair on the launch stream
+    around all of them (the calls are queued back to back)."""
+    import torch
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record(stream)
+    for _ in range(reps):
+        fn()
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    return ev[0].elapsed_time(ev[1]) / reps * 1000.0
+
+
+def _kernel_events(stream, launches, reps):
+    """Mean microseconds of each launch of a several-launch step, each bracketed by its
+    own HIP event pair on every one of reps steps (an event record costs a few
+    microseconds, under 1% of the kernels timed this way)."""
+    import numpy as np
+    import torch
+    names = list(launches)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(reps)]
+    for e in evs:
+        e[0].record(stream)
+        for i, name in enumerate(names):
+            launches[name]()
+            e[i + 1].record(stream)
+    torch.cuda.synchronize()
+    return {name: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs])) * 1000.0
+            for i, name in enumerate(names)}
+
+
+def config_blocks(G, W, stream, steps: int, warmup: int):
+    """Every workload of the mixer at one GPU, timed on inputs drawn on the device with
+    the workloads' distributions (seeded torch generator; the ragged slot list and token
+    counts from a seeded numpy generator): qkv, alpha, beta logits, z ~ N(0, 1),
+    conv_w ~ N(0, 0.5), dt ~ N(0, 0.5), ssm_a = -exp(U(-1, 1)), norm_w ~ 1 + N(0, 0.1),
+    filled states ~ N(0, 0.02) and histories ~ N(0, 1).  Parity on the numpy-drawn
+    workloads is the tests' job; these numbers only need the shapes and value ranges.
+      tiny_b1_t8      8 sequential single-launch decode tokens of one sequence, captured
+                      in one HIP graph and replayed: microseconds per token (launch- and
+                      latency-bound; GB/s of its algorithmic bytes for reference)
+      decode_b64      one single-launch decode token of 64 sequences: effective GB/s
+                      (its 192 MiB of state can sit in the 256 MB Infinity Cache)
+      decode_b256     the same at 256 sequences (the headline's configuration)
+      prefill         16 sequences x 512 tokens in one call of the two-launch form: the
+                      recurrence kernel in TFLOP/s against the fp32 VALU peak
+      ragged          1024 sequences at random slots of a 2048-slot pool, U{1..8}
+                      tokens each, in one call of the two-launch form: GB/s"""
+    import numpy as np
+    import torch
+    geom = G.Geom()
+    C, hv, vd, S = geom.channels, geom.h_v, geom.h_v * geom.s, geom.s
+    eps = 1e-6
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(41)
+    rnd = lambda *shape, std=1.0: torch.randn(*shape, generator=gen, device="cuda") * std
+    conv_w, dt, norm_w = rnd(C, geom.d_conv, std=0.5), rnd(hv, std=0.5), 1.0 + rnd(S, std=0.1)
+    ssm_a = -torch.exp(torch.rand(hv, generator=gen, device="cuda") * 2.0 - 1.0)
+    out = {}
+
+    def pool_of(n_slots, state_std, conv_std):
+        pool = G.StatePool(n_slots, geom)
+        if state_std:
+            pool.state.normal_(0.0, state_std, generator=gen)
+        else:
+            pool.state.zero_()
+        if conv_std:
+            pool.conv.normal_(0.0, conv_std, generator=gen)
+        else:
+            pool.conv.zero_()
+        pool.flags.zero_()
+        return pool
+
+    # tiny: 8 sequential decode tokens of one sequence, one graph of 8 launches
+    T = 8
+    pool = pool_of(1, 0.0, 0.0)
+    qkv, alpha, bl, z = rnd(T, 1, C), rnd(T, 1, hv), rnd(T, 1, hv), rnd(T, 1, vd)
+    y = torch.empty(T, 1, vd, device="cuda")
+    tokens = lambda: [G.gdn_decode_fused(pool, qkv[t], conv_w, alpha[t], bl[t], dt, ssm_a, z[t], norm_w, eps, y[t])
+                      for t in range(T)]
+    for _ in range(3):
+        tokens()
+    torch.cuda.synchronize()
+    eager_us = _event_span(stream, tokens, max(steps // 4, 10)) / T
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        tokens()
+    graph.replay()
+    torch.cuda.synchronize()
+    graph_us = _event_span(torch.cuda.current_stream(), graph.replay, max(steps // 4, 10)) / T
+    nb, _ = _algorithmic(geom, 1, 1)
+    out["tiny_b1_t8"] = {
+        "form": "gdn_decode_fused, 8 sequential calls of B=1, captured in one HIP graph",
+        "us_per_token_graph": graph_us, "us_per_token_eager": eager_us,
+        "algorithmic_bytes_per_token": nb["one"],
+        "roofline": {"bound": "latency", "achieved": nb["one"] / graph_us / 1e3, "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": nb["one"] / graph_us / 1e3 / HBM_PEAK_GBPS,
+                     "note": "16 workgroups, one per qk head: one workgroup's latency sets the time"}}
+    log(f"tiny_b1_t8: {graph_us:.1f} us per token in a graph, {eager_us:.1f} us eager")
+    del pool
+
+    # single-launch decode at 64 and 256 sequences
+    for B in (64, 256):
+        pool = pool_of(B, 0.02, 1.0)
+        qkv, alpha, bl, z = rnd(B, C), rnd(B, hv), rnd(B, hv), rnd(B, vd)
+        y = torch.empty(B, vd, device="cuda")
+        fn = lambda: G.gdn_decode_fused(pool, qkv, conv_w, alpha, bl, dt, ssm_a, z, norm_w, eps, y)
+        for _ in range(warmup):
+            fn()
+        us = _event_span(stream, fn, steps)
+        nb, units = _algorithmic(geom, B, 1)
+        gbps = nb["one"] / us / 1e3
+        out[f"decode_b{B}"] = {
+            "form": "gdn_decode_fused (one launch)", "us_per_step": us, "seq_head_steps_per_s": units / us * 1e6,
+            "algorithmic_bytes": nb["one"],
+            "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                         "frac": gbps / HBM_PEAK_GBPS,
+                         **({"note": "effective: the 192 MiB of state can sit in the 256 MB Infinity Cache"}
+                            if B == 64 else {})}}
+        log(f"decode_b{B}: {us:.1f} us per step, {gbps:.0f} GB/s")
+        del pool
+
+    # the two-launch form over many tokens: prefill and the ragged pool
+    def two_launch(name, n_slots, B, T, state_std, conv_std, slots=None, n_tok=None, reps=None):
+        pool = pool_of(n_slots, state_std, conv_std)
+        qkv, alpha, bl, z = rnd(B, T, C), rnd(B, T, hv), rnd(B, T, hv), rnd(B, T, vd)
+        h = torch.empty(B, T, C, device="cuda")
+        y = torch.empty(B, T, vd, device="cuda")
+        sl = None if slots is None else torch.from_numpy(slots).cuda()
+        nt = None if n_tok is None else torch.from_numpy(n_tok).cuda()
+        launches = {"conv": lambda: G.gdn_conv_silu_norm(pool, qkv, conv_w, eps, h, sl, nt),
+                    "recurrence": lambda: G.gdn_decode_step_norm(pool, h, alpha, bl, dt, ssm_a, z, norm_w, eps, y,
+                                                                 None, sl, nt)}
+        for _ in range(max(warmup // 4, 2)):
+            for f in launches.values():
+                f()
+        torch.cuda.synchronize()
+        us = _kernel_events(stream, launches, reps)
+        nb, units = _algorithmic(geom, B, T, n_tok)
+        flags = int(pool.flags.item())
+        if flags:
+            raise SystemExit(f"bench.py: device flag word set ({flags:#x}) in {name}")
+        del pool
+        return us, nb, units
+
+    reps = max(steps // 10, 10)
+    us, nb, units = two_launch("prefill", 16, 16, 512, 0.0, 0.0, reps=reps)
+    flops = units * FLOP_PER_SEQ_HEAD_STEP
+    tflops = flops / us["recurrence"] / 1e6
+    step_us = us["conv"] + us["recurrence"]
+    out["prefill_b16_t512"] = {
+        "form": "gdn_conv_silu_norm + gdn_decode_step_norm, 512 tokens per call",
+        "kernel_us": us, "us_per_step": step_us, "tokens_per_s": 16 * 512 / step_us * 1e6,
+        "algorithmic_flops_recurrence": flops, "algorithmic_bytes": {"conv": nb["conv"], "recurrence": nb["step_norm"]},
+        "conv_gbps": nb["conv"] / us["conv"] / 1e3,
+        "roofline": {"bound": "alu", "kernel": "decode_multi_kernel<fused norm>", "achieved": tflops,
+                     "peak": VALU_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": tflops / VALU_PEAK_TFLOPS,
+                     "hbm_gbps": nb["step_norm"] / us["recurrence"] / 1e3}}
+    log(f"prefill: conv {us['conv']:.1f} us, recurrence {us['recurrence']:.1f} us = {tflops:.1f} TFLOP/s")
+
+    rng = np.random.default_rng(5)
+    slots = rng.choice(2048, 1024, replace=False).astype(np.int32)
+    n_tok = rng.integers(1, 9, 1024).astype(np.int32)
+    us, nb, units = two_launch("ragged", 2048, 1024, 8, 0.02, 1.0, slots, n_tok, reps=reps)
+    gbps = nb["step_norm"] / us["recurrence"] / 1e3
+    step_us = us["conv"] + us["recurrence"]
+    out["ragged_pool2048_b1024"] = {
+        "form": "gdn_conv_silu_norm + gdn_decode_step_norm, per-sequence token counts, 8 tokens per call",
+        "tokens": int(n_tok.sum()), "kernel_us": us, "us_per_step": step_us,
+        "seq_head_steps_per_s": units / step_us * 1e6,
+        "algorithmic_bytes": {"conv": nb["conv"], "recurrence": nb["step_norm"]},
+        "step_gbps": (nb["conv"] + nb["step_norm"]) / step_us / 1e3,
+        "roofline": {"bound": "hbm", "kernel": "decode_multi_kernel<fused norm>", "achieved": gbps,
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": gbps / HBM_PEAK_GBPS}}
+    log(f"ragged: conv {us['conv']:.1f} us, recurrence {us['recurrence']:.1f} us = {gbps:.0f} GB/s")
+    return out
+
+
+def trace_summary(path: str, skip: int):
+    """Per-kernel dispatch durations from a rocprofv3 kernel trace (csv): the first `skip`
+    dispatches of each kernel (warm-up) are dropped, and the count, median, mean, min and
+    max of the rest are printed, one kernel per line, longest median first.  Kernels
+    with the same name and grid are one group."""
+    import csv
+    import statistics
+    groups = {}
+    with open(path, newline="") as f:
+        for row in csv.DictReader(f):
+            if row.get("Kind", "KERNEL_DISPATCH") != "KERNEL_DISPATCH":
+                continue
+            key = (row["Kernel_Name"], row.get("Grid_Size_X", ""), row.get("Grid_Size_Y", ""))
+            groups.setdefault(key, []).append((int(row["Start_Timestamp"]),
+                                               (int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) / 1000.0))
+    lines = []
+    for (name, gx, gy), rows in groups.items():
+        rows.sort()
+        us = [d for _, d in rows[skip:]]
+        if not us:
+            continue
+        lines.append((statistics.median(us), f"{statistics.median(us):11.1f} us median  {statistics.mean(us):9.1f} mean  "
+                                             f"{min(us):9.1f} min  {max(us):9.1f} max  x{len(us):<4d} (of {len(rows)})  "
+                                             f"grid {gx}x{gy}  {name}"))
+    for _, line in sorted(lines, reverse=True):
+        print(line)
+
+
 def main():
+    if len(sys.argv) > 1 and sys.argv[1] == "--trace-summary":
+        tp = argparse.ArgumentParser()
+        tp.add_argument("--trace-summary", required=True, help="a rocprofv3 kernel_trace.csv")
+        tp.add_argument("--skip", type=int, default=0, help="warm-up dispatches of each kernel to drop")
+        a = tp.parse_args()
+        trace_summary(a.trace_summary, a.skip)
+        return
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
@@ -442,6 +661,8 @@ def main():
                          "launch and the two launches, for kernel traces, instead of the step")
     ap.add_argument("--event-every", type=int, default=8,
                     help="record per-kernel HIP events on every N-th timed step")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the per-workload blocks (tiny, b64, b256, prefill, ragged) after the headline")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -635,6 +856,8 @@ def main():
         f"; {three_ms * 1000:.1f} us/step; recurrence kernel {three_step_gbps:.0f} GB/s; d2d copy {copy_gbps:.0f} GB/s")
     traffic = read_traffic() if args.config == "b256" else None
 
+    configs = None if args.no_configs else config_blocks(G, W, stream, args.steps, args.warmup)
+
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the oracle on the host cores ...")
@@ -687,6 +910,7 @@ def main():
                      "event_timing": ("one event pair around all timed launches" if single else
                                       "events around the kernels of every sampled step")},
         "gpu_clocks_during_timing": clocks.get("step_one" if single else "step_fused"),
+        "configs": configs,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
