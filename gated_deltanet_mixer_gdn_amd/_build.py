@@ -9,7 +9,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libgdn_hip.so")
-SOURCES = ["gdn_conv.hip", "gdn_recurrence.hip", "gdn_norm.hip", "gdn_proj.hip", "gdn_gemm.hip", "gdn_api.cpp"]
+SOURCES = ["gdn_conv.hip", "gdn_recurrence.hip", "gdn_norm.hip", "gdn_proj.hip", "gdn_gemm.hip", "gdn_noalloc.hip", "gdn_api.cpp"]
 
 # gfx950 only.  Packed fp32 instructions are switched off for device code (the
 # host pass ignores the feature with a warning).

@@ -120,6 +120,13 @@ int launched(hipError_t e, const char* fn) {
 
 }  // namespace
 
+namespace gdn {
+int set_last_error(int code, const char* fn, const char* msg) {
+    if (code == GDN_OK) return ok();
+    return fail(code, fn, "%s", msg);
+}
+}  // namespace gdn
+
 extern "C" {
 
 int gdn_abi_version(void) { return GDN_ABI_VERSION; }

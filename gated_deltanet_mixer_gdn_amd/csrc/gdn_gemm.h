@@ -77,6 +77,10 @@ long long gemm_workgroups(const GemmParams& p, const GemmConfig& c);
 // bytes of GemmParams::ws a launch of shape c needs (0 when c.parts == 1)
 long long gemm_workspace_bytes(const GemmParams& p, const GemmConfig& c);
 
+// Sets the message gdn_last_error() returns on this host thread (cleared for GDN_OK)
+// and returns code; for C-ABI entry points defined outside gdn_api.cpp.
+int set_last_error(int code, const char* fn, const char* msg);
+
 hipError_t launch_split_bf16(const SplitParams& p, hipStream_t stream);
 hipError_t launch_pack_bf16(const PackParams& p, hipStream_t stream);
 hipError_t launch_project_bf16(const GemmParams& p, const GemmConfig& c, hipStream_t stream);

@@ -25,7 +25,7 @@ EXPORTS = (
     "gdn_gated_rmsnorm",
     "gdn_ab_project", "gdn_split_bf16_bytes", "gdn_pack_bf16_bytes", "gdn_split_bf16", "gdn_pack_bf16",
     "gdn_project_bf16", "gdn_project2_bf16", "gdn_project_workspace_bytes", "gdn_project_multi_bf16",
-    "gdn_check_slots",
+    "gdn_check_slots", "gdn_project_bf16_noalloc",
 )
 
 
@@ -107,6 +107,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "gdn_project_bf16": ([vp, vp, i64, i32, i32, vp, vp, i64, vp], ctypes.c_int),
         "gdn_project_workspace_bytes": ([i64, i32, i32], ctypes.c_int64),
         "gdn_project_multi_bf16": ([vp, vp, i64, i32, i32, vp, vp, vp, i64, vp], ctypes.c_int),
+        "gdn_project_bf16_noalloc": ([vp, vp, i64, i32, i32, vp, vp], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -483,6 +484,19 @@ def gdn_project_bf16(xs: SplitX, wp: PackedW, out=None, workspace=None):
     ws, ws_bytes, _keep = _workspace(xs.rows, xs.k, wp.n, xs.data.device, workspace)
     _check(load_library().gdn_project_bf16(xs.data.data_ptr(), wp.data.data_ptr(), xs.rows, xs.k, wp.n,
                                            _f32(out, "out"), ws, ws_bytes, _stream(xs.data)))
+    return out
+
+
+def gdn_project_bf16_noalloc(xs: SplitX, wp: PackedW, out):
+    """gdn_project_bf16 without a workspace or any allocation: a k-split launch keeps its
+    partial blocks in the library's own per-GPU scratch buffer (GDN_PROJECT_SCRATCH_BYTES;
+    larger needs raise GdnError).  out [rows][n] fp32 must be given."""
+    if xs.k != wp.k:
+        raise ValueError(f"x has k={xs.k}, w has k={wp.k}")
+    if out is None or out.numel() != xs.rows * wp.n:
+        raise ValueError(f"out must be given and hold {xs.rows * wp.n} elements")
+    _check(load_library().gdn_project_bf16_noalloc(xs.data.data_ptr(), wp.data.data_ptr(), xs.rows, xs.k, wp.n,
+                                                   _f32(out, "out"), _stream(xs.data)))
     return out
 
 

@@ -348,6 +348,26 @@ int gdn_project_multi_bf16(const uint16_t* xs, const uint16_t* wp, int64_t rows,
                            const int32_t* cols, float* const* outs, void* workspace, int64_t workspace_bytes,
                            void* stream);
 
+/* Bytes of the library's own scratch buffer that gdn_project_bf16_noalloc uses, on
+ * each GPU the library runs on. */
+#define GDN_PROJECT_SCRATCH_BYTES (4u << 20)
+
+/* gdn_project_bf16 for callers that cannot allocate device memory or hand in a
+ * workspace: code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation.  Same operands, result and errors as gdn_project_bf16 (bit for bit the
+ * same output for the same shape), except that a launch which splits its k range over
+ * workgroups keeps its partial blocks in a scratch buffer of GDN_PROJECT_SCRATCH_BYTES
+ * that the library owns, one per GPU, held from the first call on that GPU until the
+ * process ends.  A shape whose gdn_project_workspace_bytes exceeds it is GDN_ERR_ARG
+ * (at the pages' sizes the out projection, 6144 -> 2560, needs 0.94 MiB at up to 32
+ * rows and none above; the qkv and z projections need none).  The call allocates
+ * nothing.  Every call on one GPU shares that GPU's buffer: calls ordered on one
+ * stream are safe, calls that may run at the same time on one GPU (other streams, no
+ * ordering between them) race.  Each launch writes every partial block before reading
+ * it, so the buffer's old contents never matter. */
+int gdn_project_bf16_noalloc(const uint16_t* xs, const uint16_t* wp, int64_t rows, int32_t k, int32_t n,
+                             float* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif
