@@ -271,14 +271,10 @@ int conv_common(const char* fn, gdn_pool* p, const int32_t* slots, const int32_t
     if (T < 1) return fail(GDN_ERR_ARG, fn, "T=%d must be >= 1", T);
     if (!(eps >= 0.0f) || !std::isfinite(eps)) return fail(GDN_ERR_ARG, fn, "eps must be finite and >= 0");
     if (B == 0) return ok();
-    // shorter token blocks while the call has fewer than 4 workgroups per CU (a short
-    // call is latency-bound: more blocks put more of its tokens in flight at once)
-    const int head_blocks = (2 * p->g.h_k + p->g.h_v + 15) / 16;
-    int tpb = gdn::kConvTokensPerBlock;
-    while (tpb > gdn::kConvMinTokensPerBlock && (int64_t) B * ((T + tpb - 1) / tpb) * head_blocks < 1024)
-        tpb /= 2;
-    const int n_tb = (T + tpb - 1) / tpb;
-    if ((int64_t) B * n_tb > INT32_MAX) return fail(GDN_ERR_ARG, fn, "B*T too large");
+    const int group = T >= gdn::kConvGroup ? gdn::kConvGroup : T >= 2 ? 4 : 1;
+    const int n_groups = (T + group - 1) / group;
+    const int64_t head_blocks = (2 * p->g.h_k + p->g.h_v + gdn::kConvHeadsPerBlock - 1) / gdn::kConvHeadsPerBlock;
+    if ((int64_t) B * n_groups * head_blocks > INT32_MAX) return fail(GDN_ERR_ARG, fn, "B*T too large");
     if (int rc = check_f4(qkv, fn, "qkv")) return rc;
     if (int rc = check_f4(conv_w, fn, "conv_w")) return rc;
     if (int rc = check_f4(h, fn, "h")) return rc;
@@ -302,9 +298,10 @@ int conv_common(const char* fn, gdn_pool* p, const int32_t* slots, const int32_t
     c.T = T;
     c.h_k = p->g.h_k;
     c.n_heads = 2 * p->g.h_k + p->g.h_v;
-    c.n_tb = n_tb;
-    c.tpb = tpb;
+    c.n_groups = n_groups;
+    c.group = group;
     c.persist = persist ? 1 : 0;
+    c.stream_h = (int64_t) B * T * channels(p->g) * (int64_t) sizeof(float) >= gdn::kConvStreamBytes ? 1 : 0;
     c.eps = eps;
     c.qscale = p->g.scale_after_readout ? 1.0f : 1.0f / std::sqrt((float) p->g.s);
     if (built) {

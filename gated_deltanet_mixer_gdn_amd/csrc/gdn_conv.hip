@@ -5,14 +5,26 @@ namespace gdn {
 
 // ------------------------------------------------------------------ conv + SiLU + L2
 //
-// grid.x = B * n_tb (sequence, token block of tpb tokens),
-// grid.y = ceil(n_heads / 16); 256 threads.  A 16-lane row (one DPP row) owns one
-// 128-channel head: lane l has the channel groups 4l..4l+3 and 64+4l..64+4l+3, so
-// every load and store instruction of the row covers 256 contiguous bytes and the
-// head's L2 norm is a 16-lane DPP sum.  Inputs are loaded three tokens ahead.  Only
-// token block 0 reads or writes the stored history; later blocks take their first
-// three history entries from qkv, so blocks never race on it.  persist = 0 leaves
-// the stored history as it was (a speculative window).
+// The conv reads only raw inputs (the stored history and qkv rows), so its tokens are
+// independent and the kernel is laid out as a flat stream over (sequence, token group,
+// head block): one 256-thread workgroup takes G consecutive tokens of 8 heads of one
+// sequence, and consecutive workgroups take the next head block, then the next token
+// group, so the chip sweeps qkv and h in address order (a token-by-token walk per
+// workgroup scatters the concurrent accesses and moved the same bytes about 20% slower
+// on MI355X).  The workgroup id is remapped so each XCD sweeps one contiguous range,
+// where the three rows before a group, which the group before it also read, are still
+// in that XCD's L2.
+//
+// A half-wave (32 lanes) owns one 128-channel head: lane l has the four channels
+// 4l..4l+3.  The L2 norm of a q or k head is summed in the order of the single-launch
+// decode's prologue (lane l < 16 and lane l + 16 hold the channel groups that prologue
+// gives one lane, so their sums of squares are added first, then the 16-lane tree),
+// which keeps h bit for bit equal across the two forms.
+//
+// Only token group 0 of a sequence reads or writes the stored history (and advances it
+// first for a commit); later groups take their three history entries from the qkv rows
+// before them, so groups never race on it.  persist = 0 leaves the stored history as it
+// was (a speculative window).
 // advance_history for channels c..c+3 that also leaves the new history in g
 __device__ __forceinline__ void advance_and_keep(ConvGroup& g, float* X, const float* xq, long long C, long long c,
                                                  int nt) {
@@ -27,116 +39,86 @@ __device__ __forceinline__ void advance_and_keep(ConvGroup& g, float* X, const f
     ConvGroup::store_history(X + c * kHist, g.x3, g.x2, g.x1);
 }
 
+template <int G>
 __global__ __launch_bounds__(256) void conv_silu_norm_kernel(ConvParams p) {
     const int tid = threadIdx.x;
-    const int head = blockIdx.y * 16 + (tid >> 4);
-    if (head >= p.n_heads) return;  // whole 16-lane rows leave together
-    const int l = tid & 15;
-    const int b = blockIdx.x / p.n_tb;
-    const int tb = blockIdx.x - b * p.n_tb;
+    const unsigned nwg = gridDim.x;
+    unsigned wid = blockIdx.x;
+    if ((nwg & 7u) == 0) wid = (wid & 7u) * (nwg >> 3) + (wid >> 3);
+    const int n_hb = (p.n_heads + kConvHeadsPerBlock - 1) / kConvHeadsPerBlock;
+    const int hb = (int) (wid % (unsigned) n_hb);
+    const int grp = (int) ((wid / (unsigned) n_hb) % (unsigned) p.n_groups);
+    const int b = (int) (wid / ((unsigned) n_hb * (unsigned) p.n_groups));
+    const int head = hb * kConvHeadsPerBlock + (tid >> 5);
+    if (head >= p.n_heads) return;  // whole half-waves leave together
     const long long C = (long long) p.n_heads * kS;
-    const long long ca = (long long) head * kS + 4 * l;
-    const long long cb = ca + 64;
-    const int t0 = tb * p.tpb;
-    const int t1 = min(t0 + p.tpb, p.T);
+    const long long c = (long long) head * kS + 4 * (tid & 31);
+    const int t0 = grp * G;
+    const int t1 = min(t0 + G, p.T);
     const float* xq = p.qkv + (long long) b * p.T * C;   // this sequence's qkv rows
     float* hq = p.h + (long long) b * p.T * C;
-    const bool reporter = (tid == 0 && blockIdx.y == 0 && tb == 0);
+    const bool reporter = (tid == 0 && hb == 0 && grp == 0);
 
     const int slot = read_slot(p.slots, b, p.n_slots, p.flags, reporter);
     int nt = read_ntok(p.n_tok, b, p.T, p.flags, reporter);
     if (slot < 0) nt = 0;  // unknown slot: no history to read or advance, outputs zero
     const int t_end = min(t1, nt);
 
-    ConvGroup ga, gb;
+    ConvGroup g;
     float* X = p.conv + ((long long) (slot < 0 ? 0 : slot) * C) * kHist;
     bool advanced = false;
-    if (p.adv_qkv && tb == 0 && slot >= 0) {
+    if (p.adv_qkv && grp == 0 && slot >= 0) {
         // the commit of the previous window comes first: its kept rows advance the
         // stored history (kept whatever this call's tokens do), and token 0 below
         // starts from the advanced history, kept in registers
         const int na = read_ntok(p.n_adv, b, p.adv_T, p.flags, reporter);
         if (na > 0) {
-            const float* xa = p.adv_qkv + (long long) b * p.adv_T * C;
-            advance_and_keep(ga, X, xa, C, ca, na);
-            advance_and_keep(gb, X, xa, C, cb, na);
+            advance_and_keep(g, X, p.adv_qkv + (long long) b * p.adv_T * C, C, c, na);
             advanced = true;
         }
     }
-    // inputs of tokens t, t + 1 and t + 2, loaded ahead
-    f4 xa_1 = {0.f, 0.f, 0.f, 0.f}, xb_1 = xa_1, xa_2 = xa_1, xb_2 = xa_1, xa_3 = xa_1, xb_3 = xa_1;
     if (t_end > t0) {
-        ga.load_taps(p.w, ca);
-        gb.load_taps(p.w, cb);
+        g.load_taps(p.w, c);
         if (t0 == 0) {
-            if (!advanced) {
-                ga.load_history(X + ca * kHist);
-                gb.load_history(X + cb * kHist);
-            }
+            if (!advanced) g.load_history(X + c * kHist);
         } else {
-            ga.x3 = *(const f4*) (xq + (t0 - 3) * C + ca);
-            ga.x2 = *(const f4*) (xq + (t0 - 2) * C + ca);
-            ga.x1 = *(const f4*) (xq + (t0 - 1) * C + ca);
-            gb.x3 = *(const f4*) (xq + (t0 - 3) * C + cb);
-            gb.x2 = *(const f4*) (xq + (t0 - 2) * C + cb);
-            gb.x1 = *(const f4*) (xq + (t0 - 1) * C + cb);
+            g.x3 = *(const f4*) (xq + (t0 - 3) * C + c);
+            g.x2 = *(const f4*) (xq + (t0 - 2) * C + c);
+            g.x1 = *(const f4*) (xq + (t0 - 1) * C + c);
         }
-        xa_1 = *(const f4*) (xq + t0 * C + ca);
-        xb_1 = *(const f4*) (xq + t0 * C + cb);
-        if (t0 + 1 < t_end) {
-            xa_2 = *(const f4*) (xq + (t0 + 1) * C + ca);
-            xb_2 = *(const f4*) (xq + (t0 + 1) * C + cb);
+        // the group's inputs, all in flight at once; slots past the last token re-read
+        // that token's row (in bounds, and no branch around a load, so the array stays
+        // in registers)
+        f4 x[G];
+#pragma unroll
+        for (int u = 0; u < G; ++u) x[u] = *(const f4*) (xq + min(t0 + u, t_end - 1) * C + c);
+        const bool normed = head < 2 * p.h_k;
+        const float extra = head < p.h_k ? p.qscale : 1.0f;
+#pragma unroll
+        for (int u = 0; u < G; ++u) {
+            if (t0 + u >= t_end) break;   // the same in every lane of the workgroup
+            const f4 uu = g.step(x[u]);
+            f4 hv = uu * sigmoid4(uu);
+            if (normed) {
+                // lanes l and l ^ 16 hold the prologue's two channel groups of one lane
+                const float ss = add_xor8(block8_sum(add_xor16(sumsq4(hv))));
+                hv *= extra / sqrtf(ss + p.eps);
+            }
+            f4* dst = (f4*) (hq + (t0 + u) * C + c);
+            if (p.stream_h) __builtin_nontemporal_store(hv, dst);
+            else *dst = hv;
         }
-        if (t0 + 2 < t_end) {
-            xa_3 = *(const f4*) (xq + (t0 + 2) * C + ca);
-            xb_3 = *(const f4*) (xq + (t0 + 2) * C + cb);
-        }
-    }
-
-    const bool normed = head < 2 * p.h_k;
-    const float extra = head < p.h_k ? p.qscale : 1.0f;
-    for (int t = t0; t < t_end; ++t) {
-        const f4 xa = xa_1, xb = xb_1;
-        xa_1 = xa_2;
-        xb_1 = xb_2;
-        xa_2 = xa_3;
-        xb_2 = xb_3;
-        if (t + 3 < t_end) {
-            xa_3 = *(const f4*) (xq + (t + 3) * C + ca);
-            xb_3 = *(const f4*) (xq + (t + 3) * C + cb);
-        }
-        const f4 ua = ga.step(xa);
-        const f4 ub = gb.step(xb);
-        f4 ha = ua * sigmoid4(ua);
-        f4 hb = ub * sigmoid4(ub);
-        if (normed) {
-            const float ss = add_xor8(block8_sum(sumsq4(ha) + sumsq4(hb)));
-            const float sc = extra / sqrtf(ss + p.eps);
-            ha *= sc;
-            hb *= sc;
-        }
-        *(f4*) (hq + t * C + ca) = ha;
-        *(f4*) (hq + t * C + cb) = hb;
     }
     const f4 zero = {0.f, 0.f, 0.f, 0.f};
-    for (int t = max(t0, nt); t < t1; ++t) {
-        *(f4*) (hq + t * C + ca) = zero;
-        *(f4*) (hq + t * C + cb) = zero;
-    }
+    for (int t = max(t0, nt); t < t1; ++t) *(f4*) (hq + t * C + c) = zero;
 
     if (t0 == 0 && nt > 0 && p.persist) {
         // the new history is the last three entries of (stored history, tokens 0..nt-1)
-        if (nt <= t1) {
-            ConvGroup::store_history(X + ca * kHist, ga.x3, ga.x2, ga.x1);
-            ConvGroup::store_history(X + cb * kHist, gb.x3, gb.x2, gb.x1);
-        } else {  // nt > t1 >= 3: all three come from qkv
-            for (int g = 0; g < 2; ++g) {
-                const long long c = g ? cb : ca;
-                ConvGroup::store_history(X + c * kHist, *(const f4*) (xq + (nt - 3) * C + c),
-                                         *(const f4*) (xq + (nt - 2) * C + c),
-                                         *(const f4*) (xq + (nt - 1) * C + c));
-            }
-        }
+        if (nt <= t1)
+            ConvGroup::store_history(X + c * kHist, g.x3, g.x2, g.x1);
+        else  // nt > t1 >= 3: all three come from qkv
+            ConvGroup::store_history(X + c * kHist, *(const f4*) (xq + (nt - 3) * C + c),
+                                     *(const f4*) (xq + (nt - 2) * C + c), *(const f4*) (xq + (nt - 1) * C + c));
     }
 }
 
@@ -169,8 +151,14 @@ __global__ __launch_bounds__(256) void zero_kernel(ZeroParams p) {
 
 // ------------------------------------------------------------------ launch
 hipError_t launch_conv_silu_norm(const ConvParams& p, hipStream_t stream) {
-    const dim3 grid((unsigned) ((long long) p.B * p.n_tb), (unsigned) ((p.n_heads + 15) / 16));
-    hipLaunchKernelGGL(conv_silu_norm_kernel, grid, dim3(256), 0, stream, p);
+    const long long n_hb = (p.n_heads + kConvHeadsPerBlock - 1) / kConvHeadsPerBlock;
+    const dim3 grid((unsigned) ((long long) p.B * p.n_groups * n_hb));
+    switch (p.group) {
+    case 1: hipLaunchKernelGGL(conv_silu_norm_kernel<1>, grid, dim3(256), 0, stream, p); break;
+    case 4: hipLaunchKernelGGL(conv_silu_norm_kernel<4>, grid, dim3(256), 0, stream, p); break;
+    case kConvGroup: hipLaunchKernelGGL(conv_silu_norm_kernel<kConvGroup>, grid, dim3(256), 0, stream, p); break;
+    default: return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 

@@ -14,13 +14,14 @@ namespace gdn {
 constexpr int kS = 128;
 constexpr int kDConv = 4;
 constexpr int kHist = kDConv - 1;
-// Tokens of one sequence handled by one conv workgroup (>= kHist, so only the
-// first token block of a sequence ever reads or writes the stored conv history).
-// Tokens per conv workgroup: 32, or fewer (down to 4) when a call has too few
-// (sequence, token block) pairs to fill the chip.  At least 3, so a later block takes
-// its whole history from qkv and never reads the stored one.
-constexpr int kConvTokensPerBlock = 32;
-constexpr int kConvMinTokensPerBlock = 4;
+// The conv kernel: 128-channel heads per 256-thread workgroup (one per half-wave), and
+// the consecutive tokens of one sequence a workgroup takes (kConvGroup for calls of
+// 8 tokens or more, 4 for 2 to 7, 1 for single-token calls).  h is written with
+// streaming stores from kConvStreamBytes of output up (a stream that large will not
+// stay in the caches for the next kernel anyway).
+constexpr int kConvHeadsPerBlock = 8;
+constexpr int kConvGroup = 8;
+constexpr long long kConvStreamBytes = 64LL << 20;
 // Rows (value heads x tokens) per gated-RMSNorm workgroup: one half-wave per row.
 constexpr int kNormRowsPerBlock = 8;
 
@@ -34,9 +35,10 @@ struct ConvParams {
     uint32_t* flags;        // pool flag word
     long long n_slots;
     int B, T, h_k, n_heads; // n_heads = 2*h_k + h_v (128-channel heads)
-    int n_tb;               // token blocks per sequence
-    int tpb;                // tokens per block (kConvMinTokensPerBlock..kConvTokensPerBlock)
+    int n_groups;           // token groups per sequence, ceil(T / group)
+    int group;              // tokens per group: 1, 4 or kConvGroup
     int persist;            // 0: leave the stored history untouched (speculative window)
+    int stream_h;           // 1: h written with streaming (non-temporal) stores
     float eps, qscale;
     // a commit first (else null): the stored history advances by the first n_adv[b] raw
     // rows of adv_qkv [B][adv_T][C] and is stored, and this call's tokens start from it
