@@ -384,7 +384,38 @@ constexpr int kNormChunk = 8;
 struct MultiLds {
     f4 qk[4][64];                        // per wave: q as 32 float4, then k as 32 float4
     f4 o_ring[2][kNormChunk][32];        // [chunk parity][token][float4 column group]
+    f4 qk_next[4][2][64];                // per wave: q|k of its two tokens of the next chunk
+    float kq[2][kNormChunk];             // [chunk parity][token]: k . q of the chunk's tokens
+    f2 gate[4][64];                      // per wave: (beta, e^g) of the 64 tokens of a round
 };
+
+// A pointer into LDS (address space 3): its integer value is the 32-bit LDS address,
+// unlike a generic pointer to shared memory, whose high bits hold the LDS aperture.
+template <typename X>
+using lds_ptr = __attribute__((address_space(3))) X*;
+
+// A raw buffer descriptor over memory from `base` on (gfx9 data format word); the
+// per-token loads and stores below address it with a lane-constant byte offset, so a new
+// token moves only the scalar base.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_at(const void* base) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, -1, 0x00020000);
+}
+__device__ __forceinline__ f4 buffer_load_f4(const void* base, unsigned byte_off) {
+    typedef unsigned u4 __attribute__((ext_vector_type(4)));
+    const u4 v = __builtin_amdgcn_raw_buffer_load_b128(buffer_at(base), (int) byte_off, 0, 0);
+    return f4{__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w)};
+}
+__device__ __forceinline__ float buffer_load_f1(const void* base, unsigned byte_off) {
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(buffer_at(base), (int) byte_off, 0, 0));
+}
+__device__ __forceinline__ void buffer_store_f4(f4 v, void* base, unsigned byte_off) {
+    typedef unsigned u4 __attribute__((ext_vector_type(4)));
+    const u4 u = {__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z), __float_as_uint(v.w)};
+    __builtin_amdgcn_raw_buffer_store_b128(u, buffer_at(base), (int) byte_off, 0, 0);
+}
+__device__ __forceinline__ void buffer_store_f1(float v, void* base, unsigned byte_off) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), buffer_at(base), (int) byte_off, 0, 0);
+}
 
 // The token loop of the multi-token recurrence for head (job.b, job.i): tokens 0..nt-1
 // of the inputs p describes (rows of h, alpha, beta_logit and z of sequence job.b, T
@@ -393,10 +424,19 @@ struct MultiLds {
 // keep_state = false: the caller discards s[] afterwards (a speculative window), so
 // the last token's state update is skipped; its outputs come from the old state in
 // the one-pass form, so they do not change.
-template <bool kNorm>
-__device__ __forceinline__ void multi_tokens(const StepParams& p, const HeadJob& job, int nt, f4 (&s)[16],
+// The loop runs in rounds of 64 tokens (one evaluation of beta and e^g per lane, parked
+// in the wave's LDS) of kNormChunk-token chunks, unrolled, so a token's slots in LDS are
+// immediates; the token count and the row bases are wave-uniform, so loop control and
+// addressing stay in scalar registers.  With the norm (kNorm), the workgroup meets once
+// per chunk anyway, and for a sequence of more than one chunk each wave also forms there
+// k . q of two tokens of the next chunk (wave_kq on the same staged rows, so the same
+// bits), which the chunk then reads from LDS instead of every wave forming it for every
+// token (kChunkKq: the kernels that store the state after long calls; a single chunk
+// keeps the per-token form, as the extra round trip before its first token would cost
+// more than it saves).
+template <bool kNorm, bool kChunkKq>
+__device__ __forceinline__ void multi_tokens(const StepParams& p, const HeadJob& job, int nt_in, f4 (&s)[16],
                                              MultiLds& lds, bool keep_state) {
-    f4 (&qk_lds)[4][64] = lds.qk;
     f4 (&o_ring)[2][kNormChunk][32] = lds.o_ring;
 
     const int tid = threadIdx.x;
@@ -406,110 +446,184 @@ __device__ __forceinline__ void multi_tokens(const StepParams& p, const HeadJob&
     const int rg = lane >> 3;
     const int col = wave * 32 + cg * 4;
     const int i = job.i;
+    const int nt = __builtin_amdgcn_readfirstlane(nt_in);   // one sequence per workgroup
     const long long C = (long long) (2 * p.h_k + p.h_v) * kS;
     const long long tok0 = (long long) job.b * p.T;
-    const long long q_off = (long long) job.j * kS + (lane & 31) * 4 + (lane < 32 ? 0 : (long long) p.h_k * kS);
-    const long long v_off = (long long) (2 * p.h_k + i) * kS + col;
-    // chunk normalisation: this thread's token within a chunk and columns
-    const int n_tt = tid >> 5;
-    const int n_c4 = (tid & 31) * 4;
+    const long long row_hv = (long long) p.h_v * kS;   // one token's o, z or y row
     // the column of its 4 whose q sum a lane ends with after scatter_sum4
     const int oc = (int) (scatter_sum4(f4{0.f, 1.f, 2.f, 3.f}) * 0.25f);
     const bool reads_out = (lane & 8) == 0;
+    // byte offsets inside one token's row of h, and of o
+    const unsigned q_off = 4u * (unsigned) (job.j * kS + (lane & 31) * 4 + (lane < 32 ? 0 : p.h_k * kS));
+    const unsigned v_off = 4u * (unsigned) ((2 * p.h_k + i) * kS + col + oc);
+    const unsigned o_off = 4u * (unsigned) (col + oc);
+    const float* h_seq = p.h + tok0 * C;
+    float* o_seq = p.o ? p.o + (tok0 * p.h_v + i) * kS : nullptr;
+    // chunk normalisation: this thread's token within a chunk and columns
+    const int n_tt = tid >> 5;
+    const int n_c4 = (tid & 31) * 4;
+    const float* z_seq = kNorm ? p.z + (tok0 * p.h_v + i) * kS : nullptr;
+    float* y_seq = kNorm ? p.y + (tok0 * p.h_v + i) * kS : nullptr;
+    const unsigned zy_off = 4u * (unsigned) n_c4;
 
     const float dt_i = p.dt[i];
     const float a_i = p.ssm_a[i];
+    const int last = nt - 1;
+    const bool chunk_kq_on = kNorm && kChunkKq && nt > kNormChunk;   // uniform over the workgroup
 
-    // q|k and v of the next token, loaded one token ahead
+    // q|k and v of the next token, loaded one token ahead (past the last token: the
+    // last token's row again, so no branch sits around the loads)
     f4 qk_n = {0.f, 0.f, 0.f, 0.f};
     float v_n = 0.f;   // v of the one column (col + oc) whose delta this lane forms
     auto fetch = [&](int t) {
-        const float* ht = p.h + (tok0 + t) * C;
-        qk_n = *(const f4*) (ht + q_off);
-        v_n = ht[v_off + oc];
+        const float* ht = h_seq + min(t, last) * C;
+        qk_n = buffer_load_f4(ht, q_off);
+        v_n = buffer_load_f1(ht, v_off);
     };
-    // beta and the decay e^g are the same for the whole head: lane l evaluates them for
-    // token t0 + l of a 64-token window, and each token reads its pair with readlane
-    float beta_w = 0.f, eg_w = 0.f;
-    auto gates = [&](int t0) {
-        if (t0 + lane < nt) {
-            const long long e = (tok0 + t0 + lane) * p.h_v + i;
-            beta_w = sigmoid_f(p.beta_logit[e]);
-            eg_w = expf(softplus_f(p.alpha[e] + dt_i) * a_i);
+    // z of this thread's token in the chunk after the current one, loaded one chunk ahead
+    f4 z_n = {0.f, 0.f, 0.f, 0.f};
+    auto fetch_z = [&](int t0c) { z_n = buffer_load_f4(z_seq + min(t0c + n_tt, last) * row_hv, zy_off); };
+    // q|k of this wave's two tokens (2 wave, 2 wave + 1) of the chunk after the current one
+    f4 qkp0 = {0.f, 0.f, 0.f, 0.f}, qkp1 = qkp0;
+    auto fetch_qkp = [&](int t0c) {
+        qkp0 = buffer_load_f4(h_seq + min(t0c + 2 * wave, last) * C, q_off);
+        qkp1 = buffer_load_f4(h_seq + min(t0c + 2 * wave + 1, last) * C, q_off);
+    };
+    // k . q of those two tokens, into kq[par]; the caller's barrier publishes them
+    auto chunk_kq = [&](int par) {
+        lds.qk_next[wave][0][lane] = qkp0;
+        lds.qk_next[wave][1][lane] = qkp1;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        const float k0 = wave_kq((const float*) lds.qk_next[wave][0], lane);
+        const float k1 = wave_kq((const float*) lds.qk_next[wave][1], lane);
+        if (lane == 0) {
+            lds.kq[par][2 * wave] = k0;
+            lds.kq[par][2 * wave + 1] = k1;
         }
     };
-    // z of this thread's token in the next chunk, loaded one chunk ahead
-    f4 z_n = {0.f, 0.f, 0.f, 0.f};
-    auto fetch_z = [&](int t0c) {
-        if (t0c + n_tt < nt) z_n = *(const f4*) (p.z + ((tok0 + t0c + n_tt) * p.h_v + i) * kS + n_c4);
+    // the gated RMSNorm of the first n tokens of the chunk that starts at token tc, from
+    // o parked in ring parity par; z of the chunk is in zz
+    auto norm_chunk = [&](int tc, int par, int n, f4 zz) {
+        if (n_tt < n) {   // whole half-waves, as halfwave_sum needs
+            const f4 o4 = o_ring[par][n_tt][n_c4 / 4];
+            const float inv = rms_inv(halfwave_sum(sumsq4(o4)), p.eps);
+            const f4 wn = *(const f4*) (p.norm_w + n_c4);
+            buffer_store_f4(o4 * inv * wn * gate4(zz, p.gate_silu), y_seq + (tc + n_tt) * row_hv, zy_off);
+        }
     };
     if (nt > 0) {
         fetch(0);
         if (kNorm) fetch_z(0);
+        if (chunk_kq_on) {
+            fetch_qkp(0);
+            chunk_kq(0);
+            fetch_qkp(kNormChunk);
+            __syncthreads();
+        }
     }
 
-    f4* buf = qk_lds[wave];
+    f4* buf = lds.qk[wave];
     const float* qrow = (const float*) buf + rg * 16;
     const float* krow = (const float*) buf + kS + rg * 16;
-    for (int t = 0; t < nt; ++t) {
-        if ((t & 63) == 0) gates(t);
-        const float beta = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(beta_w), t & 63));
-        const float eg = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(eg_w), t & 63));
-        buf[lane] = qk_n;
-        const float vc = v_n;
-        if (t + 1 < nt) fetch(t + 1);
-        // the staging above is wave-private: order it against this wave's reads
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-
-        f4 pk = {0.f, 0.f, 0.f, 0.f}, pq = pk;
-#pragma unroll
-        for (int m = 0; m < 16; ++m) {
-            pk = fma4(s[m], krow[m], pk);
-            pq = fma4(s[m], qrow[m], pq);
+    const float* ring_lane = (const float*) o_ring + wave * 32 + cg * 4 + oc;
+    for (int tg = 0; tg < nt; tg += 64) {
+        // beta and the decay e^g are the same for the whole head: lane l evaluates them
+        // for token tg + l into the wave's LDS, and each token reads its pair back
+        {
+            f2 ge = {0.f, 0.f};
+            if (tg + lane < nt) {
+                const long long e = (tok0 + tg + lane) * p.h_v + i;
+                ge.x = sigmoid_f(p.beta_logit[e]);
+                ge.y = expf(softplus_f(p.alpha[e] + dt_i) * a_i);
+            }
+            lds.gate[wave][lane] = ge;
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         }
-        const float kq = wave_kq((const float*) buf, lane);
-        // column sums over the 8 row groups of the wave (lane bits 3..5):
-        // ((g0+g1)+(g2+g3))+((g4+g5)+(g6+g7)), as in the single-token kernel
-        const float pkc = scatter_sum4(add_xor8(pk));
-        const float pqc = scatter_sum4(add_xor8(pq));
-        // delta of column col + oc, then of all 4 columns for the update
-        const float dc = beta * __builtin_fmaf(-eg, pkc, vc);
-        const f4 d = gather4(dc);
-        // the readout of column col + oc (a scale of 1 multiplies exactly)
-        const float out = __builtin_fmaf(kq, dc, eg * pqc) * p.oscale;
-        if (p.o && reads_out) p.o[((tok0 + t) * p.h_v + i) * kS + col + oc] = out;
-        if (kNorm) {
-            const int par = (t / kNormChunk) & 1;
-            const int slot8 = t % kNormChunk;
-            if (reads_out) ((float*) o_ring[par][slot8])[wave * 32 + cg * 4 + oc] = out;
-            if (slot8 == kNormChunk - 1 || t == nt - 1) {   // uniform over the workgroup
-                __syncthreads();
-                const int t0c = t - slot8;
-                const f4 zz = z_n;
-                if (t0c + kNormChunk < nt) fetch_z(t0c + kNormChunk);
-                if (n_tt <= slot8) {   // whole half-waves, as halfwave_sum needs
-                    const f4 o4 = o_ring[par][n_tt][n_c4 / 4];
-                    const float inv = rms_inv(halfwave_sum(sumsq4(o4)), p.eps);
-                    const f4 wn = *(const f4*) (p.norm_w + n_c4);
-                    *(f4*) (p.y + ((tok0 + t0c + n_tt) * p.h_v + i) * kS + n_c4) =
-                        o4 * inv * wn * gate4(zz, p.gate_silu);
+        const int tg_end = min(tg + 64, nt);
+        for (int tc = tg; tc < tg_end; tc += kNormChunk) {
+            const int par = (tc / kNormChunk) & 1;
+            // this chunk's LDS slots, as 32-bit LDS addresses held in registers once per
+            // chunk (the tokens then address them with immediate offsets)
+            unsigned ring_addr = (unsigned) (size_t) (lds_ptr<float>) (ring_lane + par * (kNormChunk * 128));
+            unsigned gate_addr = (unsigned) (size_t) (lds_ptr<f2>) &lds.gate[wave][tc - tg];
+            unsigned kq_addr = (unsigned) (size_t) (lds_ptr<float>) &lds.kq[par][0];
+            asm volatile("" : "+v"(ring_addr), "+v"(gate_addr), "+v"(kq_addr));
+            const lds_ptr<float> ring_par = (lds_ptr<float>) (size_t) ring_addr;
+            const lds_ptr<f2> gate_c = (lds_ptr<f2>) (size_t) gate_addr;
+            const lds_ptr<float> kq_c = (lds_ptr<float>) (size_t) kq_addr;
+            int u = 0;
+#pragma unroll
+            for (; u < kNormChunk; ++u) {
+                const int t = tc + u;
+                if (t >= tg_end) break;   // uniform: only the last chunk stops early
+                __builtin_amdgcn_sched_barrier(0);
+                const f2 ge = gate_c[u];
+                const float beta = ge.x, eg = ge.y;
+                buf[lane] = qk_n;
+                const float vc = v_n;
+                fetch(t + 1);
+                // the staging above is wave-private: order it against this wave's reads
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+                f4 pk = {0.f, 0.f, 0.f, 0.f}, pq = pk;
+#pragma unroll
+                for (int m = 0; m < 16; ++m) {
+                    pk = fma4(s[m], krow[m], pk);
+                    pq = fma4(s[m], qrow[m], pq);
+                }
+                const float kq = chunk_kq_on ? kq_c[u] : wave_kq((const float*) buf, lane);
+                // column sums over the 8 row groups of the wave (lane bits 3..5):
+                // ((g0+g1)+(g2+g3))+((g4+g5)+(g6+g7)), as in the single-token kernel
+                const float pkc = scatter_sum4(add_xor8(pk));
+                const float pqc = scatter_sum4(add_xor8(pq));
+                // delta and readout of column col + oc (the readout scale, when there is
+                // one, multiplies after the sum as in the single-token kernel)
+                const float dc = beta * __builtin_fmaf(-eg, pkc, vc);
+                float out = __builtin_fmaf(kq, dc, eg * pqc);
+                if (p.oscale != 1.0f) out *= p.oscale;
+                // the deltas of all 4 columns for the update
+                const f4 d = gather4(dc);
+                if (o_seq && reads_out) buffer_store_f1(out, o_seq + t * row_hv, o_off);
+                if (kNorm) {
+                    if (reads_out) ring_par[u * 128] = out;
+                    if (u == kNormChunk - 1) {   // a whole chunk: its norm, and k . q of the next
+                        const f4 zz = z_n;
+                        fetch_z(tc + kNormChunk);
+                        if (chunk_kq_on) {
+                            chunk_kq(par ^ 1);
+                            fetch_qkp(tc + 2 * kNormChunk);
+                        }
+                        __syncthreads();
+                        norm_chunk(tc, par, kNormChunk, zz);
+                    }
+                }
+                if (keep_state || t < last) {
+                    // re-read k from LDS rather than keeping 16 rows live across the
+                    // reduction (the fence stops the compiler from reusing the values
+                    // loaded above)
+                    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+                    const f4* k4 = (const f4*) krow;
+#pragma unroll
+                    for (int m4 = 0; m4 < 4; ++m4) {
+                        const f4 kk = k4[m4];
+                        s[4 * m4 + 0] = fma4(kk.x, d, eg * s[4 * m4 + 0]);
+                        s[4 * m4 + 1] = fma4(kk.y, d, eg * s[4 * m4 + 1]);
+                        s[4 * m4 + 2] = fma4(kk.z, d, eg * s[4 * m4 + 2]);
+                        s[4 * m4 + 3] = fma4(kk.w, d, eg * s[4 * m4 + 3]);
+                    }
                 }
             }
-        }
-        if (!keep_state && t + 1 == nt) break;   // uniform over the workgroup
-        // re-read k from LDS rather than keeping 16 rows live across the reduction (the
-        // fence stops the compiler from reusing the values loaded above)
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        const f4* k4 = (const f4*) krow;
-#pragma unroll
-        for (int m4 = 0; m4 < 4; ++m4) {
-            const f4 kk = k4[m4];
-            s[4 * m4 + 0] = fma4(kk.x, d, eg * s[4 * m4 + 0]);
-            s[4 * m4 + 1] = fma4(kk.y, d, eg * s[4 * m4 + 1]);
-            s[4 * m4 + 2] = fma4(kk.z, d, eg * s[4 * m4 + 2]);
-            s[4 * m4 + 3] = fma4(kk.w, d, eg * s[4 * m4 + 3]);
+            // the last chunk of the call, cut short: its norm
+            if (kNorm && u < kNormChunk) {
+                __syncthreads();
+                norm_chunk(tc, par, u, z_n);
+            }
         }
     }
     if (rg == 0) {
@@ -555,7 +669,7 @@ __global__ __launch_bounds__(256) void decode_multi_kernel(StepParams p) {
                             head * kS + 4 * (tid & 31), nt);
         }
     }
-    multi_tokens<kNorm>(p, job, nt, s, lds, kKeep);
+    multi_tokens<kNorm, kNorm && kKeep>(p, job, nt, s, lds, kKeep);
     if (nt > 0 && kKeep) store_tile(s, tile);
 }
 
@@ -583,10 +697,10 @@ __global__ __launch_bounds__(256) void commit_window_kernel(StepParams com, Step
         load_tile(s, tile);
     }
     if (nk > 0) {
-        multi_tokens<false>(com, job, nk, s, lds, true);
+        multi_tokens<false, false>(com, job, nk, s, lds, true);
         store_tile(s, tile);
     }
-    multi_tokens<true>(win, job, job.nt, s, lds, false);
+    multi_tokens<true, false>(win, job, job.nt, s, lds, false);
 }
 
 // ------------------------------------------------------------------ launch

@@ -70,6 +70,40 @@ def test_library_is_built_for_gfx950_only(tmp_path):
     assert targets and all(t.endswith("gfx950") for t in targets), targets
 
 
+def _kernel_disassembly(tmp_path):
+    """The gfx950 disassembly of every code object in the built library (the fat binary
+    section holds one bundle per source file)."""
+    from gated_deltanet_mixer_gdn_amd import gdn
+    fb = tmp_path / "fatbin.bin"
+    subprocess.check_call(["objcopy", "-O", "binary", "--only-section=.hip_fatbin", gdn.LIB_PATH, str(fb)])
+    data = fb.read_bytes()
+    starts = [m.start() for m in re.finditer(re.escape(b"__CLANG_OFFLOAD_BUNDLE__"), data)]
+    assert starts, "no offload bundle in the library"
+    text = []
+    for n, s in enumerate(starts):
+        part = tmp_path / f"bundle{n}.bin"
+        part.write_bytes(data[s:starts[n + 1] if n + 1 < len(starts) else len(data)])
+        co = tmp_path / f"bundle{n}.co"
+        subprocess.check_call(["/opt/rocm/llvm/bin/clang-offload-bundler", "--unbundle", "--type=o",
+                               "--input=" + str(part), "--targets=hipv4-amdgcn-amd-amdhsa--gfx950",
+                               "--output=" + str(co)])
+        text.append(subprocess.run(["/opt/rocm/llvm/bin/llvm-objdump", "-d", str(co)], capture_output=True,
+                                   text=True, check=True).stdout)
+    return "\n".join(text)
+
+
+def test_kernels_make_no_generic_or_scratch_memory_access(tmp_path):
+    """Every memory access of the kernels is a global, buffer or LDS instruction: a flat
+    (generic) access means an address lost its address space (an LDS pointer cast through
+    an integer once turned LDS slots into flat accesses to unmapped low addresses), and a
+    scratch access means registers spilled.  Checked on the built gfx950 code."""
+    dis = _kernel_disassembly(tmp_path)
+    kernels = re.findall(r"<(_ZN3gdn\w+)>:", dis)
+    assert any("decode_multi_kernel" in k for k in kernels) and any("conv_silu_norm_kernel" in k for k in kernels)
+    bad = [ln.strip() for ln in dis.splitlines() if re.match(r"\s*(flat|scratch)_\w+", ln)]
+    assert not bad, bad[:5]
+
+
 def test_abi_version(L):
     assert L.gdn_abi_version() == 7
 
