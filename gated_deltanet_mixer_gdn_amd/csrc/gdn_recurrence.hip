@@ -453,6 +453,24 @@ __device__ __forceinline__ void multi_tokens(const StepParams& p, const HeadJob&
     // the column of its 4 whose q sum a lane ends with after scatter_sum4
     const int oc = (int) (scatter_sum4(f4{0.f, 1.f, 2.f, 3.f}) * 0.25f);
     const bool reads_out = (lane & 8) == 0;
+    // The four lanes (lane & 15) + 16 b, b = 0..3, hold the four columns of one group,
+    // column oc_b in row pair b.  The deltas are gathered back in column order with LDS
+    // permutes (ds_bpermute, no VALU): component k reads the lane of the row pair b_k
+    // whose column is k.
+    const int oc0 = __builtin_amdgcn_readlane(oc, 0), oc1 = __builtin_amdgcn_readlane(oc, 16),
+              oc2 = __builtin_amdgcn_readlane(oc, 32);
+    auto src_of = [&](int k) {
+        const int b = oc0 == k ? 0 : oc1 == k ? 1 : oc2 == k ? 2 : 3;
+        return ((lane & 15) | (b << 4)) << 2;
+    };
+    const int gsrc0 = src_of(0), gsrc1 = src_of(1), gsrc2 = src_of(2), gsrc3 = src_of(3);
+    auto gather_d = [&](float v) {
+        const int x = __float_as_int(v);
+        return f4{__int_as_float(__builtin_amdgcn_ds_bpermute(gsrc0, x)),
+                  __int_as_float(__builtin_amdgcn_ds_bpermute(gsrc1, x)),
+                  __int_as_float(__builtin_amdgcn_ds_bpermute(gsrc2, x)),
+                  __int_as_float(__builtin_amdgcn_ds_bpermute(gsrc3, x))};
+    };
     // byte offsets inside one token's row of h, and of o
     const unsigned q_off = 4u * (unsigned) (job.j * kS + (lane & 31) * 4 + (lane < 32 ? 0 : p.h_k * kS));
     const unsigned v_off = 4u * (unsigned) ((2 * p.h_k + i) * kS + col + oc);
@@ -588,7 +606,7 @@ __device__ __forceinline__ void multi_tokens(const StepParams& p, const HeadJob&
                 float out = __builtin_fmaf(kq, dc, eg * pqc);
                 if (p.oscale != 1.0f) out *= p.oscale;
                 // the deltas of all 4 columns for the update
-                const f4 d = gather4(dc);
+                const f4 d = gather_d(dc);
                 if (o_seq && reads_out) buffer_store_f1(out, o_seq + t * row_hv, o_off);
                 if (kNorm) {
                     if (reads_out) ring_par[u * 128] = out;
