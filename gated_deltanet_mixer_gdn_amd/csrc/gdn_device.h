@@ -123,18 +123,6 @@ __device__ __forceinline__ float scatter_sum4(f4 v) {
     return __uint_as_float(c[0]) + __uint_as_float(c[1]);
 }
 
-// The inverse placement of scatter_sum4: lane holds one value of the 4-lane group
-// (lane, lane ^ 16, lane ^ 32, lane ^ 48) in the slot scatter_sum4 gives it; every lane
-// gets the group's 4 values in component order.  Each level swaps a value with itself,
-// which puts the even row's (or low half's) value first whichever way the swap
-// instruction pairs its operands.  All 64 lanes must be active.
-__device__ __forceinline__ f4 gather4(float v) {
-    const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    const auto a = __builtin_amdgcn_permlane16_swap(h[0], h[0], false, false);
-    const auto b = __builtin_amdgcn_permlane16_swap(h[1], h[1], false, false);
-    return f4{__uint_as_float(a[0]), __uint_as_float(b[0]), __uint_as_float(a[1]), __uint_as_float(b[1])};
-}
-
 // Where the single-launch decode also writes y split for the projections: row `row` of
 // a [rows][chunks * 64] activation in the tiled layout of gdn_split_bf16 (tile = 32
 // rows x 64 k; fragment (s, lane = i + 32h) of a tile holds the 8 values
