@@ -563,6 +563,49 @@ def test_verify_window_ragged_with_an_unknown_slot(T):
     assert torch.equal(y, direct.y) and torch.equal(h, direct.h)
 
 
+@pytest.mark.parametrize("B,T,ragged", [(64, 4, False), (43, 3, True), (42, 5, True), (100, 8, True), (160, 2, True)])
+def test_many_sequence_window_matches_direct_decode(B, T, ragged):
+    """Windows over many sequences (thousands of workgroups, so every CU runs several):
+    y and h equal decoding the same tokens directly, bit for bit, with ragged token
+    counts (0 to T), unknown slots flagged with zero rows, and the pool untouched;
+    sampled sequences against the oracle."""
+    import torch
+    import gated_deltanet_mixer_gdn_amd as G
+    wl = W.make("window-many", B, T, seed=300 + B + T, n_slots=B + 7, state_std=0.02, conv_std=1.0,
+                slot_choice="random")
+    rng = np.random.default_rng(400 + B)
+    slots = wl.slots.copy()
+    n_tok = np.full(B, T, np.int32)
+    if ragged:
+        n_tok = rng.integers(0, T + 1, B).astype(np.int32)
+        n_tok[0] = T
+        slots[[5, B - 1]] = [B + 7, -3]                  # outside the pool
+    log(f"many-sequence window B={B} T={T} ragged={ragged} tokens={int(n_tok.sum())}")
+    win = GpuMixer(wl)
+    before_s, before_c = win.pool.state.clone(), win.pool.conv.clone()
+    h = torch.full_like(win.h, 3.0)
+    y = torch.full_like(win.y, 3.0)
+    G.gdn_verify_window(win.pool, win.qkv, win.conv_w, win.alpha, win.beta_logit, win.dt, win.ssm_a, win.z,
+                        win.norm_w, wl.eps, h, y, dev(slots), dev(n_tok))
+    torch.cuda.synchronize()
+    assert torch.equal(win.pool.state, before_s) and torch.equal(win.pool.conv, before_c), "window wrote the pool"
+    flags = int(win.pool.flags.item())
+    assert bool(flags & G.GDN_FLAG_BAD_SLOT) == ragged and not flags & G.GDN_FLAG_BAD_NTOK
+    if ragged:
+        assert not y[[5, B - 1]].any() and not h[[5, B - 1]].any()
+    direct = GpuMixer(wl)
+    direct.run(fused=True, slots=dev(slots), n_tok=dev(n_tok))
+    assert torch.equal(y, direct.y) and torch.equal(h, direct.h)
+    for b in (0, B // 2 + 1):
+        k = int(n_tok[b])
+        if k == 0 or not 0 <= slots[b] < B + 7:
+            continue
+        slot = int(slots[b])
+        ref = oracle.mixer(wl.geom, wl.qkv[b, :k], wl.conv_w, wl.alpha[b, :k], wl.beta_logit[b, :k], wl.dt,
+                           wl.ssm_a, wl.z[b, :k], wl.norm_w, wl.eps, wl.conv_state[slot], wl.state[slot])
+        assert_tokens(f"window y seq {b}", y[b:b + 1, :k].cpu().numpy(), [ref["y"]], [k])
+
+
 @pytest.mark.parametrize("T0,T1,ragged", [(4, 4, True), (6, 1, True), (20, 9, True), (4, 3, False)])
 def test_commit_window_equals_commit_then_window(T0, T1, ragged):
     """gdn_commit_window (the commit of one window and the next window with each state
