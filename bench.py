@@ -23,6 +23,7 @@ profiles/decode_fused_b256_traffic.txt and reported only while the kernel source
 it was measured on are unchanged.
 """
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -714,40 +715,56 @@ def main():
     o = torch.empty(wl.B, wl.T, g.h_v, g.s, device="cuda")
     y = torch.empty(wl.B, wl.T, g.value_dim, device="cuda")
     stream = torch.cuda.current_stream()
+    # the tiny configuration is T sequential decode calls of one token each (a step is
+    # all T of them); every other configuration is one call per step.  Events of the
+    # multi-kernel forms bracket the first call's kernels.
+    seq = args.config == "tiny"
+    calls = wl.T if seq else 1
+    if seq:
+        cut = lambda a, t: a[:, t:t + 1].contiguous()
+        toks = [(cut(qkv, t), cut(alpha, t), cut(bl, t), cut(z, t), cut(h, t), cut(o, t), cut(y, t))
+                for t in range(wl.T)]
+    else:
+        toks = [(qkv, alpha, bl, z, h, o, y)]
 
     def step_fused(ev=None):
         # the timed hot path: conv/SiLU/L2, then the recurrence with the gated RMSNorm
         # fused into its epilogue (y only, like the pages' fused step + norm kernel)
-        if ev:
-            ev[0].record(stream)
-        G.gdn_conv_silu_norm(pool, qkv, conv_w, wl.eps, h, slots, n_tok)
-        if ev:
-            ev[1].record(stream)
-        G.gdn_decode_step_norm(pool, h, alpha, bl, dt, ssm_a, z, norm_w, wl.eps, y, None, slots, n_tok)
-        if ev:
-            ev[2].record(stream)
+        for i, (qkv_, alpha_, bl_, z_, h_, o_, y_) in enumerate(toks):
+            e = ev if i == 0 else None
+            if e:
+                e[0].record(stream)
+            G.gdn_conv_silu_norm(pool, qkv_, conv_w, wl.eps, h_, slots, n_tok)
+            if e:
+                e[1].record(stream)
+            G.gdn_decode_step_norm(pool, h_, alpha_, bl_, dt, ssm_a, z_, norm_w, wl.eps, y_, None, slots, n_tok)
+            if e:
+                e[2].record(stream)
 
     def step_one(ev=None):
         # single launch: conv/SiLU/L2, recurrence and gated RMSNorm for one token
         if ev:
             ev[0].record(stream)
-        G.gdn_decode_fused(pool, qkv, conv_w, alpha, bl, dt, ssm_a, z, norm_w, wl.eps, y, None, slots)
+        for qkv_, alpha_, bl_, z_, h_, o_, y_ in toks:
+            G.gdn_decode_fused(pool, qkv_, conv_w, alpha_, bl_, dt, ssm_a, z_, norm_w, wl.eps, y_, None, slots)
         if ev:
             ev[1].record(stream)
 
     def step_three(ev=None):
         # the same pass as three separate calls (o goes through HBM)
-        if ev:
-            ev[0].record(stream)
-        G.gdn_conv_silu_norm(pool, qkv, conv_w, wl.eps, h, slots, n_tok)
-        if ev:
-            ev[1].record(stream)
-        G.gdn_decode_step(pool, h, alpha, bl, dt, ssm_a, o, slots, n_tok)
-        if ev:
-            ev[2].record(stream)
-        G.gdn_gated_rmsnorm(o, z, norm_w, wl.eps, y)
-        if ev:
-            ev[3].record(stream)
+        for i, (qkv_, alpha_, bl_, z_, h_, o_, y_) in enumerate(toks):
+            e = ev if i == 0 else None
+            if e:
+                e[0].record(stream)
+            G.gdn_conv_silu_norm(pool, qkv_, conv_w, wl.eps, h_, slots, n_tok)
+            if e:
+                e[1].record(stream)
+            G.gdn_decode_step(pool, h_, alpha_, bl_, dt, ssm_a, o_, slots, n_tok)
+            if e:
+                e[2].record(stream)
+            G.gdn_gated_rmsnorm(o_, z_, norm_w, wl.eps, y_)
+            if e:
+                e[3].record(stream)
 
     card = _card_dir()
     clocks = {}
@@ -784,12 +801,13 @@ def main():
         return wall * 1000.0 / args.steps, k_ms, len(evs)
 
     three_ms, three_k, _ = timed(step_three, 4, ("conv", "step", "norm"))
-    single = wl.T == 1 and wl.n_tok is None
+    single = (wl.T == 1 or seq) and wl.n_tok is None
     two_ms, two_k, two_n = timed(step_fused, 3, ("conv", "step_norm"))
     # the timed hot path: the single launch for one token per sequence (the fastest
     # form), else conv/SiLU/L2 + the recurrence with the norm fused (two launches)
     if single:
         one_ms, one_k, one_n = timed(step_one, 2, ("one",))
+        one_k = {k: v / calls for k, v in one_k.items()}   # per launch
         ms_per_step, k_ms, n_samples, dominant = one_ms, one_k, one_n, "one"
     else:
         one_ms = one_k = None
@@ -834,15 +852,16 @@ def main():
     if flags:
         raise SystemExit(f"bench.py: device flag word set ({flags:#x})")
 
-    nbytes, units = algorithmic_bytes(wl)
+    nbytes, units = algorithmic_bytes(dataclasses.replace(wl, T=1) if seq else wl)   # per call
+    units *= calls                                                                     # per step
     value = units / (ms_per_step / 1000.0)
     achieved = nbytes[dominant] / (k_ms[dominant] / 1000.0) / 1e9
     # a workload whose flops per algorithmic byte exceed the VALU / HBM ridge (the
     # multi-token prefill) is priced against the fp32 VALU peak instead
-    flops = units * FLOP_PER_SEQ_HEAD_STEP
+    flops = units // calls * FLOP_PER_SEQ_HEAD_STEP                                   # per launch
     alu_bound = flops / nbytes[dominant] > VALU_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)
     achieved_tflops = flops / (k_ms[dominant] / 1000.0) / 1e12
-    mixer_bytes = nbytes["one"] if single else nbytes["conv"] + nbytes["step_norm"]
+    mixer_bytes = calls * (nbytes["one"] if single else nbytes["conv"] + nbytes["step_norm"])
     mixer_gbps = mixer_bytes / (ms_per_step / 1000.0) / 1e9
     two_gbps = nbytes["step_norm"] / (two_k["step_norm"] / 1000.0) / 1e9
     three_step_gbps = nbytes["step"] / (three_k["step"] / 1000.0) / 1e9
@@ -880,7 +899,8 @@ def main():
         "config": {"workload": wl.name, "B": wl.B, "T": wl.T, "n_slots": wl.n_slots,
                    "h_k": g.h_k, "h_v": g.h_v, "S": g.s, "d_conv": g.d_conv,
                    "state_bytes": int(wl.n_slots * g.h_v * g.s * g.s * 4), "parallelism": "none"},
-        "path": ("gdn_decode_fused (conv, recurrence and gated RMSNorm in one launch, y only)" if single else
+        "path": (f"gdn_decode_fused, {calls} sequential calls of one token per step" if seq else
+                 "gdn_decode_fused (conv, recurrence and gated RMSNorm in one launch, y only)" if single else
                  "gdn_conv_silu_norm + gdn_decode_step_norm (gated RMSNorm fused, y only)"),
         "hbm_gbps_mixer": mixer_gbps,
         "hbm_frac_mixer": mixer_gbps / HBM_PEAK_GBPS,
