@@ -41,9 +41,14 @@ def build(force: bool = True) -> str:
 def lib():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB_PATH):
-            build()
-        L = ctypes.CDLL(_LIB_PATH)
+        # GDN_ORACLE_LIB: another build of this source to load instead (the mutation
+        # tests load copies with one mistake planted, to show the pins catch it)
+        path = os.environ.get("GDN_ORACLE_LIB")
+        if not path:
+            if not os.path.exists(_LIB_PATH):
+                build()
+            path = _LIB_PATH
+        L = ctypes.CDLL(path)
         i, i64, d = ctypes.c_int, ctypes.c_int64, ctypes.c_double
         L.gdn_oracle_sigmoid.argtypes = [d]
         L.gdn_oracle_sigmoid.restype = d
